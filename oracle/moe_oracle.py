@@ -1,0 +1,386 @@
+"""Plain CPU oracle for one MoE expert-parallel layer on one GPU's share.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or
+run this module: only the tests, the smoke check of ``__graft_entry__`` and
+the CPU-baseline leg of ``bench.py`` use it.  It shares no code, constant or
+helper with the HIP library and never imports it.
+
+What it computes (the layer is the four stages of the data flow drawn in
+"MoE 专家并行的 All-to-All 通信瓶颈" (wiblog.cn), section "All-to-All
+分发与回收的机制", flowchart: route -> pack by destination -> per-expert
+grouped GEMM -> merge back to token order with the gate weights; the same
+stage list is "Gate -> dispatch -> Expert FFN -> combine -> Aggregation" in
+"MoE Inference Communication", section "系统剖析"):
+
+  route     per token: softmax over the E router logits; the K experts with
+            the largest logits (ties -> lower expert index), best first;
+            gate weight = that expert's softmax probability.
+  dispatch  histogram of expert ids (the ``bincount`` line of the dispatch
+            pseudocode in "MoE 推理服务工程真相 2026", section 2.3), a
+            per-expert capacity that drops the later tokens of an overflowing
+            expert (same page, section 2.2; zeroed router output, section
+            4.3 "Expert drop"), an exclusive prefix sum of the kept counts
+            ("MoE Inference Communication", section "MoE 计算核优化",
+            cumsum) and the dense token<->row mapping table of that same
+            section, which places every kept (token, expert) pair in an
+            expert-contiguous buffer ordered by (expert, token).  Experts are
+            owned by W virtual ranks in contiguous blocks of E/W, so the
+            buffer is also rank-major: rank r's send slice starts at
+            offsets[r*E/W].
+  ffn       per expert, on its rows: h = silu(x Wg^T) * (x Wu^T),
+            y = h Wd^T (SwiGLU, no biases).
+  combine   out[t] = sum over kept slots k (ascending) of w[t,k] * y[row(t,k)].
+
+Where the pages say nothing (the gate function, the tie-break, the order
+inside an expert, the capacity formula, the FFN form) the oracle takes the
+plain reading: fp32-input softmax, lowest index wins ties, ascending token
+order, capacity = ceil(C*N*K/E), SwiGLU.
+
+Precision: arithmetic is float64 throughout.  A value is rounded to the
+activation storage type (bf16 round-to-nearest-even, or fp32) exactly where
+the layer stores it: h, y_perm and out; gate weights are stored as fp32.
+The top-K choice compares the raw fp32 logits, so it never depends on how
+``exp`` is rounded.
+
+Every function here is pinned by tests that do not reuse its code:
+brute-force subset checks, a dense every-expert-for-every-token recompute,
+closed forms, invariants, a hand-worked example, and library routines.
+"""
+from __future__ import annotations
+
+import math
+from fractions import Fraction
+
+import numpy as np
+
+__all__ = [
+    "round_bf16",
+    "round_storage",
+    "capacity",
+    "route",
+    "dispatch",
+    "pack",
+    "silu",
+    "expert_ffn",
+    "grouped_ffn",
+    "combine",
+    "layer",
+    "token_outputs",
+]
+
+
+# --------------------------------------------------------------------------
+# storage rounding
+# --------------------------------------------------------------------------
+
+def round_bf16(a):
+    """Round float64 values to the nearest bfloat16 value, ties to even.
+
+    bfloat16 keeps 8 significant bits and fp32's exponent range (normal
+    numbers down to 2**-126, subnormal spacing 2**-133).  For |a| in
+    [2**(q-1), 2**q) the representable spacing is 2**(q-8); scaling by a power
+    of two is exact in float64, so ``rint`` (half to even) performs the
+    rounding exactly.  Results of magnitude 2**128 or more overflow to inf.
+    Returns float64 holding the rounded values.
+    """
+    a = np.asarray(a, dtype=np.float64)
+    out = np.zeros_like(a)
+    nz = (a != 0) & np.isfinite(a)
+    _, q = np.frexp(a[nz])
+    q = np.maximum(q, -125)            # below 2**-126 the spacing stays 2**-133
+    scale = np.ldexp(1.0, 8 - q)
+    r = np.rint(a[nz] * scale) / scale
+    r[np.abs(r) >= 2.0 ** 128] = np.inf * np.sign(r[np.abs(r) >= 2.0 ** 128])
+    out[nz] = r
+    out[~np.isfinite(a)] = a[~np.isfinite(a)]
+    out[a == 0] = a[a == 0]            # keeps the sign of zero
+    return out
+
+
+def round_storage(a, act):
+    """Round to the activation storage type: ``"bf16"`` or ``"f32"``.
+
+    ``"f64"`` keeps float64 values unrounded; it exists so that tests can
+    check the layer's structure without any storage rounding.
+    """
+    if act == "f64":
+        return np.asarray(a, dtype=np.float64)
+    if act == "bf16":
+        return round_bf16(a)
+    if act == "f32":
+        return np.asarray(a, dtype=np.float64).astype(np.float32).astype(np.float64)
+    raise ValueError(f"unknown activation type {act!r}")
+
+
+# --------------------------------------------------------------------------
+# capacity
+# --------------------------------------------------------------------------
+
+def capacity(C, N, K, E):
+    """Per-expert token budget ceil(C*N*K/E), computed exactly.
+
+    "MoE 推理服务工程真相 2026", section 2.2: an expert receiving more tokens
+    than its capacity drops the excess; the page's formula lost its symbols,
+    so the budget is the expected per-expert load N*K/E scaled by the
+    capacity factor C, rounded up.  C is taken as the exact rational value of
+    the given double.  Returns -1 (dropless) when C is None.
+    """
+    if C is None:
+        return -1
+    if not (isinstance(C, (int, float)) and math.isfinite(C) and C > 0):
+        raise ValueError("capacity factor must be finite and > 0")
+    v = Fraction(C) * N * K / E
+    return int(math.ceil(v))
+
+
+# --------------------------------------------------------------------------
+# route
+# --------------------------------------------------------------------------
+
+def route(logits, K, renormalize=False):
+    """Top-K routing of every token.
+
+    "MoE 专家并行的 All-to-All 通信瓶颈", section "一个反直觉的扩容结果": the
+    router picks the Top-K experts of every token; "MoE 推理服务工程真相
+    2026", section 一: the router yields top-k expert weights.
+
+    logits: float32 [N, E] (finite).  Returns (topk_idx int32 [N, K],
+    topk_w float32 [N, K]).  Slot 0 is the best expert.  A larger logit wins;
+    equal logits go to the lower expert index.  The weight of slot k is the
+    softmax probability of its expert over all E logits (max-subtracted,
+    float64), optionally divided by the sum of the K selected probabilities.
+    """
+    l32 = np.asarray(logits, dtype=np.float32)
+    N, E = l32.shape
+    if not (1 <= K <= E):
+        raise ValueError("need 1 <= K <= E")
+    if not np.all(np.isfinite(l32)):
+        raise ValueError("logits must be finite")
+    l = l32.astype(np.float64)
+    m = l.max(axis=1, keepdims=True)
+    ex = np.exp(l - m)
+    p = ex / ex.sum(axis=1, keepdims=True)
+    # Stable sort on the negated fp32 logit: descending logit, and among
+    # equal logits the original (ascending expert) order survives.
+    order = np.argsort(-l32, axis=1, kind="stable")
+    idx = order[:, :K].astype(np.int32)
+    w = np.take_along_axis(p, idx.astype(np.int64), axis=1)
+    if renormalize:
+        w = w / w.sum(axis=1, keepdims=True)
+    return idx, w.astype(np.float32)
+
+
+# --------------------------------------------------------------------------
+# dispatch
+# --------------------------------------------------------------------------
+
+def dispatch(topk_idx, E, W, cap):
+    """Histogram, capacity drop, prefix sum and the token<->row mapping.
+
+    topk_idx int32 [N, K] (distinct experts per token); E experts owned by W
+    virtual ranks in contiguous blocks of E/W; cap = -1 for dropless, else
+    the per-expert budget (>= 0).
+
+    Steps, in the order the dispatch pseudocode of "MoE 推理服务工程真相
+    2026" (section 2.3) takes them:
+      1. demand = bincount(expert ids, minlength=E)   (that page's own line)
+      2. keep: walk tokens t = 0..N-1 and their slots k = 0..K-1; the
+         r-th token seen by expert e (r counted from 0) is kept iff
+         cap < 0 or r < cap, so an overflowing expert drops its later
+         tokens (section 2.2) and the dropped pair's router output is zero
+         (section 4.3 "Expert drop").
+      3. counts = kept per expert; offsets = exclusive cumsum (E+1 entries)
+         ("MoE Inference Communication", section "MoE 计算核优化", cumsum);
+         rank_offsets[r] = offsets[r*E/W] (W+1 entries): rank r's contiguous
+         send slice ("MoE 专家并行的 All-to-All 通信瓶颈", flowchart step
+         "按目标卡分组打包").
+      4. the dense mapping table of "MoE 计算核优化": a kept pair (t,k) with
+         expert e and rank r goes to row offsets[e] + r; dest[t,k] is that
+         row (-1 when dropped) and perm_token[row] = t.
+
+    Returns a dict of int32 arrays: demand [E], counts [E], offsets [E+1],
+    rank_offsets [W+1], dest [N, K], perm_token [M] with M = offsets[E],
+    plus the int ``dropped``.
+    """
+    idx = np.asarray(topk_idx)
+    N, K = idx.shape
+    if E % W != 0:
+        raise ValueError("E must be a multiple of W")
+    if cap < -1:
+        raise ValueError("cap must be >= -1")
+    demand = np.bincount(idx.ravel().astype(np.int64), minlength=E).astype(np.int32)
+
+    seen = [0] * E
+    rank = [[0] * K for _ in range(N)]
+    kept = [[False] * K for _ in range(N)]
+    for t in range(N):
+        for k in range(K):
+            e = int(idx[t, k])
+            r = seen[e]
+            seen[e] = r + 1
+            rank[t][k] = r
+            kept[t][k] = cap < 0 or r < cap
+
+    counts = np.zeros(E, dtype=np.int64)
+    for t in range(N):
+        for k in range(K):
+            if kept[t][k]:
+                counts[int(idx[t, k])] += 1
+    offsets = np.zeros(E + 1, dtype=np.int64)
+    offsets[1:] = np.cumsum(counts)
+    per_rank = E // W
+    rank_offsets = np.array([offsets[r * per_rank] for r in range(W + 1)], dtype=np.int64)
+
+    M = int(offsets[E])
+    dest = np.full((N, K), -1, dtype=np.int64)
+    perm_token = np.full(M, -1, dtype=np.int64)
+    for t in range(N):
+        for k in range(K):
+            if kept[t][k]:
+                row = int(offsets[int(idx[t, k])]) + rank[t][k]
+                dest[t, k] = row
+                perm_token[row] = t
+    return {
+        "demand": demand,
+        "counts": counts.astype(np.int32),
+        "offsets": offsets.astype(np.int32),
+        "rank_offsets": rank_offsets.astype(np.int32),
+        "dest": dest.astype(np.int32),
+        "perm_token": perm_token.astype(np.int32),
+        "dropped": int(N * K - M),
+    }
+
+
+def pack(x, perm_token):
+    """Rank-major send buffer: row p holds a bit copy of x[perm_token[p]]."""
+    return np.asarray(x)[np.asarray(perm_token, dtype=np.int64)]
+
+
+# --------------------------------------------------------------------------
+# expert FFN
+# --------------------------------------------------------------------------
+
+def silu(z):
+    """z * sigmoid(z) = z / (1 + exp(-z)), float64."""
+    z = np.asarray(z, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        return z / (1.0 + np.exp(-z))
+
+
+def expert_ffn(R, wg, wu, wd, act):
+    """One expert's SwiGLU FFN on its rows R [m, d].
+
+    wg, wu: [ffn, d]; wd: [d, ffn] (all exactly representable in the
+    activation type).  G = R wg^T and U = R wu^T in float64; h = silu(G)*U
+    rounded to storage; y = h wd^T rounded to storage.  Returns (h, y).
+    The grouped-GEMM stage of "MoE 专家并行的 All-to-All 通信瓶颈" (flowchart
+    "Grouped GEMM 专家计算") applies this to each expert's contiguous rows.
+    """
+    R = np.asarray(R, dtype=np.float64)
+    G = R @ np.asarray(wg, dtype=np.float64).T
+    U = R @ np.asarray(wu, dtype=np.float64).T
+    h = round_storage(silu(G) * U, act)
+    y = round_storage(h @ np.asarray(wd, dtype=np.float64).T, act)
+    return h, y
+
+
+def grouped_ffn(x_perm, offsets, expert_weights, act):
+    """Apply every non-empty expert to its slice of the packed buffer.
+
+    x_perm [M, d]; offsets [E+1]; expert_weights(e) -> (wg, wu, wd).
+    Returns (h [M, ffn], y_perm [M, d]) float64 holding storage values.
+    """
+    x_perm = np.asarray(x_perm, dtype=np.float64)
+    E = len(offsets) - 1
+    M = int(offsets[E])
+    h_all = None
+    y_all = np.zeros((M, x_perm.shape[1]), dtype=np.float64)
+    for e in range(E):
+        a, b = int(offsets[e]), int(offsets[e + 1])
+        if b == a:
+            continue
+        wg, wu, wd = expert_weights(e)
+        h, y = expert_ffn(x_perm[a:b], wg, wu, wd, act)
+        if h_all is None:
+            h_all = np.zeros((M, h.shape[1]), dtype=np.float64)
+        h_all[a:b] = h
+        y_all[a:b] = y
+    if h_all is None:
+        h_all = np.zeros((M, 0), dtype=np.float64)
+    return h_all, y_all
+
+
+# --------------------------------------------------------------------------
+# combine
+# --------------------------------------------------------------------------
+
+def combine(y_perm, dest, topk_w, act):
+    """Weighted merge back to token order.
+
+    "MoE 专家并行的 All-to-All 通信瓶颈", flowchart "加权合并回原 token 顺序":
+    out[t] = sum over k ascending with dest[t,k] >= 0 of w[t,k] * y[dest[t,k]]
+    in float64, rounded to storage.  A dropped pair adds nothing ("MoE 推理
+    服务工程真相 2026", section 4.3: the dropped expert's output is zero); a
+    token with every pair dropped gets a zero row.
+    """
+    y_perm = np.asarray(y_perm, dtype=np.float64)
+    dest = np.asarray(dest)
+    w = np.asarray(topk_w, dtype=np.float32).astype(np.float64)
+    N, K = dest.shape
+    d = y_perm.shape[1]
+    out = np.zeros((N, d), dtype=np.float64)
+    for k in range(K):
+        rows = dest[:, k]
+        ok = rows >= 0
+        out[ok] += w[ok, k:k + 1] * y_perm[rows[ok].astype(np.int64)]
+    return round_storage(out, act)
+
+
+# --------------------------------------------------------------------------
+# the whole layer
+# --------------------------------------------------------------------------
+
+def layer(logits, x, expert_weights, K, W, cap, act, renormalize=False):
+    """Route, dispatch, FFN and combine; returns every intermediate."""
+    N, E = np.asarray(logits).shape
+    idx, w = route(logits, K, renormalize)
+    disp = dispatch(idx, E, W, cap)
+    x_perm = pack(x, disp["perm_token"])
+    h, y = grouped_ffn(x_perm, disp["offsets"], expert_weights, act)
+    out = combine(y, disp["dest"], w, act)
+    res = dict(disp)
+    res.update(topk_idx=idx, topk_w=w, x_perm=x_perm, h=h, y_perm=y, out=out)
+    return res
+
+
+def token_outputs(tokens, x, topk_idx, topk_w, dest, expert_weights, act):
+    """Outputs of selected tokens only, expert by expert.
+
+    For layers too large to run whole on the CPU: every kept pair (t,k) of a
+    selected token runs its expert's FFN on the single row x[t]; the rows are
+    independent, so this equals the corresponding rows of the full layer.
+    Returns (y_rows dict (t,k) -> y [d], out [len(tokens), d]).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    tokens = [int(t) for t in tokens]
+    need = {}
+    for t in tokens:
+        for k in range(topk_idx.shape[1]):
+            if dest[t, k] >= 0:
+                need.setdefault(int(topk_idx[t, k]), []).append((t, k))
+    y_rows = {}
+    for e in sorted(need):
+        wg, wu, wd = expert_weights(e)
+        pairs = need[e]
+        R = np.stack([x[t] for t, _ in pairs])
+        _, y = expert_ffn(R, wg, wu, wd, act)
+        for i, tk in enumerate(pairs):
+            y_rows[tk] = y[i]
+    d = x.shape[1]
+    w = np.asarray(topk_w, dtype=np.float32).astype(np.float64)
+    out = np.zeros((len(tokens), d), dtype=np.float64)
+    for i, t in enumerate(tokens):
+        for k in range(topk_idx.shape[1]):
+            if dest[t, k] >= 0:
+                out[i] += w[t, k] * y_rows[(t, k)]
+    return y_rows, round_storage(out, act)
