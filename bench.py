@@ -1,0 +1,231 @@
+"""Benchmark of the MoE layer hot path on one MI355X.
+
+One step = route -> dispatch -> grouped SwiGLU FFN -> combine over one batch
+of synthetic tokens, all four through the C ABI (libmoe_route.so), inputs
+already resident in HBM.  Prints one JSON line:
+
+  value            whole-layer tokens/s (N tokens per step / time per step)
+  roofline         the grouped FFN (the dominant stage) against bf16 MFMA
+                   peak: 6*M*d*ffn flops per launch / its event-timed duration
+  stages           per-stage times, dispatch+combine GB/s against HBM peak
+  cpu_baseline     the CPU oracle on a bounded sample of the same workload
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0           # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # dense bf16
+FP32_PEAK_TFLOPS = 157.3
+
+DEFAULT_WORKLOAD = "dense8"
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-sample-tokens", type=int, default=384)
+    p.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"))
+    return p.parse_args()
+
+
+def algorithmic_bytes(cfg, M, b):
+    """Dispatch and combine bytes the method must move.
+
+    dispatch: read every token row once (N*d*b), write every kept row
+    (M*d*b), plus the index traffic of the mapping table (12 bytes per
+    assignment: topk_idx read, dest and perm_token written).
+    combine: read every kept row (M*d*b), write every token row (N*d*b),
+    plus dest and topk_w reads (8 bytes per assignment).
+    """
+    N, d, K = cfg["N"], cfg["d"], cfg["K"]
+    disp = N * d * b + M * d * b + 12 * N * K
+    comb = M * d * b + N * d * b + 8 * N * K
+    return disp, comb
+
+
+def ffn_flops(cfg, M):
+    return 6.0 * M * cfg["d"] * cfg["ffn"]
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the layer's "
+              "multi-GPU exchange is not part of this build.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from grouped_gemm_route_amd import binding as B
+    from grouped_gemm_route_amd import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cfg = synth.config(args.workload)
+    N, d, ffn, E, K, W = (cfg[k] for k in ("N", "d", "ffn", "E", "K", "W"))
+    dtype = synth.TORCH_DTYPE[cfg["act"]]
+    b = 2 if cfg["act"] == "bf16" else 4
+    cap = B.moe_capacity(cfg["C"], N, K, E) if cfg["C"] is not None else -1
+
+    inp = synth.make_inputs(cfg, dev)
+    layer = B.MoeLayer(N, d, ffn, E, K, W, cap, dtype, dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        layer.route(inp["logits"])
+        if ev is not None:
+            ev[1].record(stream)
+        layer.dispatch(inp["x"])
+        if ev is not None:
+            ev[2].record(stream)
+        layer.ffn(inp["w_gate"], inp["w_up"], inp["w_down"])
+        if ev is not None:
+            ev[3].record(stream)
+        layer.combine()
+        if ev is not None:
+            ev[4].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    M = int(layer.disp["offsets"][-1].item())
+
+    # timed region: exactly `steps` steps, synchronised on both sides
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed * 1e3 / args.steps
+
+    names = ["route", "dispatch", "ffn", "combine"]
+    st = {n: float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(args.steps)]))
+          for j, n in enumerate(names)}
+    disp_b, comb_b = algorithmic_bytes(cfg, M, b)
+    flops = ffn_flops(cfg, M)
+    ffn_s = st["ffn"] * 1e-3
+    achieved_tflops = flops / ffn_s / 1e12
+    peak = MFMA_BF16_PEAK_TFLOPS if cfg["act"] == "bf16" else FP32_PEAK_TFLOPS
+    dc_gbps = (disp_b + comb_b) / ((st["dispatch"] + st["combine"]) * 1e-3) / 1e9
+
+    traffic = None
+    if os.path.exists(args.traffic_json):
+        try:
+            tj = json.load(open(args.traffic_json))
+            if tj.get("workload") == args.workload and tj.get("kernel") == "grouped_ffn":
+                traffic = tj.get("bytes_per_launch")
+        except (OSError, ValueError):
+            traffic = None
+
+    result = {
+        "metric": "MoE layer tokens/s on 1 MI355X; dispatch/combine GB/s; grouped-GEMM TFLOP/s",
+        "value": N / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if cfg["act"] == "bf16" else "f32",
+        "data": "synthetic (seeded N(0,1) logits and hidden states, N(0,1/fan_in) weights)",
+        "config": {
+            "workload": f"{args.workload}: N={N} d={d} ffn={ffn} E={E} K={K} W={W} "
+                        f"{cfg['act']} capacity={cap} (M={M} kept rows)",
+            "global_batch": N,
+            "parallelism": "single GPU; all-to-all replaced by local pack/unpack into W "
+                           "virtual-rank slices",
+        },
+        "roofline": {
+            "kernel": "moe_grouped_ffn (gate/up + down MFMA GEMMs)",
+            "bound": "mfma",
+            "achieved": achieved_tflops,
+            "peak": peak,
+            "unit": "TFLOP/s",
+            "frac": achieved_tflops / peak,
+            "traffic": traffic,
+        },
+        "stages": {
+            "route_ms": st["route"],
+            "dispatch_ms": st["dispatch"],
+            "ffn_ms": st["ffn"],
+            "combine_ms": st["combine"],
+            "dispatch_GBps": disp_b / (st["dispatch"] * 1e-3) / 1e9,
+            "combine_GBps": comb_b / (st["combine"] * 1e-3) / 1e9,
+            "dispatch_combine_GBps": dc_gbps,
+            "dispatch_combine_hbm_frac": dc_gbps / HBM_PEAK_GBPS,
+            "ffn_TFLOPs": achieved_tflops,
+            "ffn_mfma_frac": achieved_tflops / peak,
+            "tokens_per_s": {n: N / (st[n] * 1e-3) for n in names},
+        },
+    }
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(cfg, inp, cap, args.cpu_sample_tokens)
+    print(json.dumps(result))
+
+
+def cpu_baseline(cfg, inp, cap, n_tok):
+    """The oracle, untouched, on the first n_tok tokens of the same workload."""
+    import numpy as np
+    import torch
+
+    from oracle import moe_oracle as O
+
+    n = min(n_tok, cfg["N"])
+    logits = inp["logits"][:n].cpu().numpy()
+    x = inp["x"][:n].float().cpu().numpy()
+    wts = {}
+
+    def weights(e):
+        if e not in wts:
+            wts.clear()
+            wts[e] = tuple(inp[k][e].float().cpu().numpy() for k in ("w_gate", "w_up", "w_down"))
+        return wts[e]
+
+    # weights are copied to the host outside the timed region
+    host_w = {e: weights(e) for e in range(cfg["E"])} if cfg["E"] <= 16 else None
+    fn = (lambda e: host_w[e]) if host_w is not None else weights
+    cap_s = O.capacity(cfg["C"], n, cfg["K"], cfg["E"]) if cfg["C"] is not None else -1
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover - threadpoolctl missing
+        threads = 1
+    t0 = time.perf_counter()
+    O.layer(logits, x, fn, cfg["K"], cfg["W"], cap_s, cfg["act"])
+    dt = time.perf_counter() - t0
+    return {
+        "value": n / dt,
+        "unit": "tokens/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"first {n} tokens of the same workload (same logits, hidden states and "
+                  f"weights; capacity recomputed for {n} tokens), whole oracle layer, "
+                  f"{dt:.1f} s; BLAS threads {threads}, host cpus {os.cpu_count()}",
+    }
+
+
+if __name__ == "__main__":
+    main()

@@ -1,1 +1,18 @@
-"""MI355X-native MoE expert-parallel layer: route, dispatch, grouped SwiGLU FFN, combine."""
+"""MI355X-native MoE expert-parallel layer: route, dispatch, grouped SwiGLU FFN, combine.
+
+The compute runs in libmoe_route.so (HIP kernels for gfx950, C ABI in
+include/moe_route.h); ``binding`` marshals torch tensors into its calls.
+"""
+from .binding import (  # noqa: F401
+    MoeError,
+    MoeLayer,
+    load_library,
+    moe_abi_version,
+    moe_capacity,
+    moe_combine,
+    moe_dispatch,
+    moe_dispatch_workspace_bytes,
+    moe_grouped_ffn,
+    moe_grouped_ffn_workspace_bytes,
+    moe_route_topk,
+)

@@ -1,0 +1,296 @@
+"""Python binding of libmoe_route.so (ctypes): argument marshalling only.
+
+Every stage of the layer runs in the library's HIP kernels.  These wrappers
+take torch tensors (torch supplies device memory and the current stream),
+check dtype, device and contiguity, allocate outputs when none are passed,
+and call the C entry point of the same name.  There is no fallback: if the
+library is missing or a call fails, an exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_route.so")
+
+MOE_OK = 0
+DTYPE_CODE = {torch.float32: 0, torch.bfloat16: 1}
+
+# (name, restype, argtypes) of every exported function in include/moe_route.h
+_P = ctypes.c_void_p
+_I32 = ctypes.c_int32
+_I64 = ctypes.c_int64
+_SZ = ctypes.c_size_t
+SIGNATURES = [
+    ("moe_abi_version", ctypes.c_int, []),
+    ("moe_status_string", ctypes.c_char_p, [ctypes.c_int]),
+    ("moe_last_error", ctypes.c_char_p, []),
+    ("moe_capacity", _I64, [ctypes.c_double, _I64, _I32, _I32]),
+    ("moe_route_topk", ctypes.c_int, [_P, _I32, _I32, _I32, _I32, _P, _P, _P]),
+    ("moe_dispatch_workspace_bytes", _SZ, [_I32, _I32, _I32]),
+    ("moe_dispatch", ctypes.c_int,
+     [_P, _I32, _I32, _I32, _P, _I32, _I32, _I32, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    ("moe_grouped_ffn_workspace_bytes", _SZ, [_I64, _I32, _I32]),
+    ("moe_grouped_ffn", ctypes.c_int,
+     [_P, _I32, _I32, _I32, _I32, _P, _I64, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    ("moe_combine", ctypes.c_int, [_P, _I32, _I32, _I32, _I32, _P, _P, _P, _P]),
+]
+
+_lib = None
+
+
+class MoeError(RuntimeError):
+    """A library call returned a non-OK status."""
+
+    def __init__(self, name, status, detail):
+        super().__init__(f"{name}: {status_name(status)}: {detail}")
+        self.status = status
+
+
+def load_library(path=None):
+    """Load (once) and return the ctypes handle of libmoe_route.so."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(
+            f"{p} is not built; run `python -m grouped_gemm_route_amd.build` first")
+    lib = ctypes.CDLL(p)
+    for name, res, args in SIGNATURES:
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def status_name(status):
+    return load_library().moe_status_string(status).decode()
+
+
+def _check(name, status):
+    if status != MOE_OK:
+        raise MoeError(name, status, load_library().moe_last_error().decode())
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _need(t, name, dtype=None, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU (got {t.device})")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype} (got {t.dtype})")
+
+
+def _act_code(t, name):
+    if t.dtype not in DTYPE_CODE:
+        raise ValueError(f"{name}: unsupported dtype {t.dtype}")
+    return DTYPE_CODE[t.dtype]
+
+
+# ---------------------------------------------------------------------------
+# entry points
+# ---------------------------------------------------------------------------
+
+def moe_abi_version():
+    return load_library().moe_abi_version()
+
+
+def moe_capacity(C, N, K, E):
+    """ceil(C*N*K/E) computed exactly by the library (host only)."""
+    v = load_library().moe_capacity(float(C), int(N), int(K), int(E))
+    if v == -2:
+        raise ValueError(f"invalid capacity arguments C={C} N={N} K={K} E={E}")
+    return int(v)
+
+
+def moe_route_topk(logits, K, renormalize=False, topk_idx=None, topk_w=None):
+    """Top-K routing: returns (topk_idx int32 [N,K], topk_w fp32 [N,K])."""
+    _need(logits, "logits", torch.float32)
+    N, E = logits.shape
+    dev = logits.device
+    if topk_idx is None:
+        topk_idx = torch.empty(N, K, dtype=torch.int32, device=dev)
+    if topk_w is None:
+        topk_w = torch.empty(N, K, dtype=torch.float32, device=dev)
+    _need(topk_idx, "topk_idx", torch.int32, dev)
+    _need(topk_w, "topk_w", torch.float32, dev)
+    if topk_idx.numel() != N * K or topk_w.numel() != N * K:
+        raise ValueError("topk_idx/topk_w must hold N*K elements")
+    _check("moe_route_topk", load_library().moe_route_topk(
+        _ptr(logits), N, E, K, int(bool(renormalize)), _ptr(topk_idx), _ptr(topk_w),
+        _stream(logits)))
+    return topk_idx, topk_w
+
+
+def moe_dispatch_workspace_bytes(N, E, K):
+    return int(load_library().moe_dispatch_workspace_bytes(N, E, K))
+
+
+DISPATCH_OUTPUTS = ("x_perm", "perm_token", "dest", "demand", "counts", "offsets",
+                    "rank_offsets")
+
+
+def alloc_dispatch_outputs(N, d, E, K, W, dtype, device):
+    return {
+        "x_perm": torch.empty(N * K, d, dtype=dtype, device=device),
+        "perm_token": torch.empty(N * K, dtype=torch.int32, device=device),
+        "dest": torch.empty(N, K, dtype=torch.int32, device=device),
+        "demand": torch.empty(E, dtype=torch.int32, device=device),
+        "counts": torch.empty(E, dtype=torch.int32, device=device),
+        "offsets": torch.empty(E + 1, dtype=torch.int32, device=device),
+        "rank_offsets": torch.empty(W + 1, dtype=torch.int32, device=device),
+        "workspace": torch.empty(max(1, moe_dispatch_workspace_bytes(N, E, K)),
+                                 dtype=torch.uint8, device=device),
+    }
+
+
+def moe_dispatch(x, topk_idx, E, W, capacity, out=None):
+    """Pack tokens into per-expert rows; returns the dict of outputs."""
+    _need(x, "x")
+    code = _act_code(x, "x")
+    N, d = x.shape
+    dev = x.device
+    _need(topk_idx, "topk_idx", torch.int32, dev)
+    K = topk_idx.shape[1]
+    if topk_idx.shape[0] != N:
+        raise ValueError("topk_idx must be [N, K]")
+    if out is None:
+        out = alloc_dispatch_outputs(N, d, E, K, W, x.dtype, dev)
+    sizes = {"x_perm": N * K * d, "perm_token": N * K, "dest": N * K, "demand": E,
+             "counts": E, "offsets": E + 1, "rank_offsets": W + 1}
+    for k in DISPATCH_OUTPUTS:
+        _need(out[k], k, x.dtype if k == "x_perm" else torch.int32, dev)
+        if out[k].numel() < sizes[k]:
+            raise ValueError(f"{k} must hold at least {sizes[k]} elements")
+    ws = out["workspace"]
+    _need(ws, "workspace", None, dev)
+    _check("moe_dispatch", load_library().moe_dispatch(
+        _ptr(x), code, N, d, _ptr(topk_idx), E, K, W, int(capacity),
+        _ptr(out["x_perm"]), _ptr(out["perm_token"]), _ptr(out["dest"]),
+        _ptr(out["demand"]), _ptr(out["counts"]), _ptr(out["offsets"]),
+        _ptr(out["rank_offsets"]), _ptr(ws), ws.numel() * ws.element_size(),
+        _stream(x)))
+    return out
+
+
+def moe_grouped_ffn_workspace_bytes(max_rows, E, dtype):
+    return int(load_library().moe_grouped_ffn_workspace_bytes(max_rows, E, DTYPE_CODE[dtype]))
+
+
+def moe_grouped_ffn(x_perm, offsets, w_gate, w_up, w_down, max_rows=None, h=None,
+                    y_perm=None, workspace=None):
+    """Grouped SwiGLU FFN over the packed rows; returns (h, y_perm)."""
+    _need(x_perm, "x_perm")
+    code = _act_code(x_perm, "x_perm")
+    dev = x_perm.device
+    d = x_perm.shape[1]
+    E, ffn, d2 = w_gate.shape
+    if d2 != d or tuple(w_up.shape) != (E, ffn, d) or tuple(w_down.shape) != (E, d, ffn):
+        raise ValueError("weights must be w_gate/w_up [E, ffn, d] and w_down [E, d, ffn]")
+    for name, t in (("w_gate", w_gate), ("w_up", w_up), ("w_down", w_down)):
+        _need(t, name, x_perm.dtype, dev)
+    _need(offsets, "offsets", torch.int32, dev)
+    if offsets.numel() != E + 1:
+        raise ValueError("offsets must have E+1 entries")
+    if max_rows is None:
+        max_rows = x_perm.shape[0]
+    if x_perm.shape[0] < max_rows:
+        raise ValueError("x_perm must have at least max_rows rows")
+    if h is None:
+        h = torch.empty(max_rows, ffn, dtype=x_perm.dtype, device=dev)
+    if y_perm is None:
+        y_perm = torch.empty(max_rows, d, dtype=x_perm.dtype, device=dev)
+    _need(h, "h", x_perm.dtype, dev)
+    _need(y_perm, "y_perm", x_perm.dtype, dev)
+    if h.numel() < max_rows * ffn or y_perm.numel() < max_rows * d:
+        raise ValueError("h / y_perm too small for max_rows")
+    if workspace is None:
+        workspace = torch.empty(max(1, moe_grouped_ffn_workspace_bytes(max_rows, E, x_perm.dtype)),
+                                dtype=torch.uint8, device=dev)
+    _need(workspace, "workspace", None, dev)
+    _check("moe_grouped_ffn", load_library().moe_grouped_ffn(
+        _ptr(x_perm), code, d, ffn, E, _ptr(offsets), int(max_rows), _ptr(w_gate),
+        _ptr(w_up), _ptr(w_down), _ptr(h), _ptr(y_perm), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(x_perm)))
+    return h, y_perm
+
+
+def moe_combine(y_perm, dest, topk_w, out=None):
+    """Weighted merge back to token order; returns out [N, d]."""
+    _need(y_perm, "y_perm")
+    code = _act_code(y_perm, "y_perm")
+    dev = y_perm.device
+    _need(dest, "dest", torch.int32, dev)
+    _need(topk_w, "topk_w", torch.float32, dev)
+    N, K = dest.shape
+    d = y_perm.shape[1]
+    if tuple(topk_w.shape) != (N, K):
+        raise ValueError("topk_w must match dest [N, K]")
+    if out is None:
+        out = torch.empty(N, d, dtype=y_perm.dtype, device=dev)
+    _need(out, "out", y_perm.dtype, dev)
+    if out.numel() < N * d:
+        raise ValueError("out too small")
+    _check("moe_combine", load_library().moe_combine(
+        _ptr(y_perm), code, N, d, K, _ptr(dest), _ptr(topk_w), _ptr(out), _stream(y_perm)))
+    return out
+
+
+class MoeLayer:
+    """The four calls of one layer over preallocated buffers.
+
+    Buffers are sized once for (N, d, ffn, E, K, W, dtype); ``forward`` then
+    enqueues route -> dispatch -> grouped FFN -> combine on the current
+    stream with no host synchronisation and no allocation.
+    """
+
+    def __init__(self, N, d, ffn, E, K, W, capacity, dtype, device, renormalize=False):
+        self.N, self.d, self.ffn_dim, self.E, self.K, self.W = N, d, ffn, E, K, W
+        self.capacity = int(capacity)
+        self.renormalize = renormalize
+        self.max_rows = N * K
+        dev = torch.device(device)
+        self.topk_idx = torch.empty(N, K, dtype=torch.int32, device=dev)
+        self.topk_w = torch.empty(N, K, dtype=torch.float32, device=dev)
+        self.disp = alloc_dispatch_outputs(N, d, E, K, W, dtype, dev)
+        self.h = torch.empty(self.max_rows, ffn, dtype=dtype, device=dev)
+        self.y_perm = torch.empty(self.max_rows, d, dtype=dtype, device=dev)
+        self.ffn_ws = torch.empty(max(1, moe_grouped_ffn_workspace_bytes(self.max_rows, E, dtype)),
+                                  dtype=torch.uint8, device=dev)
+        self.out = torch.empty(N, d, dtype=dtype, device=dev)
+
+    def route(self, logits):
+        return moe_route_topk(logits, self.K, self.renormalize, self.topk_idx, self.topk_w)
+
+    def dispatch(self, x):
+        return moe_dispatch(x, self.topk_idx, self.E, self.W, self.capacity, self.disp)
+
+    def ffn(self, w_gate, w_up, w_down):
+        return moe_grouped_ffn(self.disp["x_perm"], self.disp["offsets"], w_gate, w_up, w_down,
+                               self.max_rows, self.h, self.y_perm, self.ffn_ws)
+
+    def combine(self):
+        return moe_combine(self.y_perm, self.disp["dest"], self.topk_w, self.out)
+
+    def forward(self, logits, x, w_gate, w_up, w_down):
+        self.route(logits)
+        self.dispatch(x)
+        self.ffn(w_gate, w_up, w_down)
+        return self.combine()

@@ -1,0 +1,204 @@
+// Host side of the C ABI declared in include/moe_route.h: argument checks,
+// workspace sizing and the launches.  Every check runs before any HIP call,
+// so a rejected call enqueues nothing.
+#include "moe_route.h"
+#include "moe_internal.h"
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+
+int hip_status(hipError_t err, const char* what) {
+  if (err == hipSuccess) return MOE_OK;
+  return fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(err));
+}
+
+int elem_size(int32_t dtype) {
+  if (dtype == MOE_DTYPE_F32) return 4;
+  if (dtype == MOE_DTYPE_BF16) return 2;
+  return 0;
+}
+
+hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+}  // namespace
+
+extern "C" {
+
+int moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+const char* moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP";
+    default: return "MOE_ERR_UNKNOWN";
+  }
+}
+
+const char* moe_last_error(void) { return g_last_error.c_str(); }
+
+int64_t moe_capacity(double C, int64_t N, int32_t K, int32_t E) {
+  if (!(std::isfinite(C) && C > 0.0) || N < 0 || K < 1 || E < 1) return -2;
+  const unsigned __int128 nk = (unsigned __int128)N * (unsigned __int128)K;
+  if (nk >> 62) return -2;
+  // C = m * 2^ex exactly, with m an odd integer below 2^53.
+  int ex = 0;
+  const double fr = std::frexp(C, &ex);
+  int64_t m = (int64_t)std::ldexp(fr, 53);
+  ex -= 53;
+  while ((m & 1) == 0) {
+    m >>= 1;
+    ++ex;
+  }
+  unsigned __int128 num = (unsigned __int128)m * nk;  // < 2^115
+  if (ex >= 0) {
+    // num * 2^ex must stay far from overflow; any result above INT64_MAX fails.
+    if (num != 0 && ex > 126 - 115) {
+      int bits = 0;
+      for (unsigned __int128 v = num; v; v >>= 1) ++bits;
+      if (bits + ex > 126) return -2;
+    }
+    num <<= ex;
+  } else {
+    // ceil(num / (E * 2^s)) = ceil(ceil(num / 2^s) / E)
+    const int s = -ex;
+    if (s >= 120) {
+      num = num != 0 ? 1 : 0;
+    } else {
+      const unsigned __int128 one = 1;
+      num = (num + (one << s) - 1) >> s;
+    }
+  }
+  const unsigned __int128 q = (num + (unsigned)E - 1) / (unsigned)E;
+  if (q > (unsigned __int128)INT64_MAX) return -2;
+  return (int64_t)q;
+}
+
+int moe_route_topk(const float* logits, int32_t N, int32_t E, int32_t K,
+                   int32_t renormalize, int32_t* topk_idx, float* topk_w,
+                   void* stream) {
+  if (!logits || !topk_idx || !topk_w)
+    return fail(MOE_ERR_INVALID_ARG, "moe_route_topk: null pointer");
+  if (N < 0 || E < 1 || K < 1 || K > E)
+    return fail(MOE_ERR_INVALID_ARG, "moe_route_topk: need N >= 0 and 1 <= K <= E (N=%d E=%d K=%d)", N, E, K);
+  if (E > MOE_MAX_EXPERTS || K > MOE_MAX_TOPK)
+    return fail(MOE_ERR_UNSUPPORTED, "moe_route_topk: E <= %d and K <= %d supported", MOE_MAX_EXPERTS, MOE_MAX_TOPK);
+  if ((int64_t)N * E >= ((int64_t)1 << 31) * 4 || (int64_t)N * K >= ((int64_t)1 << 31))
+    return fail(MOE_ERR_UNSUPPORTED, "moe_route_topk: N too large");
+  return hip_status(moe::launch_route_topk(logits, N, E, K, renormalize,
+                                           topk_idx, topk_w, as_stream(stream)),
+                    "moe_route_topk");
+}
+
+size_t moe_dispatch_workspace_bytes(int32_t N, int32_t E, int32_t K) {
+  if (N < 1 || E < 1 || K < 1) return 0;
+  return moe::dispatch_workspace_bytes(N, E, K);
+}
+
+int moe_dispatch(const void* x, int32_t dtype, int32_t N, int32_t d,
+                 const int32_t* topk_idx, int32_t E, int32_t K, int32_t W,
+                 int64_t capacity, void* x_perm, int32_t* perm_token,
+                 int32_t* dest, int32_t* demand, int32_t* counts,
+                 int32_t* offsets, int32_t* rank_offsets, void* workspace,
+                 size_t workspace_bytes, void* stream) {
+  if (!x || !topk_idx || !x_perm || !perm_token || !dest || !demand ||
+      !counts || !offsets || !rank_offsets)
+    return fail(MOE_ERR_INVALID_ARG, "moe_dispatch: null pointer");
+  const int es = elem_size(dtype);
+  if (es == 0) return fail(MOE_ERR_UNSUPPORTED, "moe_dispatch: dtype %d", dtype);
+  if (N < 1 || d < 1 || K < 1 || K > E || W < 1 || E % W != 0 || capacity < -1)
+    return fail(MOE_ERR_INVALID_ARG,
+                "moe_dispatch: need N >= 1, d >= 1, 1 <= K <= E, W >= 1, E %% W == 0, "
+                "capacity >= -1 (N=%d d=%d E=%d K=%d W=%d capacity=%lld)",
+                N, d, E, K, W, (long long)capacity);
+  if (((int64_t)d * es) % 16 != 0)
+    return fail(MOE_ERR_INVALID_ARG, "moe_dispatch: row bytes d*%d must be a multiple of 16", es);
+  if ((int64_t)N * K >= ((int64_t)1 << 31))
+    return fail(MOE_ERR_INVALID_ARG, "moe_dispatch: N*K must be below 2^31");
+  if (E > MOE_MAX_EXPERTS || K > MOE_MAX_TOPK)
+    return fail(MOE_ERR_UNSUPPORTED, "moe_dispatch: E <= %d and K <= %d supported", MOE_MAX_EXPERTS, MOE_MAX_TOPK);
+  const size_t need = moe::dispatch_workspace_bytes(N, E, K);
+  if (!workspace || workspace_bytes < need)
+    return fail(MOE_ERR_WORKSPACE, "moe_dispatch: workspace needs %zu bytes", need);
+  const moe::DispatchWorkspace ws = moe::dispatch_workspace(workspace, N, E, K);
+  return hip_status(
+      moe::launch_dispatch(x, (size_t)d * es, N, topk_idx, E, K, W, capacity,
+                           x_perm, perm_token, dest, demand, counts, offsets,
+                           rank_offsets, ws, as_stream(stream)),
+      "moe_dispatch");
+}
+
+size_t moe_grouped_ffn_workspace_bytes(int64_t max_rows, int32_t E,
+                                       int32_t dtype) {
+  if (max_rows < 0 || E < 1 || elem_size(dtype) == 0) return 0;
+  return moe::grouped_ffn_workspace_bytes(max_rows, E, dtype == MOE_DTYPE_BF16);
+}
+
+int moe_grouped_ffn(const void* x_perm, int32_t dtype, int32_t d, int32_t ffn,
+                    int32_t E, const int32_t* offsets, int64_t max_rows,
+                    const void* w_gate, const void* w_up, const void* w_down,
+                    void* h, void* y_perm, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  if (!x_perm || !offsets || !w_gate || !w_up || !w_down || !h || !y_perm)
+    return fail(MOE_ERR_INVALID_ARG, "moe_grouped_ffn: null pointer");
+  const int es = elem_size(dtype);
+  if (es == 0) return fail(MOE_ERR_UNSUPPORTED, "moe_grouped_ffn: dtype %d", dtype);
+  if (d < 1 || ffn < 1 || E < 1 || max_rows < 0)
+    return fail(MOE_ERR_INVALID_ARG, "moe_grouped_ffn: need d, ffn, E >= 1 and max_rows >= 0");
+  if (E > MOE_MAX_EXPERTS)
+    return fail(MOE_ERR_UNSUPPORTED, "moe_grouped_ffn: E <= %d supported", MOE_MAX_EXPERTS);
+  if (max_rows >= ((int64_t)1 << 31))
+    return fail(MOE_ERR_UNSUPPORTED, "moe_grouped_ffn: max_rows must be below 2^31");
+  if (dtype == MOE_DTYPE_BF16 && (d % 64 != 0 || ffn % 64 != 0))
+    return fail(MOE_ERR_UNSUPPORTED, "moe_grouped_ffn: bf16 needs d and ffn multiples of 64 (d=%d ffn=%d)", d, ffn);
+  if (dtype == MOE_DTYPE_F32 && (d % 8 != 0 || ffn % 8 != 0))
+    return fail(MOE_ERR_UNSUPPORTED, "moe_grouped_ffn: fp32 needs d and ffn multiples of 8 (d=%d ffn=%d)", d, ffn);
+  if (max_rows == 0) return MOE_OK;
+  const size_t need = moe::grouped_ffn_workspace_bytes(max_rows, E, dtype == MOE_DTYPE_BF16);
+  if (!workspace || workspace_bytes < need)
+    return fail(MOE_ERR_WORKSPACE, "moe_grouped_ffn: workspace needs %zu bytes", need);
+  return hip_status(
+      moe::launch_grouped_ffn(x_perm, dtype == MOE_DTYPE_BF16, d, ffn, E,
+                              offsets, max_rows, w_gate, w_up, w_down, h,
+                              y_perm, workspace, as_stream(stream)),
+      "moe_grouped_ffn");
+}
+
+int moe_combine(const void* y_perm, int32_t dtype, int32_t N, int32_t d,
+                int32_t K, const int32_t* dest, const float* topk_w, void* out,
+                void* stream) {
+  if (!y_perm || !dest || !topk_w || !out)
+    return fail(MOE_ERR_INVALID_ARG, "moe_combine: null pointer");
+  const int es = elem_size(dtype);
+  if (es == 0) return fail(MOE_ERR_UNSUPPORTED, "moe_combine: dtype %d", dtype);
+  if (N < 1 || d < 1 || K < 1)
+    return fail(MOE_ERR_INVALID_ARG, "moe_combine: need N, d, K >= 1");
+  if (((int64_t)d * es) % 16 != 0)
+    return fail(MOE_ERR_INVALID_ARG, "moe_combine: row bytes d*%d must be a multiple of 16", es);
+  if (K > MOE_MAX_TOPK)
+    return fail(MOE_ERR_UNSUPPORTED, "moe_combine: K <= %d supported", MOE_MAX_TOPK);
+  return hip_status(moe::launch_combine(y_perm, dtype == MOE_DTYPE_BF16, N, d,
+                                        K, dest, topk_w, out, as_stream(stream)),
+                    "moe_combine");
+}
+
+}  // extern "C"

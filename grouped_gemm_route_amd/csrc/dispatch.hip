@@ -1,0 +1,229 @@
+// Dispatch: histogram, capacity drop, prefix scan and the stable permutation
+// of tokens into per-expert contiguous rows, rank-major.
+//
+// Follows the dispatch pseudocode of "MoE 推理服务工程真相 2026", section 2.3
+// (bincount of expert ids -> overflow against the capacity -> grouping for
+// the all-to-all), with the capacity of section 2.2 and the expert drop of
+// section 4.3, and the dense token-to-expert mapping table built from a
+// cumsum in "MoE Inference Communication", section "MoE 计算核优化".
+//
+// Row of a kept pair (t, k) with expert e: offsets[e] + r, where r is the
+// number of tokens t' < t routed to e (each token names an expert at most
+// once).  r is assembled from three integer parts, so every row position is
+// exact and independent of scheduling:
+//   rank kernel    (one thread per token, 256 tokens per block): within a
+//                  wave, lane l routed to e sets bit l of mask[wave][e] with
+//                  an LDS atomic OR (order-free); its rank inside the block
+//                  is popcount(mask[wave][e] & lanes-below-l) plus the
+//                  popcounts of the earlier waves' masks.  The block's
+//                  per-expert totals go to block_counts[b][e].
+//   scan kernel    (one block): per expert, an exclusive scan of the block
+//                  totals over blocks (block_excl) and their sum (demand);
+//                  counts = min(demand, capacity); offsets = exclusive scan
+//                  of counts over experts; rank_offsets[r] = offsets[r*E/W].
+//   scatter kernel (one wave per token): r = block_excl + local rank; kept
+//                  iff capacity < 0 or r < capacity; writes dest and
+//                  perm_token, then copies the token's row once from HBM to
+//                  each kept destination row in 16-byte vectors.
+// Because experts are numbered rank by rank, the (expert, token) order is
+// rank-major: rank r's send slice is rows [rank_offsets[r], rank_offsets[r+1]).
+#include "moe_internal.h"
+#include "block_scan.h"
+
+namespace moe {
+namespace {
+
+constexpr int kRankWaves = kRankBlockTokens / kWave;  // 4
+
+__global__ __launch_bounds__(kRankBlockTokens) void dispatch_rank_kernel(
+    const int32_t* __restrict__ topk_idx, int N, int E, int K,
+    int32_t* __restrict__ block_counts, int32_t* __restrict__ local_rank) {
+  extern __shared__ unsigned long long masks[];  // [kRankWaves][E]
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  for (int i = tid; i < kRankWaves * E; i += blockDim.x) masks[i] = 0ull;
+  __syncthreads();
+
+  const int t = blockIdx.x * kRankBlockTokens + tid;
+  const bool valid = t < N;
+  if (valid) {
+    for (int k = 0; k < K; ++k) {
+      const int e = topk_idx[(size_t)t * K + k];
+      if ((unsigned)e < (unsigned)E) atomicOr(&masks[wave * E + e], 1ull << lane);
+    }
+  }
+  __syncthreads();
+
+  if (valid) {
+    const unsigned long long below = (1ull << lane) - 1ull;
+    for (int k = 0; k < K; ++k) {
+      const int e = topk_idx[(size_t)t * K + k];
+      int r = 0;
+      if ((unsigned)e < (unsigned)E) {
+        r = __popcll(masks[wave * E + e] & below);
+        for (int w = 0; w < wave; ++w) r += __popcll(masks[w * E + e]);
+      }
+      local_rank[(size_t)t * K + k] = r;
+    }
+  }
+  for (int e = tid; e < E; e += blockDim.x) {
+    int c = 0;
+#pragma unroll
+    for (int w = 0; w < kRankWaves; ++w) c += __popcll(masks[w * E + e]);
+    block_counts[(size_t)blockIdx.x * E + e] = c;
+  }
+}
+
+constexpr int kScanThreads = 1024;
+
+__global__ __launch_bounds__(kScanThreads) void dispatch_scan_kernel(
+    const int32_t* __restrict__ block_counts, int B, int E, int W,
+    int64_t capacity, int32_t* __restrict__ block_excl,
+    int32_t* __restrict__ demand, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ rank_offsets) {
+  __shared__ int part_sum[kScanThreads];
+  __shared__ int kept_s[kScanThreads + 1];
+  __shared__ int wave_sums[kScanThreads / kWave];
+  const int tid = threadIdx.x;
+  // Thread (e, part): part p of P sums a contiguous range of blocks.
+  const int P = kScanThreads / E;  // E <= 1024
+  const int e = tid % E;
+  const int part = tid / E;
+  const bool active = part < P;
+  const int chunk = (B + P - 1) / P;
+  const int b0 = min(B, part * chunk);
+  const int b1 = min(B, b0 + chunk);
+  int s = 0;
+  if (active)
+    for (int b = b0; b < b1; ++b) s += block_counts[(size_t)b * E + e];
+  part_sum[tid] = s;
+  __syncthreads();
+  int kept = 0;
+  if (active) {
+    int run = 0;
+    for (int p = 0; p < part; ++p) run += part_sum[p * E + e];
+    for (int b = b0; b < b1; ++b) {
+      const int c = block_counts[(size_t)b * E + e];
+      block_excl[(size_t)b * E + e] = run;
+      run += c;
+    }
+    if (part == 0) {
+      int tot = 0;
+      for (int p = 0; p < P; ++p) tot += part_sum[p * E + e];
+      demand[e] = tot;
+      kept = capacity < 0 ? tot : (int)min((int64_t)tot, capacity);
+      counts[e] = kept;
+    }
+  }
+  // Exclusive scan of the kept counts over experts (threads 0..E-1 hold them).
+  int total = 0;
+  const int excl = block_exclusive_scan(tid < E ? kept : 0, wave_sums, &total);
+  if (tid < E) {
+    offsets[tid] = excl;
+    kept_s[tid] = excl;
+  }
+  if (tid == 0) {
+    offsets[E] = total;
+    kept_s[E] = total;
+  }
+  __syncthreads();
+  const int per_rank = E / W;
+  for (int r = tid; r <= W; r += blockDim.x) rank_offsets[r] = kept_s[r * per_rank];
+}
+
+constexpr int kScatterWaves = 4;
+constexpr int kCopyUnroll = 4;
+
+__global__ __launch_bounds__(kScatterWaves * kWave) void dispatch_scatter_kernel(
+    const uint4* __restrict__ x, int row_chunks, int N,
+    const int32_t* __restrict__ topk_idx, int E, int K, int64_t capacity,
+    const int32_t* __restrict__ block_excl,
+    const int32_t* __restrict__ local_rank,
+    const int32_t* __restrict__ offsets, uint4* __restrict__ x_perm,
+    int32_t* __restrict__ perm_token, int32_t* __restrict__ dest) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int t = blockIdx.x * kScatterWaves + threadIdx.x / kWave;
+  if (t >= N) return;  // whole wave leaves together
+
+  int row = -1;
+  if (lane < K) {
+    const int e = topk_idx[(size_t)t * K + lane];
+    if ((unsigned)e < (unsigned)E) {
+      const int r = block_excl[(size_t)(t / kRankBlockTokens) * E + e] +
+                    local_rank[(size_t)t * K + lane];
+      if (capacity < 0 || (int64_t)r < capacity) row = offsets[e] + r;
+    }
+    dest[(size_t)t * K + lane] = row;
+    if (row >= 0) perm_token[row] = t;
+  }
+
+  const uint4* src = x + (size_t)t * row_chunks;
+  for (int c0 = 0; c0 < row_chunks; c0 += kWave * kCopyUnroll) {
+    uint4 v[kCopyUnroll];
+#pragma unroll
+    for (int u = 0; u < kCopyUnroll; ++u) {
+      const int c = c0 + u * kWave + lane;
+      if (c < row_chunks) v[u] = src[c];
+    }
+    for (int k = 0; k < K; ++k) {
+      const int rk = __shfl(row, k);
+      if (rk < 0) continue;  // uniform across the wave
+      uint4* dst = x_perm + (size_t)rk * row_chunks;
+#pragma unroll
+      for (int u = 0; u < kCopyUnroll; ++u) {
+        const int c = c0 + u * kWave + lane;
+        if (c < row_chunks) dst[c] = v[u];
+      }
+    }
+  }
+}
+
+}  // namespace
+
+size_t dispatch_workspace_bytes(int N, int E, int K) {
+  const size_t B = (size_t)(N + kRankBlockTokens - 1) / kRankBlockTokens;
+  return 2 * align_up(B * E * sizeof(int32_t), 256) +
+         align_up((size_t)N * K * sizeof(int32_t), 256);
+}
+
+DispatchWorkspace dispatch_workspace(void* base, int N, int E, int K) {
+  const size_t B = (size_t)(N + kRankBlockTokens - 1) / kRankBlockTokens;
+  char* p = static_cast<char*>(base);
+  DispatchWorkspace ws;
+  ws.block_counts = reinterpret_cast<int32_t*>(p);
+  p += align_up(B * E * sizeof(int32_t), 256);
+  ws.block_excl = reinterpret_cast<int32_t*>(p);
+  p += align_up(B * E * sizeof(int32_t), 256);
+  ws.local_rank = reinterpret_cast<int32_t*>(p);
+  return ws;
+}
+
+hipError_t launch_dispatch(const void* x, size_t row_bytes, int N,
+                           const int32_t* topk_idx, int E, int K, int W,
+                           int64_t capacity, void* x_perm,
+                           int32_t* perm_token, int32_t* dest,
+                           int32_t* demand, int32_t* counts,
+                           int32_t* offsets, int32_t* rank_offsets,
+                           const DispatchWorkspace& ws, hipStream_t stream) {
+  const int B = (N + kRankBlockTokens - 1) / kRankBlockTokens;
+  const size_t lds = (size_t)kRankWaves * E * sizeof(unsigned long long);
+  dispatch_rank_kernel<<<B, kRankBlockTokens, lds, stream>>>(
+      topk_idx, N, E, K, ws.block_counts, ws.local_rank);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  dispatch_scan_kernel<<<1, kScanThreads, 0, stream>>>(
+      ws.block_counts, B, E, W, capacity, ws.block_excl, demand, counts,
+      offsets, rank_offsets);
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  const int row_chunks = (int)(row_bytes / 16);
+  const int blocks = (N + kScatterWaves - 1) / kScatterWaves;
+  dispatch_scatter_kernel<<<blocks, kScatterWaves * kWave, 0, stream>>>(
+      static_cast<const uint4*>(x), row_chunks, N, topk_idx, E, K, capacity,
+      ws.block_excl, ws.local_rank, offsets, static_cast<uint4*>(x_perm),
+      perm_token, dest);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,64 @@
+// Internal declarations shared by the HIP translation units of libmoe_route.
+// Not part of the public ABI (include/moe_route.h is).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef __bf16 bf16;
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+
+constexpr int kWave = 64;
+
+// Dispatch: tokens handled by one block of the rank kernel (one per thread).
+constexpr int kRankBlockTokens = 256;
+
+// Grouped FFN tile heights (rows of the packed buffer per tile).
+constexpr int kBf16TileRows = 128;
+constexpr int kF32TileRows = 64;
+
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// ---- launchers (each returns the hipError_t of its launches) -------------
+
+hipError_t launch_route_topk(const float* logits, int N, int E, int K,
+                             int renormalize, int32_t* topk_idx,
+                             float* topk_w, hipStream_t stream);
+
+// Workspace carve-up of moe_dispatch.
+struct DispatchWorkspace {
+  int32_t* block_counts;  // [B, E]
+  int32_t* block_excl;    // [B, E]
+  int32_t* local_rank;    // [N, K]
+};
+size_t dispatch_workspace_bytes(int N, int E, int K);
+DispatchWorkspace dispatch_workspace(void* base, int N, int E, int K);
+
+hipError_t launch_dispatch(const void* x, size_t row_bytes, int N,
+                           const int32_t* topk_idx, int E, int K, int W,
+                           int64_t capacity, void* x_perm,
+                           int32_t* perm_token, int32_t* dest,
+                           int32_t* demand, int32_t* counts,
+                           int32_t* offsets, int32_t* rank_offsets,
+                           const DispatchWorkspace& ws, hipStream_t stream);
+
+hipError_t launch_combine(const void* y_perm, bool bf16_data, int N, int d,
+                          int K, const int32_t* dest, const float* topk_w,
+                          void* out, hipStream_t stream);
+
+size_t grouped_ffn_workspace_bytes(int64_t max_rows, int E, bool bf16_data);
+
+hipError_t launch_grouped_ffn(const void* x_perm, bool bf16_data, int d,
+                              int ffn, int E, const int32_t* offsets,
+                              int64_t max_rows, const void* w_gate,
+                              const void* w_up, const void* w_down, void* h,
+                              void* y_perm, void* workspace,
+                              hipStream_t stream);
+
+}  // namespace moe

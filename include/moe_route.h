@@ -1,0 +1,195 @@
+/*
+ * moe_route.h -- C ABI of the MI355X (gfx950) MoE expert-parallel layer.
+ *
+ * One MoE layer on one GPU's share, in four calls that follow the layer's
+ * data flow as drawn in "MoE 专家并行的 All-to-All 通信瓶颈" (wiblog.cn),
+ * section "All-to-All 分发与回收的机制", flowchart: the router picks the
+ * Top-K experts (moe_route_topk); tokens are grouped and packed by
+ * destination card (moe_dispatch); each expert runs a grouped GEMM over its
+ * variable number of tokens (moe_grouped_ffn); the outputs are merged back to
+ * token order with the gate weights (moe_combine).  "MoE Inference
+ * Communication", section "系统剖析", names the same stages Gate -> dispatch
+ * -> Expert FFN -> combine -> Aggregation.  On one GPU the two all-to-all
+ * exchanges become the local pack into W virtual-rank send slices and the
+ * unpack back to token order.
+ *
+ * Conventions shared by every call
+ *   - Arrays are caller-owned DEVICE pointers, row-major and contiguous, and
+ *     16-byte aligned.  The library never allocates, never synchronises the
+ *     host and keeps no pointer after a call returns.
+ *   - Work is enqueued on `stream` (a hipStream_t passed as void*; NULL is the
+ *     default stream).  The caller keeps buffers alive until the stream has
+ *     passed them.
+ *   - Every argument check happens on the host before any launch: a non-OK
+ *     status means nothing was enqueued, except MOE_ERR_HIP, which reports a
+ *     failed launch (hipGetLastError) after enqueueing.
+ *   - moe_last_error() gives a thread-local message for the last failure.
+ *   - No global mutable state: calls are thread-safe.
+ *   - dtype is a moe_dtype_t value: MOE_DTYPE_F32 or MOE_DTYPE_BF16.  It is
+ *     the storage type of activations and weights; arithmetic accumulates in
+ *     fp32 and rounds to the storage type (round-to-nearest-even) where a
+ *     value is stored.
+ */
+#ifndef MOE_ROUTE_H
+#define MOE_ROUTE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1, /* a null pointer, a size out of range, ... */
+  MOE_ERR_UNSUPPORTED = 2, /* legal but beyond this implementation's limits */
+  MOE_ERR_WORKSPACE = 3,   /* workspace missing or too small */
+  MOE_ERR_HIP = 4          /* a HIP launch failed */
+} moe_status_t;
+
+typedef enum { MOE_DTYPE_F32 = 0, MOE_DTYPE_BF16 = 1 } moe_dtype_t;
+
+#define MOE_ABI_VERSION 1
+#define MOE_MAX_EXPERTS 1024
+#define MOE_MAX_TOPK 16
+
+/* Version of this ABI (MOE_ABI_VERSION). */
+int moe_abi_version(void);
+
+/* Static text naming a status code. */
+const char* moe_status_string(int status);
+
+/* Thread-local detail of this thread's last failed call ("" if none). */
+const char* moe_last_error(void);
+
+/*
+ * Per-expert capacity ceil(C * N * K / E), host only.
+ * "MoE 推理服务工程真相 2026", section 2.2 (Expert Capacity Factor): an expert
+ * that receives more tokens than its capacity drops the excess.  The page's
+ * formula lost its symbols; the budget here is the mean per-expert load
+ * N*K/E scaled by C and rounded up, computed exactly on the rational value of
+ * the double C.  Returns -2 if C is not finite and > 0, or N < 0, K < 1,
+ * E < 1, or the result exceeds INT64_MAX.  Callers pass -1 to moe_dispatch
+ * for a dropless layer.
+ */
+int64_t moe_capacity(double C, int64_t N, int32_t K, int32_t E);
+
+/*
+ * Top-K routing.  "MoE 专家并行的 All-to-All 通信瓶颈", section
+ * "一个反直觉的扩容结果": the router picks the Top-K experts of each token;
+ * "MoE 推理服务工程真相 2026", section 一: it yields the top-k expert weights.
+ *
+ *   logits     [N, E] fp32, finite (unchecked precondition).
+ *   topk_idx   [N, K] int32 out: the K experts with the largest logits,
+ *              best first; equal logits go to the lower expert index.
+ *   topk_w     [N, K] fp32 out: softmax probability of the chosen expert over
+ *              all E logits (max-subtracted); if renormalize != 0, divided by
+ *              the sum of the K chosen probabilities.
+ * Checks: pointers non-null; N >= 0; 1 <= K <= E (INVALID_ARG);
+ *         E <= MOE_MAX_EXPERTS, K <= MOE_MAX_TOPK (UNSUPPORTED).
+ * N == 0 enqueues nothing.
+ */
+int moe_route_topk(const float* logits, int32_t N, int32_t E, int32_t K,
+                   int32_t renormalize, int32_t* topk_idx, float* topk_w,
+                   void* stream);
+
+/* Bytes of device workspace moe_dispatch needs for these sizes. */
+size_t moe_dispatch_workspace_bytes(int32_t N, int32_t E, int32_t K);
+
+/*
+ * Dispatch: histogram, capacity drop, prefix scan and permutation of the
+ * tokens into per-expert contiguous rows laid out by destination rank.
+ * Follows the dispatch pseudocode of "MoE 推理服务工程真相 2026", section 2.3
+ * (bincount of the expert ids, overflow against the capacity, grouping for
+ * the all-to-all), the expert drop of section 4.3 (a dropped pair's output is
+ * zero), and the dense token-to-expert mapping table and cumsum of "MoE
+ * Inference Communication", section "MoE 计算核优化".
+ *
+ *   x          [N, d] activations of type dtype.
+ *   topk_idx   [N, K] int32 from moe_route_topk (distinct, in [0, E);
+ *              unchecked precondition).
+ *   W          virtual ranks; rank r owns experts [r*E/W, (r+1)*E/W).
+ *   capacity   -1 dropless, else 0 <= capacity: the r-th token (r from 0,
+ *              in token order) routed to an expert is kept iff r < capacity,
+ *              so an overflowing expert drops its later tokens.
+ *   x_perm     [N*K, d] out: row offsets[e] + r holds a bit copy of the
+ *              token that is the r-th kept token of expert e.  Rows at and
+ *              beyond offsets[E] are not written.  Rank r's send slice is rows
+ *              [rank_offsets[r], rank_offsets[r+1]).
+ *   perm_token [N*K] int32 out: row -> source token (rows < offsets[E]).
+ *   dest       [N, K] int32 out: (t, k) -> row, or -1 if dropped.
+ *   demand     [E] int32 out: tokens routed to each expert (before the drop).
+ *   counts     [E] int32 out: tokens kept per expert = min(demand, capacity).
+ *   offsets    [E+1] int32 out: exclusive prefix sum of counts.
+ *   rank_offsets [W+1] int32 out: offsets[r*E/W].
+ *   workspace  device scratch of moe_dispatch_workspace_bytes(N, E, K).
+ * Checks: pointers non-null; N >= 1; d >= 1 and d*sizeof(dtype) a multiple
+ *         of 16; 1 <= K <= E; W >= 1 and E % W == 0; capacity >= -1;
+ *         N*K < 2^31 (INVALID_ARG); E, K limits and dtype (UNSUPPORTED);
+ *         workspace (WORKSPACE).
+ */
+int moe_dispatch(const void* x, int32_t dtype, int32_t N, int32_t d,
+                 const int32_t* topk_idx, int32_t E, int32_t K, int32_t W,
+                 int64_t capacity, void* x_perm, int32_t* perm_token,
+                 int32_t* dest, int32_t* demand, int32_t* counts,
+                 int32_t* offsets, int32_t* rank_offsets, void* workspace,
+                 size_t workspace_bytes, void* stream);
+
+/* Bytes of device workspace moe_grouped_ffn needs for these sizes. */
+size_t moe_grouped_ffn_workspace_bytes(int64_t max_rows, int32_t E,
+                                       int32_t dtype);
+
+/*
+ * Ragged grouped-GEMM SwiGLU expert FFN over the packed rows: per expert e,
+ * on rows R = x_perm[offsets[e] : offsets[e+1]],
+ *   h = silu(R w_gate[e]^T) * (R w_up[e]^T)      (stored in dtype)
+ *   y = h w_down[e]^T                            (stored in dtype)
+ * with fp32 accumulation.  "MoE 专家并行的 All-to-All 通信瓶颈", flowchart
+ * step "Grouped GEMM 专家计算" and section "容量因子、专家复制与 dropless 的
+ * 取舍": one call handles every expert's variable token count, without drop
+ * or padding.  The row count M = offsets[E] stays on the device.
+ *
+ *   x_perm     [max_rows, d] from moe_dispatch.
+ *   offsets    [E+1] int32 device, from moe_dispatch; offsets[E] <= max_rows
+ *              (rows beyond max_rows are ignored).
+ *   max_rows   host-side upper bound on M (N*K for a dispatch output); sizes
+ *              the launch grid.
+ *   w_gate, w_up [E, ffn, d]; w_down [E, d, ffn] (rows contiguous along the
+ *              reduction dimension).
+ *   h          [max_rows, ffn] out (rows < offsets[E] written).
+ *   y_perm     [max_rows, d] out (rows < offsets[E] written).
+ *   workspace  device scratch of moe_grouped_ffn_workspace_bytes(...).
+ * Checks: pointers non-null; d, ffn >= 1; E >= 1; max_rows >= 0
+ *         (INVALID_ARG); bf16 needs d and ffn multiples of 64, fp32 needs
+ *         multiples of 8; E limit; max_rows < 2^31 (UNSUPPORTED); workspace
+ *         (WORKSPACE).  max_rows == 0 enqueues nothing.
+ */
+int moe_grouped_ffn(const void* x_perm, int32_t dtype, int32_t d, int32_t ffn,
+                    int32_t E, const int32_t* offsets, int64_t max_rows,
+                    const void* w_gate, const void* w_up, const void* w_down,
+                    void* h, void* y_perm, void* workspace,
+                    size_t workspace_bytes, void* stream);
+
+/*
+ * Combine: inverse permutation with the gate-weighted sum.
+ * "MoE 专家并行的 All-to-All 通信瓶颈", flowchart step "加权合并回原 token
+ * 顺序"; a dropped pair adds zero ("MoE 推理服务工程真相 2026", section 4.3).
+ *   out[t] = sum over k = 0..K-1 with dest[t,k] >= 0 of
+ *            topk_w[t,k] * y_perm[dest[t,k]]
+ * accumulated in fp32 in ascending k and rounded to dtype; a token with every
+ * pair dropped gets a zero row.
+ *   y_perm [rows, d]; dest [N, K] int32 (each >= 0 entry a valid row:
+ *   unchecked precondition); topk_w [N, K] fp32; out [N, d] of dtype.
+ * Checks: pointers non-null; N >= 1; d >= 1 and d*sizeof(dtype) a multiple
+ *         of 16; 1 <= K (INVALID_ARG); K limit and dtype (UNSUPPORTED).
+ */
+int moe_combine(const void* y_perm, int32_t dtype, int32_t N, int32_t d,
+                int32_t K, const int32_t* dest, const float* topk_w, void* out,
+                void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_ROUTE_H */

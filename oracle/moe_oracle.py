@@ -353,16 +353,17 @@ def layer(logits, x, expert_weights, K, W, cap, act, renormalize=False):
     return res
 
 
-def token_outputs(tokens, x, topk_idx, topk_w, dest, expert_weights, act):
+def token_outputs(tokens, x_tokens, topk_idx, topk_w, dest, expert_weights, act):
     """Outputs of selected tokens only, expert by expert.
 
     For layers too large to run whole on the CPU: every kept pair (t,k) of a
     selected token runs its expert's FFN on the single row x[t]; the rows are
     independent, so this equals the corresponding rows of the full layer.
+    x_tokens[i] is the hidden state of token tokens[i].
     Returns (y_rows dict (t,k) -> y [d], out [len(tokens), d]).
     """
-    x = np.asarray(x, dtype=np.float64)
     tokens = [int(t) for t in tokens]
+    xs = {t: np.asarray(x_tokens[i], dtype=np.float64) for i, t in enumerate(tokens)}
     need = {}
     for t in tokens:
         for k in range(topk_idx.shape[1]):
@@ -372,11 +373,11 @@ def token_outputs(tokens, x, topk_idx, topk_w, dest, expert_weights, act):
     for e in sorted(need):
         wg, wu, wd = expert_weights(e)
         pairs = need[e]
-        R = np.stack([x[t] for t, _ in pairs])
+        R = np.stack([xs[t] for t, _ in pairs])
         _, y = expert_ffn(R, wg, wu, wd, act)
         for i, tk in enumerate(pairs):
             y_rows[tk] = y[i]
-    d = x.shape[1]
+    d = len(next(iter(xs.values())))
     w = np.asarray(topk_w, dtype=np.float32).astype(np.float64)
     out = np.zeros((len(tokens), d), dtype=np.float64)
     for i, t in enumerate(tokens):

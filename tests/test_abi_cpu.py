@@ -1,0 +1,158 @@
+"""The C-ABI library on a machine without a GPU: it loads, exports every
+symbol the header declares, computes capacities exactly, and rejects bad
+arguments on the host before any launch.  No call here reaches a kernel."""
+import ctypes
+import os
+import re
+import random
+from fractions import Fraction
+import math
+
+import numpy as np
+import pytest
+
+from grouped_gemm_route_amd import binding as B
+from oracle import moe_oracle as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADERS = [os.path.join(ROOT, "include", f) for f in os.listdir(os.path.join(ROOT, "include"))
+           if f.endswith(".h")]
+
+FAKE = ctypes.c_void_p(4096)   # never dereferenced: every case fails its checks first
+NUL = ctypes.c_void_p(0)
+
+
+def declared_functions():
+    names = []
+    for h in HEADERS:
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names += re.findall(r"^\s*(?:[\w\*]+\s+)+\**(moe_\w+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return B.load_library()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared but not exported"
+    assert sorted(n for n, _, _ in B.SIGNATURES) == names
+
+
+def test_version_and_status_strings(lib):
+    assert lib.moe_abi_version() == 1
+    for s, text in [(0, "MOE_OK"), (1, "MOE_ERR_INVALID_ARG"), (2, "MOE_ERR_UNSUPPORTED"),
+                    (3, "MOE_ERR_WORKSPACE"), (4, "MOE_ERR_HIP"), (99, "MOE_ERR_UNKNOWN")]:
+        assert lib.moe_status_string(s).decode() == text
+
+
+def test_capacity_matches_oracle_exactly(lib):
+    rnd = random.Random(7)
+    cases = [(1.25, 8192, 8, 128), (1.0, 32768, 8, 256), (1.0, 4, 2, 4), (1.1, 10, 1, 1),
+             (float(np.nextafter(1.0, 2.0)), 1024, 1, 1), (0.5, 3, 1, 1), (1e-300, 5, 1, 7),
+             (1e-300, 0, 1, 7), (3.0, 0, 4, 2), (2.0 ** 40, 1000, 2, 3)]
+    for _ in range(2000):
+        C = rnd.choice([rnd.uniform(0.01, 4.0), rnd.randint(1, 8) / rnd.choice([1, 2, 4, 8, 3, 10]),
+                        math.ldexp(rnd.random(), rnd.randint(-60, 10))])
+        if C <= 0:
+            continue
+        cases.append((C, rnd.randint(0, 1 << 20), rnd.randint(1, 16), rnd.randint(1, 1024)))
+    for C, N, K, E in cases:
+        assert lib.moe_capacity(C, N, K, E) == O.capacity(C, N, K, E), (C, N, K, E)
+    for bad in [(0.0, 1, 1, 1), (-1.0, 1, 1, 1), (float("inf"), 1, 1, 1), (float("nan"), 1, 1, 1),
+                (1.0, -1, 1, 1), (1.0, 1, 0, 1), (1.0, 1, 1, 0), (1e300, 1 << 40, 16, 1)]:
+        assert lib.moe_capacity(*bad) == -2
+    # the bound is the exact rational ceiling, not a float computation
+    assert lib.moe_capacity(1.0, 3, 1, 3) == 1
+    assert Fraction(0.1) * 30 != 3 and lib.moe_capacity(0.1, 30, 1, 1) == math.ceil(Fraction(0.1) * 30)
+
+
+def _status(fn, *args):
+    return fn(*args)
+
+
+def test_route_rejects_bad_arguments(lib):
+    f = lib.moe_route_topk
+    assert f(NUL, 4, 8, 2, 0, FAKE, FAKE, NUL) == 1
+    assert f(FAKE, 4, 8, 2, 0, NUL, FAKE, NUL) == 1
+    assert f(FAKE, -1, 8, 2, 0, FAKE, FAKE, NUL) == 1
+    assert f(FAKE, 4, 8, 0, 0, FAKE, FAKE, NUL) == 1
+    assert f(FAKE, 4, 8, 9, 0, FAKE, FAKE, NUL) == 1          # K > E
+    assert f(FAKE, 4, 1025, 2, 0, FAKE, FAKE, NUL) == 2       # E limit
+    assert f(FAKE, 4, 32, 17, 0, FAKE, FAKE, NUL) == 2        # K limit
+    assert "K" in lib.moe_last_error().decode()
+
+
+def _dispatch(lib, **kw):
+    a = dict(x=FAKE, dtype=1, N=16, d=64, idx=FAKE, E=8, K=2, W=4, cap=-1, x_perm=FAKE,
+             perm=FAKE, dest=FAKE, demand=FAKE, counts=FAKE, offsets=FAKE, roff=FAKE,
+             ws=FAKE, ws_bytes=1 << 30)
+    a.update(kw)
+    return lib.moe_dispatch(a["x"], a["dtype"], a["N"], a["d"], a["idx"], a["E"], a["K"],
+                            a["W"], a["cap"], a["x_perm"], a["perm"], a["dest"], a["demand"],
+                            a["counts"], a["offsets"], a["roff"], a["ws"], a["ws_bytes"], NUL)
+
+
+def test_dispatch_rejects_bad_arguments(lib):
+    assert _dispatch(lib, x=NUL) == 1
+    assert _dispatch(lib, dest=NUL) == 1
+    assert _dispatch(lib, dtype=5) == 2
+    assert _dispatch(lib, N=0) == 1
+    assert _dispatch(lib, K=9) == 1
+    assert _dispatch(lib, W=3) == 1                 # E % W != 0
+    assert _dispatch(lib, W=0) == 1
+    assert _dispatch(lib, cap=-2) == 1
+    assert _dispatch(lib, d=4) == 1                 # 8 bytes per bf16 row
+    assert _dispatch(lib, dtype=0, d=2) == 1        # 8 bytes per fp32 row
+    assert _dispatch(lib, E=2048, W=8) == 2
+    assert _dispatch(lib, E=32, K=17, W=8) == 2
+    assert _dispatch(lib, N=1 << 28, K=8, E=8, W=8) == 1   # N*K >= 2^31
+    need = lib.moe_dispatch_workspace_bytes(16, 8, 2)
+    assert need > 0
+    assert _dispatch(lib, ws_bytes=need - 1) == 3
+    assert _dispatch(lib, ws=NUL) == 3
+    assert "workspace" in lib.moe_last_error().decode()
+
+
+def _ffn(lib, **kw):
+    a = dict(x=FAKE, dtype=1, d=128, ffn=128, E=8, off=FAKE, max_rows=64, wg=FAKE, wu=FAKE,
+             wd=FAKE, h=FAKE, y=FAKE, ws=FAKE, ws_bytes=1 << 30)
+    a.update(kw)
+    return lib.moe_grouped_ffn(a["x"], a["dtype"], a["d"], a["ffn"], a["E"], a["off"],
+                               a["max_rows"], a["wg"], a["wu"], a["wd"], a["h"], a["y"],
+                               a["ws"], a["ws_bytes"], NUL)
+
+
+def test_grouped_ffn_rejects_bad_arguments(lib):
+    assert _ffn(lib, wd=NUL) == 1
+    assert _ffn(lib, dtype=3) == 2
+    assert _ffn(lib, d=0) == 1
+    assert _ffn(lib, max_rows=-1) == 1
+    assert _ffn(lib, d=96) == 2                     # bf16 needs multiples of 64
+    assert _ffn(lib, dtype=0, ffn=12) == 2          # fp32 needs multiples of 8
+    assert _ffn(lib, E=1025) == 2
+    assert _ffn(lib, max_rows=1 << 31) == 2
+    need = lib.moe_grouped_ffn_workspace_bytes(64, 8, 1)
+    assert need > 0
+    assert _ffn(lib, ws_bytes=need - 1) == 3
+    assert _ffn(lib, max_rows=0, ws=NUL) == 0       # nothing to do: no launch
+
+
+def test_combine_rejects_bad_arguments(lib):
+    f = lib.moe_combine
+    assert f(NUL, 1, 4, 64, 2, FAKE, FAKE, FAKE, NUL) == 1
+    assert f(FAKE, 2, 4, 64, 2, FAKE, FAKE, FAKE, NUL) == 2
+    assert f(FAKE, 1, 0, 64, 2, FAKE, FAKE, FAKE, NUL) == 1
+    assert f(FAKE, 1, 4, 4, 2, FAKE, FAKE, FAKE, NUL) == 1
+    assert f(FAKE, 1, 4, 64, 17, FAKE, FAKE, FAKE, NUL) == 2
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    with pytest.raises(ValueError):
+        B.moe_route_topk(torch.zeros(4, 8), 2)

@@ -301,7 +301,7 @@ def test_token_outputs_equal_full_layer_rows():
     fn = lambda e: (wg[e], wu[e], wd[e])
     full = O.layer(logits, x, fn, K, W, 6, "bf16")
     toks = [0, 3, 7, 19]
-    y_rows, out = O.token_outputs(toks, x, full["topk_idx"], full["topk_w"],
+    y_rows, out = O.token_outputs(toks, x[toks], full["topk_idx"], full["topk_w"],
                                   full["dest"], fn, "bf16")
     assert np.array_equal(out, full["out"][toks])
     for (t, k), y in y_rows.items():

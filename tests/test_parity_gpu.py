@@ -1,0 +1,246 @@
+"""HIP path vs the CPU oracle, element by element, on seeded inputs.
+
+Integer results (topk_idx, demand, counts, offsets, rank_offsets, dest,
+perm_token) and the permuted payload x_perm must match bit for bit.  Floating
+results must satisfy, per element, |got - ref| <= atol + rtol * |ref| with
+  bf16 layers: atol = 2e-2, rtol = 1e-2   (h, y_perm, out)
+  fp32 layers: atol = 1e-4, rtol = 1e-4
+  gate weights: |got - ref| <= 1e-6.
+Small shapes run the whole oracle; the full-size layers run the oracle's
+route and dispatch in full and its FFN/combine on sampled tokens.
+"""
+import numpy as np
+import pytest
+import torch
+
+from grouped_gemm_route_amd import binding as B
+from grouped_gemm_route_amd import synth
+from oracle import moe_oracle as O
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"bf16": (2e-2, 1e-2), "f32": (1e-4, 1e-4)}
+W_TOL = 1e-6
+DEV = "cuda:0"
+
+
+def _np(t):
+    if t.dtype == torch.bfloat16:
+        t = t.float()
+    return t.detach().cpu().numpy()
+
+
+def _close(name, got, ref, act):
+    atol, rtol = TOL[act]
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert got.shape == ref.shape, (name, got.shape, ref.shape)
+    err = np.abs(got - ref)
+    bad = err > atol + rtol * np.abs(ref)
+    assert not bad.any(), (
+        f"{name}: {int(bad.sum())} of {bad.size} elements out of tolerance; "
+        f"max abs err {err.max():.3e}")
+
+
+def _cap(cfg):
+    if cfg.get("cap") is not None:
+        return cfg["cap"]
+    return O.capacity(cfg["C"], cfg["N"], cfg["K"], cfg["E"]) if cfg["C"] is not None else -1
+
+
+def _run_gpu(cfg, inp, cap):
+    layer = B.MoeLayer(cfg["N"], cfg["d"], cfg["ffn"], cfg["E"], cfg["K"], cfg["W"], cap,
+                       synth.TORCH_DTYPE[cfg["act"]], DEV, cfg.get("renormalize", False))
+    layer.forward(inp["logits"], inp["x"], inp["w_gate"], inp["w_up"], inp["w_down"])
+    torch.cuda.synchronize()
+    return layer
+
+
+def _expert_weights_np(inp):
+    cache = {}
+
+    def fn(e):
+        if e not in cache:
+            cache.clear()
+            cache[e] = tuple(_np(inp[k][e]) for k in ("w_gate", "w_up", "w_down"))
+        return cache[e]
+    return fn
+
+
+def _check_route_dispatch(cfg, layer, ref, x_dev):
+    assert np.array_equal(_np(layer.topk_idx), ref["topk_idx"])
+    dw = np.abs(_np(layer.topk_w).astype(np.float64) - ref["topk_w"].astype(np.float64))
+    assert dw.max() <= W_TOL, dw.max()
+    d = layer.disp
+    for k in ("demand", "counts", "offsets", "rank_offsets", "dest"):
+        assert np.array_equal(_np(d[k]), ref[k]), k
+    M = int(ref["offsets"][-1])
+    assert np.array_equal(_np(d["perm_token"])[:M], ref["perm_token"])
+    perm = torch.from_numpy(ref["perm_token"].astype(np.int64)).to(DEV)
+    assert torch.equal(d["x_perm"][:M], x_dev[perm])          # bitwise row copies
+    return M
+
+
+# ---------------------------------------------------------------------------
+# small shapes: whole oracle
+# ---------------------------------------------------------------------------
+
+SMALL = {
+    "tiny_f32": synth.config("tiny_f32"),
+    "ragged_bf16": synth.config("ragged_bf16", N=700, d=256, ffn=320, E=4, K=2, W=2,
+                                act="bf16", C=None),
+    "ragged_bf16_c0.8": synth.config("ragged_bf16_c0.8", N=700, d=256, ffn=320, E=4, K=2,
+                                     W=2, act="bf16", C=0.8),
+    "skew_bf16_c1.25": synth.config("skew_bf16_c1.25", N=512, d=128, ffn=192, E=32, K=4,
+                                    W=8, act="bf16", bias="zipf", C=1.25),
+    "single_token": synth.config("single_token", N=1, d=64, ffn=64, E=8, K=2, W=2,
+                                 act="bf16", C=None),
+    "k_equals_e": synth.config("k_equals_e", N=37, d=64, ffn=128, E=4, K=4, W=4,
+                               act="bf16", C=None),
+    "one_expert": synth.config("one_expert", N=50, d=128, ffn=64, E=1, K=1, W=1,
+                               act="bf16", C=None),
+    "capacity_zero": synth.config("capacity_zero", N=40, d=64, ffn=64, E=8, K=2, W=4,
+                                  act="bf16", cap=0),
+    "e256_small": synth.config("e256_small", N=64, d=64, ffn=64, E=256, K=8, W=8,
+                               act="bf16", C=None),
+    "e1024_k16": synth.config("e1024_k16", N=40, d=64, ffn=64, E=1024, K=16, W=8,
+                              act="bf16", C=None),
+    "f32_nonpow2": synth.config("f32_nonpow2", N=100, d=24, ffn=40, E=6, K=3, W=3,
+                                act="f32", C=1.0),
+    "renormalized": synth.config("renormalized", N=90, d=64, ffn=64, E=16, K=4, W=4,
+                                 act="bf16", C=None, renormalize=True),
+    "many_blocks_e8": synth.config("many_blocks_e8", N=1500, d=64, ffn=128, E=8, K=2, W=8,
+                                   act="bf16", C=1.1),
+}
+
+
+def _small_inputs(cfg, logits_override=None):
+    inp = synth.make_inputs(cfg, DEV)
+    if logits_override is not None:
+        inp["logits"] = logits_override.to(DEV)
+    return inp
+
+
+def _check_small(cfg, inp):
+    cap = _cap(cfg)
+    layer = _run_gpu(cfg, inp, cap)
+    ref = O.layer(_np(inp["logits"]), _np(inp["x"]), _expert_weights_np(inp), cfg["K"],
+                  cfg["W"], cap, cfg["act"], cfg.get("renormalize", False))
+    M = _check_route_dispatch(cfg, layer, ref, inp["x"])
+    if M > 0:
+        _close("h", _np(layer.h)[:M], ref["h"], cfg["act"])
+        _close("y_perm", _np(layer.y_perm)[:M], ref["y_perm"], cfg["act"])
+    _close("out", _np(layer.out), ref["out"], cfg["act"])
+    return layer, ref
+
+
+@pytest.mark.parametrize("name", sorted(SMALL))
+def test_small_layer_matches_oracle(name):
+    cfg = SMALL[name]
+    print(f"[parity] {name} {cfg}", flush=True)
+    layer, ref = _check_small(cfg, _small_inputs(cfg))
+    if name == "capacity_zero":
+        assert ref["offsets"][-1] == 0 and (_np(layer.out) == 0).all()
+
+
+def test_tied_logits_match_oracle():
+    cfg = synth.config("ties", N=300, d=64, ffn=64, E=16, K=4, W=4, act="bf16", C=1.0)
+    g = torch.Generator().manual_seed(5)
+    logits = (torch.randint(-2, 3, (cfg["N"], cfg["E"]), generator=g) * 0.5).float()
+    logits[::5] = 0.0
+    logits[1::7] = -0.0
+    _check_small(cfg, _small_inputs(cfg, logits))
+
+
+def test_unused_rows_are_not_written():
+    cfg = SMALL["ragged_bf16_c0.8"]
+    inp = _small_inputs(cfg)
+    cap = _cap(cfg)
+    layer = B.MoeLayer(cfg["N"], cfg["d"], cfg["ffn"], cfg["E"], cfg["K"], cfg["W"], cap,
+                       torch.bfloat16, DEV)
+    sentinel = torch.tensor(-12345.0, dtype=torch.bfloat16)
+    for t in (layer.disp["x_perm"], layer.h, layer.y_perm):
+        t.fill_(sentinel)
+    layer.disp["perm_token"].fill_(-7)
+    layer.forward(inp["logits"], inp["x"], inp["w_gate"], inp["w_up"], inp["w_down"])
+    torch.cuda.synchronize()
+    M = int(layer.disp["offsets"][-1])
+    assert M < cfg["N"] * cfg["K"]
+    for t in (layer.disp["x_perm"], layer.h, layer.y_perm):
+        assert bool((t[M:] == sentinel).all())
+    assert bool((layer.disp["perm_token"][M:] == -7).all())
+
+
+def test_runs_are_bitwise_deterministic():
+    cfg = SMALL["skew_bf16_c1.25"]
+    inp = _small_inputs(cfg)
+    a = _run_gpu(cfg, inp, _cap(cfg))
+    b = _run_gpu(cfg, inp, _cap(cfg))
+    M = int(a.disp["offsets"][-1])
+    for name in ("topk_idx", "topk_w", "out"):
+        assert torch.equal(getattr(a, name), getattr(b, name)), name
+    for name in ("h", "y_perm"):                      # rows >= M are never written
+        assert torch.equal(getattr(a, name)[:M], getattr(b, name)[:M]), name
+    for k in ("perm_token",):
+        assert torch.equal(a.disp[k][:M], b.disp[k][:M]), k
+    for k in ("dest", "offsets", "counts", "demand", "rank_offsets"):
+        assert torch.equal(a.disp[k], b.disp[k]), k
+    assert torch.equal(a.disp["x_perm"][:M], b.disp["x_perm"][:M])
+
+
+def test_identity_ffn_round_trip_is_bitwise():
+    # dispatch then combine with the FFN replaced by the identity and one-hot
+    # gate weights gives back x exactly (kept slot 0) or a zero row
+    cfg = SMALL["ragged_bf16_c0.8"]
+    inp = _small_inputs(cfg)
+    layer = B.MoeLayer(cfg["N"], cfg["d"], cfg["ffn"], cfg["E"], cfg["K"], cfg["W"],
+                       _cap(cfg), torch.bfloat16, DEV)
+    layer.route(inp["logits"])
+    layer.dispatch(inp["x"])
+    onehot = torch.zeros_like(layer.topk_w)
+    onehot[:, 0] = 1.0
+    out = B.moe_combine(layer.disp["x_perm"], layer.disp["dest"], onehot)
+    torch.cuda.synchronize()
+    kept0 = layer.disp["dest"][:, 0] >= 0
+    assert torch.equal(out[kept0], inp["x"][kept0])
+    assert bool((out[~kept0] == 0).all())
+
+
+# ---------------------------------------------------------------------------
+# full-size layers: full route/dispatch, sampled FFN and combine
+# ---------------------------------------------------------------------------
+
+FULL = ["dense8", "fine128_zipf_c1.25", "decode256", "prefill256_hot", "prefill256_hot_c1.0"]
+SAMPLES = {"dense8": 6, "fine128_zipf_c1.25": 8, "decode256": 4, "prefill256_hot": 4,
+           "prefill256_hot_c1.0": 4}
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_layer_matches_oracle(name):
+    cfg = synth.config(name)
+    print(f"[parity] {name} {cfg}", flush=True)
+    inp = synth.make_inputs(cfg, DEV)
+    cap = _cap(cfg)
+    layer = _run_gpu(cfg, inp, cap)
+    logits = _np(inp["logits"])
+    idx, w = O.route(logits, cfg["K"])
+    ref = O.dispatch(idx, cfg["E"], cfg["W"], cap)
+    ref.update(topk_idx=idx, topk_w=w)
+    M = _check_route_dispatch(cfg, layer, ref, inp["x"])
+    print(f"[parity] {name}: M={M} dropped={ref['dropped']}", flush=True)
+
+    rng = np.random.default_rng(0)
+    n = SAMPLES[name]
+    toks = sorted(set([0, cfg["N"] - 1] + rng.choice(cfg["N"], n, replace=False).tolist()))
+    # include a token that lost a slot to the capacity, if any
+    dropped_t = np.nonzero((ref["dest"] < 0).any(1))[0]
+    if len(dropped_t):
+        toks = sorted(set(toks + [int(dropped_t[0]), int(dropped_t[-1])]))
+    xs = _np(inp["x"][torch.tensor(toks, device=DEV)])
+    y_rows, out_ref = O.token_outputs(toks, xs, idx, w, ref["dest"],
+                                      _expert_weights_np(inp), cfg["act"])
+    out_got = _np(layer.out[torch.tensor(toks, device=DEV)])
+    _close("out", out_got, out_ref, cfg["act"])
+    for (t, k), y in y_rows.items():
+        row = int(ref["dest"][t, k])
+        _close(f"y_perm[{row}]", _np(layer.y_perm[row]), y, cfg["act"])
