@@ -7,11 +7,13 @@
 // offsets[e+1]]:  h = silu(R Wg[e]^T) * (R Wu[e]^T);  y = h Wd[e]^T.
 //
 // Scheduling.  A one-block kernel turns offsets[] (which stays on the device)
-// into a list of row tiles (expert, first row, end row), each at most
-// kTileRows rows of one expert.  The GEMM grid is sized on the host from the
-// upper bound max_rows; block (n_tile, slot) with slot >= the real tile count
-// exits at once.  Slots vary fastest, so the blocks that run together share
-// one weight tile (the large operand) and it is fetched from HBM about once.
+// into row tiles (expert, first row, end row) of at most BM rows of one
+// expert, plus each expert's first tile.  The GEMM grid is sized on the host
+// from the upper bound max_rows; blocks beyond the real work exit at once.
+// Work is ordered expert-major, then output-column tile, then the expert's
+// row tiles, and renumbered so that each XCD (block b runs on XCD b % 8)
+// takes one contiguous run of that order: the blocks resident on an XCD
+// share one weight tile and a few token tiles through its L2.
 //
 // bf16 GEMM (gfx950 MFMA v_mfma_f32_32x32x16_bf16, fp32 accumulate).  Both
 // operands are contiguous along the reduction dimension (x_perm and h rows;
@@ -19,17 +21,19 @@
 // is the MFMA "A" operand (32 output features) and the activations the "B"
 // operand (32 tokens): each lane's accumulator then holds runs of 4
 // consecutive features of one token, which the epilogue stores as 8 bytes.
-//   block tile: 128 tokens x 256 weight rows x 64 reduction elements;
-//     the gate/up pass loads 128 gate rows and the same 128 up rows, so a
-//     wave holds matching gate and up accumulators and applies SwiGLU in
-//     registers; the down pass loads 256 rows of Wd.
-//   4 waves in 2 x 2; each wave: 4 weight tiles x 2 token tiles of 32 x 32.
-//   LDS: two stages of (256 + 128) rows x 128 bytes = 96 KB; 16-byte chunks
-//     XOR-swizzled by (row & 7) so the 8 lanes of an LDS read phase hit 8
-//     different bank groups.
-//   pipeline: the next reduction tile is loaded to registers while the
-//     current one feeds the MFMAs, then written to the other LDS stage; one
-//     barrier per reduction tile.
+//   block tile: BM tokens x 256 weight rows x 64 reduction elements, BM =
+//     256 / 128 / 32 chosen from the mean rows per expert; the gate/up pass
+//     loads 128 gate rows and the same 128 up rows, so a wave holds matching
+//     gate and up accumulators and applies SwiGLU in registers; the down
+//     pass loads 256 rows of Wd.
+//   4 waves; at BM = 256 each wave owns 128 tokens x 128 weight rows
+//     (16 accumulators of 32 x 32, 256 AGPRs).
+//   LDS: two stages of (256 + BM) rows x 128 bytes (128 KB at BM = 256);
+//     16-byte chunks XOR-swizzled by (row & 7) so the 8 lanes of an LDS read
+//     phase hit 8 different bank groups.
+//   pipeline: buffer loads of the next reduction tile are issued before the
+//     current tile's MFMAs (a scheduling barrier keeps them there), then
+//     written to the other LDS stage; one barrier per reduction tile.
 // fp32 path: a plain LDS-tiled FMA kernel (64 x 64 tiles), used for fp32
 // layers, which are small.
 #include "moe_internal.h"
@@ -46,9 +50,26 @@ constexpr int kThreads = 256;
 // tile schedule
 // ---------------------------------------------------------------------------
 
+// Workspace layout: [num_tiles | pad to 256 B][tile_start[E+1] | pad][tiles].
+struct FfnWorkspace {
+  int* num_tiles;
+  int* tile_start;  // tiles of expert e are slots [tile_start[e], tile_start[e+1])
+  int4* tiles;      // (expert, first row, end row, 0)
+};
+
+inline FfnWorkspace ffn_workspace(void* base, int E) {
+  char* p = static_cast<char*>(base);
+  FfnWorkspace ws;
+  ws.num_tiles = reinterpret_cast<int*>(p);
+  ws.tile_start = reinterpret_cast<int*>(p + 256);
+  ws.tiles = reinterpret_cast<int4*>(p + 256 + align_up((size_t)(E + 1) * sizeof(int), 256));
+  return ws;
+}
+
 __global__ __launch_bounds__(1024) void ffn_schedule_kernel(
     const int32_t* __restrict__ offsets, int E, int tile_rows, int max_rows,
-    int max_tiles, int4* __restrict__ tiles, int* __restrict__ num_tiles) {
+    int max_tiles, int4* __restrict__ tiles, int* __restrict__ tile_start,
+    int* __restrict__ num_tiles) {
   __shared__ int wave_sums[1024 / kWave];
   const int e = threadIdx.x;
   int a = 0, b = 0, nt = 0;
@@ -59,6 +80,8 @@ __global__ __launch_bounds__(1024) void ffn_schedule_kernel(
   }
   int total = 0;
   const int base = block_exclusive_scan(nt, wave_sums, &total);
+  if (e < E) tile_start[e] = min(base, max_tiles);
+  if (e == 0) tile_start[E] = min(total, max_tiles);
   for (int i = 0; i < nt; ++i) {
     const int slot = base + i;
     if (slot < max_tiles) {
@@ -74,33 +97,76 @@ inline int max_tiles_for(int64_t max_rows, int E, int tile_rows) {
                (max_rows < E ? max_rows : E));
 }
 
+// Block -> (tile slot, output column tile).  The first round_up(total, 8)
+// blocks carry work; block b runs on XCD b % 8, so blocks are renumbered to
+// give every XCD one contiguous run of the work order.  The work order is
+// expert-major, then column tile, then the expert's row tiles, so the blocks
+// that an XCD runs together read the same weight tile and the same few row
+// tiles from its L2.  Returns false for blocks without work.
+__device__ __forceinline__ bool map_block(const int* __restrict__ tile_start,
+                                          const int* __restrict__ num_tiles_p,
+                                          int E, int n_tiles, int* slot,
+                                          int* n_tile) {
+  const int total = n_tiles * *num_tiles_p;
+  const int per_xcd = (total + 7) / 8;
+  const int b = blockIdx.x;
+  if (b >= per_xcd * 8) return false;
+  const int L = (b % 8) * per_xcd + b / 8;
+  if (L >= total) return false;
+  int lo = 0, hi = E;  // largest e with n_tiles * tile_start[e] <= L
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (n_tiles * tile_start[mid] <= L) lo = mid; else hi = mid;
+  }
+  const int first = tile_start[lo];
+  const int cnt = tile_start[lo + 1] - first;
+  const int r = L - n_tiles * first;
+  *n_tile = r / cnt;
+  *slot = first + r % cnt;
+  return true;
+}
+
 // ---------------------------------------------------------------------------
 // bf16 MFMA GEMM
 // ---------------------------------------------------------------------------
 
-constexpr int kBM = kBf16TileRows;  // 128 token rows
+// Buffer descriptor word 3 for raw (untyped) buffer loads on CDNA.
+constexpr int kBufferFlags = 0x00020000;
+
 constexpr int kBW = 256;            // weight rows per block tile
 constexpr int kBK = 64;             // reduction elements per stage
 constexpr int kWElems = kBW * kBK;
-constexpr int kAElems = kBM * kBK;
-constexpr int kStageElems = kWElems + kAElems;
-constexpr size_t kBf16Lds = 2 * kStageElems * sizeof(bf16);  // 96 KB
 
 // Element offset of 16-byte chunk `chunk` (0..7) of LDS row `row`.
 __device__ __forceinline__ int swz(int row, int chunk) {
   return row * kBK + ((chunk ^ (row & 7)) << 3);
 }
 
-template <bool kDual>
+// Geometry of a block tile of BM token rows x 256 weight rows, 4 waves laid
+// out WM (along tokens) x 4/WM (along weight rows).
+template <int BM, int WM>
+struct TileGeo {
+  static constexpr int kWN = 4 / WM;
+  static constexpr int kTM = BM / WM / 32;   // 32-token MFMA tiles per wave
+  static constexpr int kTW = kBW / kWN / 32; // 32-row weight MFMA tiles per wave
+  static constexpr int kAElems = BM * kBK;
+  static constexpr int kStage = kWElems + kAElems;
+  static constexpr int kWLoads = kWElems / 8 / kThreads;
+  static constexpr int kALoads = kAElems / 8 / kThreads;
+  static constexpr size_t kLds = 2 * (size_t)kStage * sizeof(bf16);
+  static_assert(kALoads >= 1 && kTM >= 1 && kTW >= 2, "tile shape");
+};
+
+template <int BM, int WM, bool kDual>
 __global__ __launch_bounds__(kThreads, 1) void ffn_gemm_bf16_kernel(
     const bf16* __restrict__ act, int Kdim, const bf16* __restrict__ w0,
     const bf16* __restrict__ w1, int Nout, bf16* __restrict__ out,
-    const int4* __restrict__ tiles, const int* __restrict__ num_tiles,
-    int m_slots) {
+    const int4* __restrict__ tiles, const int* __restrict__ tile_start,
+    const int* __restrict__ num_tiles, int E, int n_tiles) {
+  using G = TileGeo<BM, WM>;
   extern __shared__ __attribute__((aligned(16))) bf16 lds[];
-  const int slot = blockIdx.x % m_slots;
-  const int n_tile = blockIdx.x / m_slots;
-  if (slot >= *num_tiles) return;
+  int slot, n_tile;
+  if (!map_block(tile_start, num_tiles, E, n_tiles, &slot, &n_tile)) return;
   const int4 tile = tiles[slot];
   const int e = tile.x;
   const int row0 = tile.y;
@@ -114,118 +180,134 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_gemm_bf16_kernel(
   const int ld_row = tid >> 3;   // 0..31
   const int ld_chunk = tid & 7;  // 16-byte chunk within a 128-byte row
 
-  // Global sources of this thread's 8 weight rows and 4 token rows.
-  const size_t wbase = (size_t)e * Nout * Kdim;
-  const bf16* wsrc[8];
-  int w_off[8];
+  // Global sources through buffer descriptors: one per weight matrix of this
+  // expert and one for this tile's token rows.  A load past a descriptor's
+  // size returns zeros, so edge rows (weight rows >= Nout, token rows >=
+  // rows) need no clamping; their results are never stored.  The per-thread
+  // byte offsets stay fixed and the reduction position rides in the scalar
+  // offset.
+  const size_t wexp = (size_t)e * Nout * Kdim;
+  const uint32_t wbytes = (uint32_t)((size_t)Nout * Kdim * sizeof(bf16));
+  const __amdgpu_buffer_rsrc_t wr0 =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(w0 + wexp), 0, wbytes, kBufferFlags);
+  const __amdgpu_buffer_rsrc_t wr1 = kDual
+      ? __builtin_amdgcn_make_buffer_rsrc((void*)(w1 + wexp), 0, wbytes, kBufferFlags)
+      : wr0;
+  const __amdgpu_buffer_rsrc_t ar = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(act + (size_t)row0 * Kdim), 0,
+      (uint32_t)((size_t)rows * Kdim * sizeof(bf16)), kBufferFlags);
+  int w_src[G::kWLoads], w_dst[G::kWLoads];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < G::kWLoads; ++i) {
     const int lr = i * 32 + ld_row;
-    int n;
-    const bf16* base;
+    const int n = kDual ? n0 + (lr & (kBW / 2 - 1)) : n0 + lr;
+    w_src[i] = (n * Kdim + ld_chunk * 8) * (int)sizeof(bf16);
+    w_dst[i] = swz(lr, ld_chunk);
+  }
+  int a_src[G::kALoads], a_dst[G::kALoads];
+#pragma unroll
+  for (int i = 0; i < G::kALoads; ++i) {
+    const int lr = i * 32 + ld_row;
+    a_src[i] = (lr * Kdim + ld_chunk * 8) * (int)sizeof(bf16);
+    a_dst[i] = kWElems + swz(lr, ld_chunk);
+  }
+
+  // Wave tiling.  In the gate/up pass the first half of a wave's weight
+  // tiles are gate rows and the second half the up rows of the same output
+  // features, so SwiGLU pairs accumulator i with i + kTW / 2.
+  const int wm = wave % WM;
+  const int wn = wave / WM;
+  int wrow[G::kTW];
+#pragma unroll
+  for (int i = 0; i < G::kTW; ++i) {
     if (kDual) {
-      n = n0 + (lr & (kBW / 2 - 1));
-      base = lr < kBW / 2 ? w0 : w1;
+      constexpr int kHalf = G::kTW / 2;
+      wrow[i] = (i / kHalf) * (kBW / 2) + wn * (kBW / 2 / G::kWN) + (i % kHalf) * 32;
     } else {
-      n = n0 + lr;
-      base = w0;
+      wrow[i] = wn * (kBW / G::kWN) + i * 32;
     }
-    n = min(n, Nout - 1);  // rows past the edge are loaded but not stored
-    wsrc[i] = base + wbase + (size_t)n * Kdim + ld_chunk * 8;
-    w_off[i] = swz(lr, ld_chunk);
   }
-  const bf16* asrc[4];
-  int a_off[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int lr = i * 32 + ld_row;
-    const int r = row0 + min(lr, rows - 1);
-    asrc[i] = act + (size_t)r * Kdim + ld_chunk * 8;
-    a_off[i] = kWElems + swz(lr, ld_chunk);
-  }
-
-  uint4 wreg[8], areg[4];
-  auto gload = [&](int k0) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) wreg[i] = *reinterpret_cast<const uint4*>(wsrc[i] + k0);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) areg[i] = *reinterpret_cast<const uint4*>(asrc[i] + k0);
-  };
-  auto lstore = [&](int stage) {
-    bf16* s = lds + stage * kStageElems;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) *reinterpret_cast<uint4*>(s + w_off[i]) = wreg[i];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(s + a_off[i]) = areg[i];
-  };
-
-  // Wave tiling: wm picks 64 of the 128 tokens, wn half of the weight rows.
-  const int wm = wave & 1;
-  const int wn = wave >> 1;
-  int wrow[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    wrow[i] = kDual ? (i >> 1) * (kBW / 2) + wn * 64 + (i & 1) * 32 : wn * 128 + i * 32;
-  const int arow0 = wm * 64;
+  const int arow0 = wm * (BM / WM);
   const int lrow = lane & 31;
   const int lhalf = lane >> 5;
 
-  f32x16 acc[4][2];
+  f32x16 acc[G::kTW][G::kTM];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < G::kTW; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < G::kTM; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  const int nk = Kdim / kBK;
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) gload((kt + 1) * kBK);
-    const bf16* s = lds + cur * kStageElems;
-#pragma unroll
-    for (int ks = 0; ks < kBK / 16; ++ks) {
-      const int chunk = ks * 2 + lhalf;
-      bf16x8 af[4], bfr[2];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        af[i] = *reinterpret_cast<const bf16x8*>(s + swz(wrow[i] + lrow, chunk));
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-        bfr[j] = *reinterpret_cast<const bf16x8*>(s + kWElems + swz(arow0 + j * 32 + lrow, chunk));
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-    }
-    if (kt + 1 < nk) lstore(cur ^ 1);
-    __syncthreads();
+#define MOE_GLOAD(k0)                                                        \
+  _Pragma("unroll") for (int i = 0; i < G::kWLoads; ++i) wreg[i] =             \
+      __builtin_amdgcn_raw_buffer_load_b128(                                   \
+          (kDual && i >= G::kWLoads / 2) ? wr1 : wr0, w_src[i],                \
+          (k0) * (int)sizeof(bf16), 0);                                        \
+  _Pragma("unroll") for (int i = 0; i < G::kALoads; ++i) areg[i] =             \
+      __builtin_amdgcn_raw_buffer_load_b128(ar, a_src[i],                      \
+                                            (k0) * (int)sizeof(bf16), 0);
+#define MOE_LSTORE(stage)                                                    \
+  _Pragma("unroll") for (int i = 0; i < G::kWLoads; ++i)                       \
+      *reinterpret_cast<u32x4*>(lds + (stage) * G::kStage + w_dst[i]) = wreg[i]; \
+  _Pragma("unroll") for (int i = 0; i < G::kALoads; ++i)                       \
+      *reinterpret_cast<u32x4*>(lds + (stage) * G::kStage + a_dst[i]) = areg[i];
+#define MOE_COMPUTE(stage)                                                   \
+  _Pragma("unroll") for (int ks = 0; ks < kBK / 16; ++ks) {                    \
+    const bf16* s_ = lds + (stage) * G::kStage;                                \
+    const int chunk = ks * 2 + lhalf;                                          \
+    bf16x8 af[G::kTW], bfr[G::kTM];                                            \
+    _Pragma("unroll") for (int i = 0; i < G::kTW; ++i) af[i] =                 \
+        *reinterpret_cast<const bf16x8*>(s_ + swz(wrow[i] + lrow, chunk));     \
+    _Pragma("unroll") for (int j = 0; j < G::kTM; ++j) bfr[j] =                \
+        *reinterpret_cast<const bf16x8*>(s_ + kWElems +                        \
+                                         swz(arow0 + j * 32 + lrow, chunk));   \
+    _Pragma("unroll") for (int i = 0; i < G::kTW; ++i)                         \
+        _Pragma("unroll") for (int j = 0; j < G::kTM; ++j) acc[i][j] =         \
+            __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j],  \
+                                                   0, 0, 0);                   \
   }
 
-  // Epilogue.  Accumulator register r of lane l holds feature
+  u32x4 wreg[G::kWLoads], areg[G::kALoads];
+  const int nk = Kdim / kBK;
+  MOE_GLOAD(0)
+  MOE_LSTORE(0)
+  __syncthreads();
+  for (int kt = 0; kt < nk - 1; ++kt) {
+    MOE_GLOAD((kt + 1) * kBK)
+    // keep the next tile's loads in flight across this tile's MFMAs: stop
+    // the scheduler from sinking them next to their LDS stores
+    __builtin_amdgcn_sched_barrier(0);
+    MOE_COMPUTE(kt & 1)
+    MOE_LSTORE((kt + 1) & 1)
+    __syncthreads();
+  }
+  MOE_COMPUTE((nk - 1) & 1)
+#undef MOE_GLOAD
+#undef MOE_LSTORE
+#undef MOE_COMPUTE
+
+  // Epilogue.  Accumulator register r of lane l holds weight row
   // (r / 4) * 8 + (l / 32) * 4 + r % 4 of its 32-row weight tile and token
-  // l % 32 of its 32-row token tile.
+  // l % 32 of its 32-row token tile: runs of 4 consecutive output features.
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
+  for (int j = 0; j < G::kTM; ++j) {
     const int m_local = arow0 + j * 32 + lrow;
     if (m_local >= rows) continue;
     bf16* orow = out + (size_t)(row0 + m_local) * Nout;
     if (kDual) {
+      constexpr int kHalf = G::kTW / 2;
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
+      for (int i = 0; i < kHalf; ++i) {
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
-          const int f = n0 + wn * 64 + i * 32 + r4 * 8 + lhalf * 4;
+          const int f = n0 + wrow[i] + r4 * 8 + lhalf * 4;
           if (f >= Nout) continue;
           bf16x4 o;
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const float g = acc[i][j][r4 * 4 + q];
-            const float u = acc[i + 2][j][r4 * 4 + q];
+            const float u = acc[i + kHalf][j][r4 * 4 + q];
             o[q] = (bf16)(g / (1.0f + __expf(-g)) * u);
           }
           *reinterpret_cast<bf16x4*>(orow + f) = o;
@@ -233,10 +315,10 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_gemm_bf16_kernel(
       }
     } else {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < G::kTW; ++i) {
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
-          const int f = n0 + wn * 128 + i * 32 + r4 * 8 + lhalf * 4;
+          const int f = n0 + wrow[i] + r4 * 8 + lhalf * 4;
           if (f >= Nout) continue;
           bf16x4 o;
 #pragma unroll
@@ -260,14 +342,13 @@ template <bool kDual>
 __global__ __launch_bounds__(kThreads) void ffn_gemm_f32_kernel(
     const float* __restrict__ act, int Kdim, const float* __restrict__ w0,
     const float* __restrict__ w1, int Nout, float* __restrict__ out,
-    const int4* __restrict__ tiles, const int* __restrict__ num_tiles,
-    int m_slots) {
+    const int4* __restrict__ tiles, const int* __restrict__ tile_start,
+    const int* __restrict__ num_tiles, int E, int n_tiles) {
   __shared__ float a_s[kFK][kFM + 1];
   __shared__ float w0_s[kFK][kFN + 1];
   __shared__ float w1_s[kDual ? kFK : 1][kFN + 1];
-  const int slot = blockIdx.x % m_slots;
-  const int n_tile = blockIdx.x / m_slots;
-  if (slot >= *num_tiles) return;
+  int slot, n_tile;
+  if (!map_block(tile_start, num_tiles, E, n_tiles, &slot, &n_tile)) return;
   const int4 tile = tiles[slot];
   const int e = tile.x;
   const int row0 = tile.y;
@@ -327,27 +408,64 @@ __global__ __launch_bounds__(kThreads) void ffn_gemm_f32_kernel(
   }
 }
 
-std::once_flag g_lds_once;
-hipError_t g_lds_status = hipSuccess;
-
-hipError_t ensure_lds_attributes() {
-  std::call_once(g_lds_once, [] {
-    hipError_t e1 = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&ffn_gemm_bf16_kernel<true>),
-        hipFuncAttributeMaxDynamicSharedMemorySize, (int)kBf16Lds);
-    hipError_t e2 = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&ffn_gemm_bf16_kernel<false>),
-        hipFuncAttributeMaxDynamicSharedMemorySize, (int)kBf16Lds);
-    g_lds_status = e1 != hipSuccess ? e1 : e2;
+template <int BM, int WM, bool kDual>
+hipError_t launch_bf16_gemm(const bf16* act, int Kdim, const bf16* w0,
+                            const bf16* w1, int Nout, bf16* out,
+                            const FfnWorkspace& ws, int E, int max_tiles,
+                            hipStream_t stream) {
+  using G = TileGeo<BM, WM>;
+  static std::once_flag once;
+  static hipError_t attr = hipSuccess;
+  std::call_once(once, [] {
+    attr = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&ffn_gemm_bf16_kernel<BM, WM, kDual>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, (int)G::kLds);
   });
-  return g_lds_status;
+  if (attr != hipSuccess) return attr;
+  constexpr int kNOut = kDual ? kBW / 2 : kBW;
+  const int n_tiles = (Nout + kNOut - 1) / kNOut;
+  const long long blocks = (long long)n_tiles * max_tiles;
+  const int grid = (int)((blocks + 7) / 8 * 8);
+  ffn_gemm_bf16_kernel<BM, WM, kDual><<<grid, kThreads, G::kLds, stream>>>(
+      act, Kdim, w0, w1, Nout, out, ws.tiles, ws.tile_start, ws.num_tiles, E,
+      n_tiles);
+  return hipGetLastError();
+}
+
+template <int BM, int WM>
+hipError_t launch_bf16_ffn(const void* x_perm, int d, int ffn, int E,
+                           const void* w_gate, const void* w_up,
+                           const void* w_down, void* h, void* y_perm,
+                           const FfnWorkspace& ws, int max_tiles,
+                           hipStream_t stream) {
+  hipError_t err = launch_bf16_gemm<BM, WM, true>(
+      static_cast<const bf16*>(x_perm), d, static_cast<const bf16*>(w_gate),
+      static_cast<const bf16*>(w_up), ffn, static_cast<bf16*>(h), ws, E,
+      max_tiles, stream);
+  if (err != hipSuccess) return err;
+  return launch_bf16_gemm<BM, WM, false>(
+      static_cast<const bf16*>(h), ffn, static_cast<const bf16*>(w_down),
+      nullptr, d, static_cast<bf16*>(y_perm), ws, E, max_tiles, stream);
+}
+
+// Row-tile height for the bf16 path, from what the host knows: the mean
+// rows per expert if every row bound were used.  Decode-sized layers (a few
+// rows per expert) take 32-row tiles, mid-sized 128, large 256.
+int bf16_tile_rows(int64_t max_rows, int E) {
+  const int64_t used = max_rows < E ? max_rows : E;
+  const int64_t mean = used > 0 ? max_rows / used : 0;
+  if (mean >= 192) return 256;
+  if (mean >= 48) return 128;
+  return 32;
 }
 
 }  // namespace
 
 size_t grouped_ffn_workspace_bytes(int64_t max_rows, int E, bool bf16_data) {
-  const int tr = bf16_data ? kBf16TileRows : kF32TileRows;
-  return 256 + (size_t)max_tiles_for(max_rows, E, tr) * sizeof(int4);
+  // sized for the smallest row tile, so it covers every tile choice
+  const int tr = bf16_data ? 32 : kF32TileRows;
+  return 256 + align_up((size_t)(E + 1) * sizeof(int), 256) +
+         (size_t)max_tiles_for(max_rows, E, tr) * sizeof(int4);
 }
 
 hipError_t launch_grouped_ffn(const void* x_perm, bool bf16_data, int d,
@@ -357,42 +475,39 @@ hipError_t launch_grouped_ffn(const void* x_perm, bool bf16_data, int d,
                               void* y_perm, void* workspace,
                               hipStream_t stream) {
   if (max_rows == 0) return hipSuccess;
-  const int tr = bf16_data ? kBf16TileRows : kF32TileRows;
-  const int m_slots = max_tiles_for(max_rows, E, tr);
-  int* num_tiles = static_cast<int*>(workspace);
-  int4* tiles = reinterpret_cast<int4*>(static_cast<char*>(workspace) + 256);
+  const int tr = bf16_data ? bf16_tile_rows(max_rows, E) : kF32TileRows;
+  const int max_tiles = max_tiles_for(max_rows, E, tr);
+  const FfnWorkspace ws = ffn_workspace(workspace, E);
   ffn_schedule_kernel<<<1, 1024, 0, stream>>>(offsets, E, tr, (int)max_rows,
-                                              m_slots, tiles, num_tiles);
+                                              max_tiles, ws.tiles,
+                                              ws.tile_start, ws.num_tiles);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
 
   if (bf16_data) {
-    err = ensure_lds_attributes();
-    if (err != hipSuccess) return err;
-    const int n_up = (ffn + kBW / 2 - 1) / (kBW / 2);
-    ffn_gemm_bf16_kernel<true><<<n_up * m_slots, kThreads, kBf16Lds, stream>>>(
-        static_cast<const bf16*>(x_perm), d, static_cast<const bf16*>(w_gate),
-        static_cast<const bf16*>(w_up), ffn, static_cast<bf16*>(h), tiles,
-        num_tiles, m_slots);
-    err = hipGetLastError();
-    if (err != hipSuccess) return err;
-    const int n_dn = (d + kBW - 1) / kBW;
-    ffn_gemm_bf16_kernel<false><<<n_dn * m_slots, kThreads, kBf16Lds, stream>>>(
-        static_cast<const bf16*>(h), ffn, static_cast<const bf16*>(w_down),
-        nullptr, d, static_cast<bf16*>(y_perm), tiles, num_tiles, m_slots);
-    return hipGetLastError();
+    if (tr == 256)
+      return launch_bf16_ffn<256, 2>(x_perm, d, ffn, E, w_gate, w_up, w_down, h,
+                                     y_perm, ws, max_tiles, stream);
+    if (tr == 128)
+      return launch_bf16_ffn<128, 2>(x_perm, d, ffn, E, w_gate, w_up, w_down, h,
+                                     y_perm, ws, max_tiles, stream);
+    return launch_bf16_ffn<32, 1>(x_perm, d, ffn, E, w_gate, w_up, w_down, h,
+                                  y_perm, ws, max_tiles, stream);
   }
   const int n_up = (ffn + kFN - 1) / kFN;
-  ffn_gemm_f32_kernel<true><<<n_up * m_slots, kThreads, 0, stream>>>(
+  const int g_up = (int)(((long long)n_up * max_tiles + 7) / 8 * 8);
+  ffn_gemm_f32_kernel<true><<<g_up, kThreads, 0, stream>>>(
       static_cast<const float*>(x_perm), d, static_cast<const float*>(w_gate),
-      static_cast<const float*>(w_up), ffn, static_cast<float*>(h), tiles,
-      num_tiles, m_slots);
+      static_cast<const float*>(w_up), ffn, static_cast<float*>(h), ws.tiles,
+      ws.tile_start, ws.num_tiles, E, n_up);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   const int n_dn = (d + kFN - 1) / kFN;
-  ffn_gemm_f32_kernel<false><<<n_dn * m_slots, kThreads, 0, stream>>>(
+  const int g_dn = (int)(((long long)n_dn * max_tiles + 7) / 8 * 8);
+  ffn_gemm_f32_kernel<false><<<g_dn, kThreads, 0, stream>>>(
       static_cast<const float*>(h), ffn, static_cast<const float*>(w_down),
-      nullptr, d, static_cast<float*>(y_perm), tiles, num_tiles, m_slots);
+      nullptr, d, static_cast<float*>(y_perm), ws.tiles, ws.tile_start,
+      ws.num_tiles, E, n_dn);
   return hipGetLastError();
 }
 
