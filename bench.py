@@ -5,9 +5,11 @@ of synthetic tokens, all four through the C ABI (libmoe_route.so), inputs
 already resident in HBM.  Prints one JSON line:
 
   value            whole-layer tokens/s (N tokens per step / time per step)
-  roofline         the grouped FFN (the dominant stage) against bf16 MFMA
-                   peak: 6*M*d*ffn flops per launch / its event-timed duration
-  stages           per-stage times, dispatch+combine GB/s against HBM peak
+  roofline         the grouped FFN call (the dominant stage: its tile-schedule,
+                   gate/up and down kernels) against bf16 MFMA peak:
+                   6*M*d*ffn flops per call / its event-timed duration
+  stages           per-stage times of the timed steps; dispatch and combine
+                   also timed alone with a cold cache (HBM GB/s vs peak)
   cpu_baseline     the CPU oracle on a bounded sample of the same workload
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
@@ -15,6 +17,7 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -29,6 +32,8 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0   # dense bf16
 FP32_PEAK_TFLOPS = 157.3
 
 DEFAULT_WORKLOAD = "dense8"
+SCRUB_MIB = 512                  # > the 256 MB last-level (MALL) cache
+FFN_SOURCE = os.path.join(ROOT, "grouped_gemm_route_amd", "csrc", "grouped_ffn.hip")
 
 
 def parse():
@@ -38,8 +43,13 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default=DEFAULT_WORKLOAD)
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-sample-tokens", type=int, default=384)
+    p.add_argument("--cpu-sample-tokens", type=int, default=4096)
     p.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"))
+    p.add_argument("--cold-reps", type=int, default=10,
+                   help="reps of the cold-cache dispatch/combine timing (0 skips it)")
+    p.add_argument("--copy-ref-mib", type=int, default=0,
+                   help="run one plain device-to-device copy of this many MiB first "
+                        "(the reference kernel for scaling HBM byte counters)")
     return p.parse_args()
 
 
@@ -62,6 +72,27 @@ def ffn_flops(cfg, M):
     return 6.0 * M * cfg["d"] * cfg["ffn"]
 
 
+def source_digest(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def load_traffic(path, workload):
+    """HBM bytes per grouped-FFN call from the counter summary, or None when
+    the summary is missing, is for another workload, or predates the current
+    kernel source."""
+    if not os.path.exists(path):
+        return None
+    try:
+        with open(path) as f:
+            tj = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if tj.get("workload") != workload or tj.get("source_sha256_16") != source_digest(FFN_SOURCE):
+        return None
+    return tj.get("bytes_per_call")
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -77,15 +108,25 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    B.load_library()
     cfg = synth.config(args.workload)
     N, d, ffn, E, K, W = (cfg[k] for k in ("N", "d", "ffn", "E", "K", "W"))
     dtype = synth.TORCH_DTYPE[cfg["act"]]
     b = 2 if cfg["act"] == "bf16" else 4
     cap = B.moe_capacity(cfg["C"], N, K, E) if cfg["C"] is not None else -1
+    stream = torch.cuda.current_stream(dev)
+
+    if args.copy_ref_mib > 0:
+        nbytes = args.copy_ref_mib << 20
+        src = torch.ones(nbytes, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     inp = synth.make_inputs(cfg, dev)
     layer = B.MoeLayer(N, d, ffn, E, K, W, cap, dtype, dev)
-    stream = torch.cuda.current_stream(dev)
 
     def step(ev=None):
         if ev is not None:
@@ -123,19 +164,58 @@ def main():
           for j, n in enumerate(names)}
     disp_b, comb_b = algorithmic_bytes(cfg, M, b)
     flops = ffn_flops(cfg, M)
-    ffn_s = st["ffn"] * 1e-3
-    achieved_tflops = flops / ffn_s / 1e12
+    achieved_tflops = flops / (st["ffn"] * 1e-3) / 1e12
     peak = MFMA_BF16_PEAK_TFLOPS if cfg["act"] == "bf16" else FP32_PEAK_TFLOPS
-    dc_gbps = (disp_b + comb_b) / ((st["dispatch"] + st["combine"]) * 1e-3) / 1e9
 
-    traffic = None
-    if os.path.exists(args.traffic_json):
-        try:
-            tj = json.load(open(args.traffic_json))
-            if tj.get("workload") == args.workload and tj.get("kernel") == "grouped_ffn":
-                traffic = tj.get("bytes_per_launch")
-        except (OSError, ValueError):
-            traffic = None
+    # Cold-cache timing of the two HBM-bound stages, outside the timed steps:
+    # before each rep a 512 MiB buffer is written and then read, so neither
+    # the stage's inputs nor dirty lines of its own are left in L2 or MALL.
+    cold = {}
+    if args.cold_reps > 0:
+        scrub = torch.empty(SCRUB_MIB << 18, dtype=torch.float32, device=dev)
+
+        def flush(i):
+            scrub.fill_(float(i))
+            scrub.sum()
+
+        for name, fn in (("dispatch", lambda: layer.dispatch(inp["x"])),
+                         ("combine", layer.combine)):
+            times = []
+            for i in range(args.cold_reps):
+                flush(i)
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                fn()
+                e1.record(stream)
+                e1.synchronize()
+                times.append(e0.elapsed_time(e1))
+            cold[name] = float(np.median(times))
+        del scrub
+        cold_dc = (disp_b + comb_b) / ((cold["dispatch"] + cold["combine"]) * 1e-3) / 1e9
+    hot_dc = (disp_b + comb_b) / ((st["dispatch"] + st["combine"]) * 1e-3) / 1e9
+
+    stages = {
+        "route_ms": st["route"],
+        "dispatch_ms": st["dispatch"],
+        "ffn_ms": st["ffn"],
+        "combine_ms": st["combine"],
+        "dispatch_bytes": disp_b,
+        "combine_bytes": comb_b,
+        "dispatch_combine_GBps_in_step": hot_dc,
+        "ffn_TFLOPs": achieved_tflops,
+        "ffn_mfma_frac": achieved_tflops / peak,
+        "tokens_per_s": {n: N / (st[n] * 1e-3) for n in names},
+    }
+    if cold:
+        stages.update({
+            "cold_dispatch_ms": cold["dispatch"],
+            "cold_combine_ms": cold["combine"],
+            "cold_dispatch_GBps": disp_b / (cold["dispatch"] * 1e-3) / 1e9,
+            "cold_combine_GBps": comb_b / (cold["combine"] * 1e-3) / 1e9,
+            "cold_dispatch_combine_GBps": cold_dc,
+            "cold_dispatch_combine_hbm_frac": cold_dc / HBM_PEAK_GBPS,
+        })
 
     result = {
         "metric": "MoE layer tokens/s on 1 MI355X; dispatch/combine GB/s; grouped-GEMM TFLOP/s",
@@ -149,7 +229,8 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16" if cfg["act"] == "bf16" else "f32",
-        "data": "synthetic (seeded N(0,1) logits and hidden states, N(0,1/fan_in) weights)",
+        "data": "synthetic (seeded N(0,1) logits and hidden states, N(0,1/sqrt(fan_in)) "
+                "weights)",
         "config": {
             "workload": f"{args.workload}: N={N} d={d} ffn={ffn} E={E} K={K} W={W} "
                         f"{cfg['act']} capacity={cap} (M={M} kept rows)",
@@ -158,53 +239,38 @@ def main():
                            "virtual-rank slices",
         },
         "roofline": {
-            "kernel": "moe_grouped_ffn (gate/up + down MFMA GEMMs)",
+            "kernel": "moe_grouped_ffn call (tile schedule + gate/up GEMM + down GEMM)",
             "bound": "mfma",
             "achieved": achieved_tflops,
             "peak": peak,
             "unit": "TFLOP/s",
             "frac": achieved_tflops / peak,
-            "traffic": traffic,
+            "traffic": load_traffic(args.traffic_json, args.workload),
         },
-        "stages": {
-            "route_ms": st["route"],
-            "dispatch_ms": st["dispatch"],
-            "ffn_ms": st["ffn"],
-            "combine_ms": st["combine"],
-            "dispatch_GBps": disp_b / (st["dispatch"] * 1e-3) / 1e9,
-            "combine_GBps": comb_b / (st["combine"] * 1e-3) / 1e9,
-            "dispatch_combine_GBps": dc_gbps,
-            "dispatch_combine_hbm_frac": dc_gbps / HBM_PEAK_GBPS,
-            "ffn_TFLOPs": achieved_tflops,
-            "ffn_mfma_frac": achieved_tflops / peak,
-            "tokens_per_s": {n: N / (st[n] * 1e-3) for n in names},
-        },
+        "stages": stages,
     }
 
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(cfg, inp, cap, args.cpu_sample_tokens)
+        result["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_sample_tokens)
     print(json.dumps(result))
 
 
-def cpu_baseline(cfg, inp, cap, n_tok):
+def cpu_baseline(cfg, inp, n_tok):
     """The oracle, untouched, on the first n_tok tokens of the same workload."""
-    import numpy as np
-    import torch
-
     from oracle import moe_oracle as O
 
     n = min(n_tok, cfg["N"])
     logits = inp["logits"][:n].cpu().numpy()
     x = inp["x"][:n].float().cpu().numpy()
-    wts = {}
+    cache = {}
 
     def weights(e):
-        if e not in wts:
-            wts.clear()
-            wts[e] = tuple(inp[k][e].float().cpu().numpy() for k in ("w_gate", "w_up", "w_down"))
-        return wts[e]
+        if e not in cache:
+            cache.clear()
+            cache[e] = tuple(inp[k][e].float().cpu().numpy() for k in ("w_gate", "w_up", "w_down"))
+        return cache[e]
 
-    # weights are copied to the host outside the timed region
+    # with few experts the weights are copied to the host before the clock starts
     host_w = {e: weights(e) for e in range(cfg["E"])} if cfg["E"] <= 16 else None
     fn = (lambda e: host_w[e]) if host_w is not None else weights
     cap_s = O.capacity(cfg["C"], n, cfg["K"], cfg["E"]) if cfg["C"] is not None else -1
@@ -221,9 +287,10 @@ def cpu_baseline(cfg, inp, cap, n_tok):
         "unit": "tokens/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": f"first {n} tokens of the same workload (same logits, hidden states and "
-                  f"weights; capacity recomputed for {n} tokens), whole oracle layer, "
-                  f"{dt:.1f} s; BLAS threads {threads}, host cpus {os.cpu_count()}",
+        "sample": f"first {n} of {cfg['N']} tokens of the same workload (same logits, hidden "
+                  f"states and weights; capacity recomputed for {n} tokens), whole oracle "
+                  f"layer in float64 numpy, {dt:.1f} s; BLAS threads {threads}, host cpus "
+                  f"{os.cpu_count()}",
     }
 
 

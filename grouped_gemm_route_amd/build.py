@@ -66,6 +66,10 @@ def build(verbose=True):
     if p.returncode != 0:
         raise RuntimeError(f"link failed:\n{p.stderr}")
     os.replace(tmp, LIB)
+    # a load resolves every symbol: a kernel whose host-side stub was not
+    # emitted shows up here, not at the first test
+    import ctypes
+    ctypes.CDLL(LIB)
     if verbose:
         print(f"built {LIB}")
     return LIB

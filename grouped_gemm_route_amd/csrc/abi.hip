@@ -172,6 +172,8 @@ int moe_grouped_ffn(const void* x_perm, int32_t dtype, int32_t d, int32_t ffn,
     return fail(MOE_ERR_UNSUPPORTED, "moe_grouped_ffn: bf16 needs d and ffn multiples of 64 (d=%d ffn=%d)", d, ffn);
   if (dtype == MOE_DTYPE_F32 && (d % 8 != 0 || ffn % 8 != 0))
     return fail(MOE_ERR_UNSUPPORTED, "moe_grouped_ffn: fp32 needs d and ffn multiples of 8 (d=%d ffn=%d)", d, ffn);
+  if ((int64_t)d * ffn * es >= ((int64_t)1 << 31))
+    return fail(MOE_ERR_UNSUPPORTED, "moe_grouped_ffn: one expert's weight matrix must stay below 2 GiB (d=%d ffn=%d)", d, ffn);
   if (max_rows == 0) return MOE_OK;
   const size_t need = moe::grouped_ffn_workspace_bytes(max_rows, E, dtype == MOE_DTYPE_BF16);
   if (!workspace || workspace_bytes < need)

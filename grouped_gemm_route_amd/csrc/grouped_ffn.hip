@@ -40,6 +40,7 @@
 #include "block_scan.h"
 
 #include <mutex>
+#include <type_traits>
 
 namespace moe {
 namespace {
@@ -136,8 +137,26 @@ constexpr int kBufferFlags = 0x00020000;
 constexpr int kBW = 256;            // weight rows per block tile
 constexpr int kBK = 64;             // reduction elements per stage
 constexpr int kWElems = kBW * kBK;
+constexpr int kRowBytes = kBK * (int)sizeof(bf16);  // 128: one LDS row
 
-// Element offset of 16-byte chunk `chunk` (0..7) of LDS row `row`.
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// Ask the scheduler to alternate LDS reads and MFMAs in min(R, M) even
+// groups (sched_group_barrier masks: 0x100 LDS read, 0x8 MFMA), so the reads
+// of the next reduction step never bunch up ahead of the matrix cores.
+template <int R, int M, int G = 0>
+__device__ __forceinline__ void interleave_reads_mfma() {
+  constexpr int kGroups = R < M ? R : M;
+  if constexpr (G < kGroups) {
+    __builtin_amdgcn_sched_group_barrier(0x100, R / kGroups + (G < R % kGroups ? 1 : 0), 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, M / kGroups + (G < M % kGroups ? 1 : 0), 0);
+    interleave_reads_mfma<R, M, G + 1>();
+  }
+}
+
+// Element offset of 16-byte chunk `chunk` (0..7) of LDS row `row`.  The
+// chunk is XOR-swizzled by (row & 7), so the 8 lanes of one LDS read phase,
+// which read 8 consecutive rows at one chunk, hit 8 different bank groups.
 __device__ __forceinline__ int swz(int row, int chunk) {
   return row * kBK + ((chunk ^ (row & 7)) << 3);
 }
@@ -151,8 +170,10 @@ struct TileGeo {
   static constexpr int kTW = kBW / kWN / 32; // 32-row weight MFMA tiles per wave
   static constexpr int kAElems = BM * kBK;
   static constexpr int kStage = kWElems + kAElems;
-  static constexpr int kWLoads = kWElems / 8 / kThreads;
-  static constexpr int kALoads = kAElems / 8 / kThreads;
+  // one wave-wide direct-to-LDS load moves 64 lanes x 16 bytes = 8 LDS rows;
+  // the 4 waves together fill 32 rows per round
+  static constexpr int kWLoads = kBW / 32;
+  static constexpr int kALoads = BM / 32;
   static constexpr size_t kLds = 2 * (size_t)kStage * sizeof(bf16);
   static_assert(kALoads >= 1 && kTM >= 1 && kTW >= 2, "tile shape");
 };
@@ -174,43 +195,65 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_gemm_bf16_kernel(
   constexpr int kNOut = kDual ? kBW / 2 : kBW;  // output columns per block
   const int n0 = n_tile * kNOut;
 
-  const int tid = threadIdx.x;
-  const int lane = tid & (kWave - 1);
-  const int wave = tid / kWave;
-  const int ld_row = tid >> 3;   // 0..31
-  const int ld_chunk = tid & 7;  // 16-byte chunk within a 128-byte row
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
 
-  // Global sources through buffer descriptors: one per weight matrix of this
-  // expert and one for this tile's token rows.  A load past a descriptor's
-  // size returns zeros, so edge rows (weight rows >= Nout, token rows >=
-  // rows) need no clamping; their results are never stored.  The per-thread
-  // byte offsets stay fixed and the reduction position rides in the scalar
-  // offset.
+  // Global -> LDS.  Loads go straight into LDS (buffer_load ... lds): a
+  // wave-wide load writes its 64 lanes' 16-byte pieces to 1 KB of
+  // consecutive LDS, i.e. 8 rows of 128 bytes.  Lane l fills slot l % 8 of
+  // row l / 8 of its group, and since slot s of row r must hold chunk
+  // s ^ (r & 7), the lane fetches global chunk (l % 8) ^ (l / 8).
+  // Sources are buffer descriptors (one per weight matrix of this expert,
+  // one for this tile's token rows); a load past a descriptor's size
+  // returns zeros, so edge rows (weight rows >= Nout, token rows >= rows)
+  // need no clamping and their results are never stored.  Per-lane byte
+  // offsets stay fixed; the reduction position rides in the scalar offset.
   const size_t wexp = (size_t)e * Nout * Kdim;
   const uint32_t wbytes = (uint32_t)((size_t)Nout * Kdim * sizeof(bf16));
   const __amdgpu_buffer_rsrc_t wr0 =
       __builtin_amdgcn_make_buffer_rsrc((void*)(w0 + wexp), 0, wbytes, kBufferFlags);
-  const __amdgpu_buffer_rsrc_t wr1 = kDual
-      ? __builtin_amdgcn_make_buffer_rsrc((void*)(w1 + wexp), 0, wbytes, kBufferFlags)
-      : wr0;
+  const __amdgpu_buffer_rsrc_t wr1 = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)((kDual ? w1 : w0) + wexp), 0, wbytes, kBufferFlags);
   const __amdgpu_buffer_rsrc_t ar = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(act + (size_t)row0 * Kdim), 0,
       (uint32_t)((size_t)rows * Kdim * sizeof(bf16)), kBufferFlags);
-  int w_src[G::kWLoads], w_dst[G::kWLoads];
+  const int grow = lane >> 3;                   // row within the wave's 8
+  const int gchunk = (lane & 7) ^ grow;         // pre-swizzled global chunk
+  int w_src[G::kWLoads];
 #pragma unroll
   for (int i = 0; i < G::kWLoads; ++i) {
-    const int lr = i * 32 + ld_row;
+    const int lr = (i * 4 + wave) * 8 + grow;
     const int n = kDual ? n0 + (lr & (kBW / 2 - 1)) : n0 + lr;
-    w_src[i] = (n * Kdim + ld_chunk * 8) * (int)sizeof(bf16);
-    w_dst[i] = swz(lr, ld_chunk);
+    w_src[i] = (n * Kdim + gchunk * 8) * (int)sizeof(bf16);
   }
-  int a_src[G::kALoads], a_dst[G::kALoads];
+  int a_src[G::kALoads];
 #pragma unroll
   for (int i = 0; i < G::kALoads; ++i) {
-    const int lr = i * 32 + ld_row;
-    a_src[i] = (lr * Kdim + ld_chunk * 8) * (int)sizeof(bf16);
-    a_dst[i] = kWElems + swz(lr, ld_chunk);
+    const int lr = (i * 4 + wave) * 8 + grow;
+    a_src[i] = (lr * Kdim + gchunk * 8) * (int)sizeof(bf16);
   }
+  char* const lds_bytes = reinterpret_cast<char*>(lds);
+  constexpr int kLoads = G::kWLoads + G::kALoads;  // wave-wide loads per tile
+  auto issue_load = [&](int stage, int k0, int i) {
+    char* base = lds_bytes + stage * G::kStage * (int)sizeof(bf16);
+    const int soff = k0 * (int)sizeof(bf16);
+    // (the offsets go through locals and each descriptor has its own call:
+    // an array element or a conditional expression of descriptor type as a
+    // builtin argument here drops the kernel's host-side stub)
+    if (i < G::kWLoads) {
+      const int voff = w_src[i];
+      lds_void_t* dst = (lds_void_t*)(base + (i * 4 + wave) * 8 * kRowBytes);
+      if (kDual && i >= G::kWLoads / 2)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(wr1, dst, 16, voff, soff, 0, 0);
+      else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(wr0, dst, 16, voff, soff, 0, 0);
+    } else {
+      const int voff = a_src[i - G::kWLoads];
+      lds_void_t* dst = (lds_void_t*)(base + kWElems * (int)sizeof(bf16) +
+                                      ((i - G::kWLoads) * 4 + wave) * 8 * kRowBytes);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ar, dst, 16, voff, soff, 0, 0);
+    }
+  };
 
   // Wave tiling.  In the gate/up pass the first half of a wave's weight
   // tiles are gate rows and the second half the up rows of the same output
@@ -239,53 +282,118 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_gemm_bf16_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-#define MOE_GLOAD(k0)                                                        \
-  _Pragma("unroll") for (int i = 0; i < G::kWLoads; ++i) wreg[i] =             \
-      __builtin_amdgcn_raw_buffer_load_b128(                                   \
-          (kDual && i >= G::kWLoads / 2) ? wr1 : wr0, w_src[i],                \
-          (k0) * (int)sizeof(bf16), 0);                                        \
-  _Pragma("unroll") for (int i = 0; i < G::kALoads; ++i) areg[i] =             \
-      __builtin_amdgcn_raw_buffer_load_b128(ar, a_src[i],                      \
-                                            (k0) * (int)sizeof(bf16), 0);
-#define MOE_LSTORE(stage)                                                    \
-  _Pragma("unroll") for (int i = 0; i < G::kWLoads; ++i)                       \
-      *reinterpret_cast<u32x4*>(lds + (stage) * G::kStage + w_dst[i]) = wreg[i]; \
-  _Pragma("unroll") for (int i = 0; i < G::kALoads; ++i)                       \
-      *reinterpret_cast<u32x4*>(lds + (stage) * G::kStage + a_dst[i]) = areg[i];
-#define MOE_COMPUTE(stage)                                                   \
-  _Pragma("unroll") for (int ks = 0; ks < kBK / 16; ++ks) {                    \
-    const bf16* s_ = lds + (stage) * G::kStage;                                \
-    const int chunk = ks * 2 + lhalf;                                          \
-    bf16x8 af[G::kTW], bfr[G::kTM];                                            \
-    _Pragma("unroll") for (int i = 0; i < G::kTW; ++i) af[i] =                 \
-        *reinterpret_cast<const bf16x8*>(s_ + swz(wrow[i] + lrow, chunk));     \
-    _Pragma("unroll") for (int j = 0; j < G::kTM; ++j) bfr[j] =                \
-        *reinterpret_cast<const bf16x8*>(s_ + kWElems +                        \
-                                         swz(arow0 + j * 32 + lrow, chunk));   \
-    _Pragma("unroll") for (int i = 0; i < G::kTW; ++i)                         \
-        _Pragma("unroll") for (int j = 0; j < G::kTM; ++j) acc[i][j] =         \
-            __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j],  \
-                                                   0, 0, 0);                   \
+  // LDS byte addresses of this lane's MFMA operands.  With the XOR swizzle
+  // the chunk part depends on the reduction step ks only through
+  // (ks * 2 + lane / 32) ^ (lane & 7), so one per-lane base per ks covers
+  // every operand tile (their rows differ by multiples of 32 bytes * 32).
+  int wbase[kBK / 16], abase[kBK / 16];
+#pragma unroll
+  for (int ks = 0; ks < kBK / 16; ++ks) {
+    const int chunk = ks * 2 + lhalf;
+    wbase[ks] = swz(wrow[0] + lrow, chunk) * (int)sizeof(bf16);
+    abase[ks] = (kWElems + swz(arow0 + lrow, chunk)) * (int)sizeof(bf16);
   }
 
-  u32x4 wreg[G::kWLoads], areg[G::kALoads];
+  // MFMA operands of one 16-wide reduction step, double-buffered in
+  // registers: the LDS reads of step ks + 1 are spread between the MFMAs of
+  // step ks.
+  bf16x8 wf[2][G::kTW], af[2][G::kTM];
+  constexpr int kFrags = G::kTW + G::kTM;  // LDS reads per step
+  auto read_frag = [&](int stage, int ks, int buf, int r) {
+    const char* s = reinterpret_cast<const char*>(lds) + stage * G::kStage * (int)sizeof(bf16);
+    if (r < G::kTW)
+      wf[buf][r] = *reinterpret_cast<const bf16x8*>(
+          s + wbase[ks] + (wrow[r] - wrow[0]) * kRowBytes);
+    else
+      af[buf][r - G::kTW] = *reinterpret_cast<const bf16x8*>(
+          s + abase[ks] + (r - G::kTW) * 32 * kRowBytes);
+  };
+  // MFMAs of weight tiles [I0, I1) on operand buffer `buf`.  If kReads,
+  // the kFrags operand reads of (stage, ks) into buffer rbuf are spread
+  // evenly between them, and so are the loads [L0, L1) of the next tile
+  // (into stage lstage at reduction offset lk0).  A scheduling fence after
+  // every MFMA keeps this exact order: left alone, the compiler sinks each
+  // read next to its first use and bunches the loads, leaving the matrix
+  // cores idle meanwhile.
+  auto mfma_step = [&](auto i0_c, auto i1_c, auto reads_c, auto l0_c, auto l1_c, int buf,
+                       int stage, int ks, int rbuf, int lstage, int lk0) {
+    constexpr int I0 = decltype(i0_c)::value;
+    constexpr int I1 = decltype(i1_c)::value;
+    constexpr bool kReads = decltype(reads_c)::value;
+    constexpr int L0 = decltype(l0_c)::value;
+    constexpr int L1 = decltype(l1_c)::value;
+    constexpr int n = (I1 - I0) * G::kTM;
+#pragma unroll
+    for (int m = 0; m < n; ++m) {
+#pragma unroll
+      for (int l = L0 + (m * (L1 - L0) + n - 1) / n; l < L0 + ((m + 1) * (L1 - L0) + n - 1) / n;
+           ++l)
+        issue_load(lstage, lk0, l);
+      if (kReads) {
+#pragma unroll
+        for (int r = (m * kFrags + n - 1) / n; r < ((m + 1) * kFrags + n - 1) / n; ++r)
+          read_frag(stage, ks, rbuf, r);
+      }
+      const int i = I0 + m / G::kTM;
+      const int j = m % G::kTM;
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[buf][i], af[buf][j],
+                                                          acc[i][j], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  using IC0 = std::integral_constant<int, 0>;
+  using ICH = std::integral_constant<int, G::kTW / 2>;
+  using ICW = std::integral_constant<int, G::kTW>;
+  using LH = std::integral_constant<int, kLoads / 2>;
+  using LA = std::integral_constant<int, kLoads>;
+  using YES = std::true_type;
+  using NO = std::false_type;
+
+  // One reduction tile (index kt) on LDS stage S.  The loads of the next
+  // tile go to the other stage (last read by the tile before this one,
+  // which every wave finished ahead of the barrier that closed it) and are
+  // spread over the first two steps; in the middle of the last step this
+  // wave waits for its loads and meets the others at a barrier, after which
+  // every wave's loads are visible, and the next tile's first operands are
+  // read between the last MFMAs.  The body has no branches: after the last
+  // tile the "next" loads repeat the last tile and the reads that follow are
+  // unused.
+  static_assert(kBK / 16 == 4, "four reduction steps per tile");
   const int nk = Kdim / kBK;
-  MOE_GLOAD(0)
-  MOE_LSTORE(0)
-  __syncthreads();
-  for (int kt = 0; kt < nk - 1; ++kt) {
-    MOE_GLOAD((kt + 1) * kBK)
-    // keep the next tile's loads in flight across this tile's MFMAs: stop
-    // the scheduler from sinking them next to their LDS stores
-    __builtin_amdgcn_sched_barrier(0);
-    MOE_COMPUTE(kt & 1)
-    MOE_LSTORE((kt + 1) & 1)
+  auto tile_step = [&](auto stage_c, int kt) {
+    constexpr int S = decltype(stage_c)::value;
+    const int nk0 = min(kt + 1, nk - 1) * kBK;
+    mfma_step(IC0{}, ICW{}, YES{}, IC0{}, LH{}, 0, S, 1, 1, 1 - S, nk0);
+    mfma_step(IC0{}, ICW{}, YES{}, LH{}, LA{}, 1, S, 2, 0, 1 - S, nk0);
+    mfma_step(IC0{}, ICW{}, YES{}, IC0{}, IC0{}, 0, S, 3, 1, 0, 0);
+    mfma_step(IC0{}, ICH{}, NO{}, IC0{}, IC0{}, 1, 0, 0, 0, 0, 0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
+    mfma_step(ICH{}, ICW{}, YES{}, IC0{}, IC0{}, 1, 1 - S, 0, 0, 0, 0);
+  };
+  using St0 = std::integral_constant<int, 0>;
+  using St1 = std::integral_constant<int, 1>;
+
+#pragma unroll
+  for (int l = 0; l < kLoads; ++l) issue_load(0, 0, l);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < kFrags; ++r) read_frag(0, 0, 0, r);
+  // tiles in pairs (stage 0, stage 1); an odd count starts with one tile
+  // on stage 0 and pairs (stage 1, stage 0) after it
+  if (nk & 1) {
+    tile_step(St0{}, 0);
+    for (int kt = 1; kt < nk; kt += 2) {
+      tile_step(St1{}, kt);
+      tile_step(St0{}, kt + 1);
+    }
+  } else {
+    for (int kt = 0; kt < nk; kt += 2) {
+      tile_step(St0{}, kt);
+      tile_step(St1{}, kt + 1);
+    }
   }
-  MOE_COMPUTE((nk - 1) & 1)
-#undef MOE_GLOAD
-#undef MOE_LSTORE
-#undef MOE_COMPUTE
 
   // Epilogue.  Accumulator register r of lane l holds weight row
   // (r / 4) * 8 + (l / 32) * 4 + r % 4 of its 32-row weight tile and token

@@ -162,7 +162,8 @@ size_t moe_grouped_ffn_workspace_bytes(int64_t max_rows, int32_t E,
  *   workspace  device scratch of moe_grouped_ffn_workspace_bytes(...).
  * Checks: pointers non-null; d, ffn >= 1; E >= 1; max_rows >= 0
  *         (INVALID_ARG); bf16 needs d and ffn multiples of 64, fp32 needs
- *         multiples of 8; E limit; max_rows < 2^31 (UNSUPPORTED); workspace
+ *         multiples of 8; E limit; max_rows < 2^31 and d*ffn*sizeof(dtype) < 2^31
+ *         (UNSUPPORTED); workspace
  *         (WORKSPACE).  max_rows == 0 enqueues nothing.
  */
 int moe_grouped_ffn(const void* x_perm, int32_t dtype, int32_t d, int32_t ffn,
