@@ -141,24 +141,16 @@ constexpr int kRowBytes = kBK * (int)sizeof(bf16);  // 128: one LDS row
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
-// Ask the scheduler to alternate LDS reads and MFMAs in min(R, M) even
-// groups (sched_group_barrier masks: 0x100 LDS read, 0x8 MFMA), so the reads
-// of the next reduction step never bunch up ahead of the matrix cores.
-template <int R, int M, int G = 0>
-__device__ __forceinline__ void interleave_reads_mfma() {
-  constexpr int kGroups = R < M ? R : M;
-  if constexpr (G < kGroups) {
-    __builtin_amdgcn_sched_group_barrier(0x100, R / kGroups + (G < R % kGroups ? 1 : 0), 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, M / kGroups + (G < M % kGroups ? 1 : 0), 0);
-    interleave_reads_mfma<R, M, G + 1>();
-  }
+// Element offset of 16-byte chunk `chunk` (0..7) of LDS row `row`.  An MFMA
+// operand read has 16 lanes in flight per LDS cycle (64 banks x 4 bytes),
+// reading 16 consecutive 128-byte rows at one chunk; rows r and r + 1 fall
+// in different halves of the 256-byte bank window, so XOR-ing the chunk
+// with (row / 2) & 7 puts the 16 lanes on 16 different 16-byte bank groups.
+__device__ __forceinline__ int swz_chunk(int row, int chunk) {
+  return chunk ^ ((row >> 1) & 7);
 }
-
-// Element offset of 16-byte chunk `chunk` (0..7) of LDS row `row`.  The
-// chunk is XOR-swizzled by (row & 7), so the 8 lanes of one LDS read phase,
-// which read 8 consecutive rows at one chunk, hit 8 different bank groups.
 __device__ __forceinline__ int swz(int row, int chunk) {
-  return row * kBK + ((chunk ^ (row & 7)) << 3);
+  return row * kBK + (swz_chunk(row, chunk) << 3);
 }
 
 // Geometry of a block tile of BM token rows x 256 weight rows, 4 waves laid
@@ -201,8 +193,9 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_gemm_bf16_kernel(
   // Global -> LDS.  Loads go straight into LDS (buffer_load ... lds): a
   // wave-wide load writes its 64 lanes' 16-byte pieces to 1 KB of
   // consecutive LDS, i.e. 8 rows of 128 bytes.  Lane l fills slot l % 8 of
-  // row l / 8 of its group, and since slot s of row r must hold chunk
-  // s ^ (r & 7), the lane fetches global chunk (l % 8) ^ (l / 8).
+  // row r = (its group's first row) + l / 8, and since slot s of row r must
+  // hold the chunk that swz_chunk maps to s (an involution), the lane
+  // fetches global chunk swz_chunk(r, l % 8).
   // Sources are buffer descriptors (one per weight matrix of this expert,
   // one for this tile's token rows); a load past a descriptor's size
   // returns zeros, so edge rows (weight rows >= Nout, token rows >= rows)
@@ -218,23 +211,22 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_gemm_bf16_kernel(
       (void*)(act + (size_t)row0 * Kdim), 0,
       (uint32_t)((size_t)rows * Kdim * sizeof(bf16)), kBufferFlags);
   const int grow = lane >> 3;                   // row within the wave's 8
-  const int gchunk = (lane & 7) ^ grow;         // pre-swizzled global chunk
   int w_src[G::kWLoads];
 #pragma unroll
   for (int i = 0; i < G::kWLoads; ++i) {
     const int lr = (i * 4 + wave) * 8 + grow;
     const int n = kDual ? n0 + (lr & (kBW / 2 - 1)) : n0 + lr;
-    w_src[i] = (n * Kdim + gchunk * 8) * (int)sizeof(bf16);
+    w_src[i] = (n * Kdim + swz_chunk(lr, lane & 7) * 8) * (int)sizeof(bf16);
   }
   int a_src[G::kALoads];
 #pragma unroll
   for (int i = 0; i < G::kALoads; ++i) {
     const int lr = (i * 4 + wave) * 8 + grow;
-    a_src[i] = (lr * Kdim + gchunk * 8) * (int)sizeof(bf16);
+    a_src[i] = (lr * Kdim + swz_chunk(lr, lane & 7) * 8) * (int)sizeof(bf16);
   }
   char* const lds_bytes = reinterpret_cast<char*>(lds);
   constexpr int kLoads = G::kWLoads + G::kALoads;  // wave-wide loads per tile
-  auto issue_load = [&](int stage, int k0, int i) {
+  auto issue_load = [&](int stage, int k0, int i) __attribute__((always_inline)) {
     char* base = lds_bytes + stage * G::kStage * (int)sizeof(bf16);
     const int soff = k0 * (int)sizeof(bf16);
     // (the offsets go through locals and each descriptor has its own call:
@@ -271,6 +263,8 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_gemm_bf16_kernel(
     }
   }
   const int arow0 = wm * (BM / WM);
+  // this wave's 32-token subtiles that hold at least one of the tile's rows
+  const int jlim = min(G::kTM, max(0, (rows - arow0 + 31) / 32));
   const int lrow = lane & 31;
   const int lhalf = lane >> 5;
 
@@ -282,10 +276,10 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_gemm_bf16_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  // LDS byte addresses of this lane's MFMA operands.  With the XOR swizzle
-  // the chunk part depends on the reduction step ks only through
-  // (ks * 2 + lane / 32) ^ (lane & 7), so one per-lane base per ks covers
-  // every operand tile (their rows differ by multiples of 32 bytes * 32).
+  // LDS byte addresses of this lane's MFMA operands.  Operand tiles start
+  // at multiples of 32 rows, so the swizzle of row (tile + lane % 32) is
+  // that of lane % 32 and one per-lane base per reduction step ks covers
+  // every operand tile.
   int wbase[kBK / 16], abase[kBK / 16];
 #pragma unroll
   for (int ks = 0; ks < kBK / 16; ++ks) {
@@ -299,7 +293,7 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_gemm_bf16_kernel(
   // step ks.
   bf16x8 wf[2][G::kTW], af[2][G::kTM];
   constexpr int kFrags = G::kTW + G::kTM;  // LDS reads per step
-  auto read_frag = [&](int stage, int ks, int buf, int r) {
+  auto read_frag = [&](int stage, int ks, int buf, int r) __attribute__((always_inline)) {
     const char* s = reinterpret_cast<const char*>(lds) + stage * G::kStage * (int)sizeof(bf16);
     if (r < G::kTW)
       wf[buf][r] = *reinterpret_cast<const bf16x8*>(
@@ -315,8 +309,9 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_gemm_bf16_kernel(
   // every MFMA keeps this exact order: left alone, the compiler sinks each
   // read next to its first use and bunches the loads, leaving the matrix
   // cores idle meanwhile.
-  auto mfma_step = [&](auto i0_c, auto i1_c, auto reads_c, auto l0_c, auto l1_c, int buf,
-                       int stage, int ks, int rbuf, int lstage, int lk0) {
+  auto mfma_step = [&](auto jn_c, auto i0_c, auto i1_c, auto reads_c, auto l0_c, auto l1_c,
+                       int buf, int stage, int ks, int rbuf, int lstage, int lk0) __attribute__((always_inline)) {
+    constexpr int JN = decltype(jn_c)::value;
     constexpr int I0 = decltype(i0_c)::value;
     constexpr int I1 = decltype(i1_c)::value;
     constexpr bool kReads = decltype(reads_c)::value;
@@ -336,8 +331,9 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_gemm_bf16_kernel(
       }
       const int i = I0 + m / G::kTM;
       const int j = m % G::kTM;
-      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[buf][i], af[buf][j],
-                                                          acc[i][j], 0, 0, 0);
+      if (j < JN)  // 32-token subtiles past the tile's last row are skipped
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[buf][i], af[buf][j],
+                                                            acc[i][j], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -360,16 +356,16 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_gemm_bf16_kernel(
   // unused.
   static_assert(kBK / 16 == 4, "four reduction steps per tile");
   const int nk = Kdim / kBK;
-  auto tile_step = [&](auto stage_c, int kt) {
+  auto tile_step = [&](auto jn_c, auto stage_c, int kt) __attribute__((always_inline)) {
     constexpr int S = decltype(stage_c)::value;
     const int nk0 = min(kt + 1, nk - 1) * kBK;
-    mfma_step(IC0{}, ICW{}, YES{}, IC0{}, LH{}, 0, S, 1, 1, 1 - S, nk0);
-    mfma_step(IC0{}, ICW{}, YES{}, LH{}, LA{}, 1, S, 2, 0, 1 - S, nk0);
-    mfma_step(IC0{}, ICW{}, YES{}, IC0{}, IC0{}, 0, S, 3, 1, 0, 0);
-    mfma_step(IC0{}, ICH{}, NO{}, IC0{}, IC0{}, 1, 0, 0, 0, 0, 0);
+    mfma_step(jn_c, IC0{}, ICW{}, YES{}, IC0{}, LH{}, 0, S, 1, 1, 1 - S, nk0);
+    mfma_step(jn_c, IC0{}, ICW{}, YES{}, LH{}, LA{}, 1, S, 2, 0, 1 - S, nk0);
+    mfma_step(jn_c, IC0{}, ICW{}, YES{}, IC0{}, IC0{}, 0, S, 3, 1, 0, 0);
+    mfma_step(jn_c, IC0{}, ICH{}, NO{}, IC0{}, IC0{}, 1, 0, 0, 0, 0, 0);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    mfma_step(ICH{}, ICW{}, YES{}, IC0{}, IC0{}, 1, 1 - S, 0, 0, 0, 0);
+    mfma_step(jn_c, ICH{}, ICW{}, YES{}, IC0{}, IC0{}, 1, 1 - S, 0, 0, 0, 0);
   };
   using St0 = std::integral_constant<int, 0>;
   using St1 = std::integral_constant<int, 1>;
@@ -380,20 +376,35 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_gemm_bf16_kernel(
   __syncthreads();
 #pragma unroll
   for (int r = 0; r < kFrags; ++r) read_frag(0, 0, 0, r);
-  // tiles in pairs (stage 0, stage 1); an odd count starts with one tile
-  // on stage 0 and pairs (stage 1, stage 0) after it
-  if (nk & 1) {
-    tile_step(St0{}, 0);
-    for (int kt = 1; kt < nk; kt += 2) {
-      tile_step(St1{}, kt);
-      tile_step(St0{}, kt + 1);
+  // Tiles in pairs (stage 0, stage 1); an odd count starts with one tile
+  // on stage 0 and pairs (stage 1, stage 0) after it.  JN is the number of
+  // this wave's 32-token subtiles that are multiplied: a ragged last tile of
+  // an expert has all-zero subtiles past its last row, and the loop comes in
+  // variants that skip them (a run-time test per MFMA would force the
+  // accumulators out of registers).
+  auto main_loop = [&](auto jn_c) __attribute__((always_inline)) {
+    if (nk & 1) {
+      tile_step(jn_c, St0{}, 0);
+      for (int kt = 1; kt < nk; kt += 2) {
+        tile_step(jn_c, St1{}, kt);
+        tile_step(jn_c, St0{}, kt + 1);
+      }
+    } else {
+      for (int kt = 0; kt < nk; kt += 2) {
+        tile_step(jn_c, St0{}, kt);
+        tile_step(jn_c, St1{}, kt + 1);
+      }
     }
-  } else {
-    for (int kt = 0; kt < nk; kt += 2) {
-      tile_step(St0{}, kt);
-      tile_step(St1{}, kt + 1);
-    }
-  }
+  };
+  constexpr int kTM = G::kTM;
+  if (jlim >= kTM || (kTM > 2 && jlim > 2))
+    main_loop(std::integral_constant<int, kTM>{});
+  else if (kTM > 2 && jlim == 2)
+    main_loop(std::integral_constant<int, (kTM > 2 ? 2 : kTM)>{});
+  else if (kTM > 1 && jlim == 1)
+    main_loop(std::integral_constant<int, (kTM > 1 ? 1 : kTM)>{});
+  else
+    main_loop(std::integral_constant<int, 0>{});
 
   // Epilogue.  Accumulator register r of lane l holds weight row
   // (r / 4) * 8 + (l / 32) * 4 + r % 4 of its 32-row weight tile and token
