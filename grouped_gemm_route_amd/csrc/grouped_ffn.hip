@@ -160,13 +160,15 @@ struct TileGeo {
   static constexpr int kWN = 4 / WM;
   static constexpr int kTM = BM / WM / 32;   // 32-token MFMA tiles per wave
   static constexpr int kTW = kBW / kWN / 32; // 32-row weight MFMA tiles per wave
-  static constexpr int kAElems = BM * kBK;
-  static constexpr int kStage = kWElems + kAElems;
+  // LDS: two activation stages, then a ring of three weight slots
+  static constexpr int kAStageBytes = BM * kRowBytes;
+  static constexpr int kWSlotBytes = kBW * kRowBytes;
+  static constexpr int kWRegion = 2 * kAStageBytes;
   // one wave-wide direct-to-LDS load moves 64 lanes x 16 bytes = 8 LDS rows;
   // the 4 waves together fill 32 rows per round
   static constexpr int kWLoads = kBW / 32;
   static constexpr int kALoads = BM / 32;
-  static constexpr size_t kLds = 2 * (size_t)kStage * sizeof(bf16);
+  static constexpr size_t kLds = (size_t)kWRegion + 3 * (size_t)kWSlotBytes;
   static_assert(kALoads >= 1 && kTM >= 1 && kTW >= 2, "tile shape");
 };
 
@@ -225,26 +227,25 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_gemm_bf16_kernel(
     a_src[i] = (lr * Kdim + swz_chunk(lr, lane & 7) * 8) * (int)sizeof(bf16);
   }
   char* const lds_bytes = reinterpret_cast<char*>(lds);
-  constexpr int kLoads = G::kWLoads + G::kALoads;  // wave-wide loads per tile
-  auto issue_load = [&](int stage, int k0, int i) __attribute__((always_inline)) {
-    char* base = lds_bytes + stage * G::kStage * (int)sizeof(bf16);
+  // (offsets go through locals and each descriptor has its own call: an
+  // array element or a conditional expression of descriptor type as a
+  // builtin argument here drops the kernel's host-side stub)
+  auto issue_wload = [&](int wslot, int k0, int i) __attribute__((always_inline)) {
+    const int voff = w_src[i];
     const int soff = k0 * (int)sizeof(bf16);
-    // (the offsets go through locals and each descriptor has its own call:
-    // an array element or a conditional expression of descriptor type as a
-    // builtin argument here drops the kernel's host-side stub)
-    if (i < G::kWLoads) {
-      const int voff = w_src[i];
-      lds_void_t* dst = (lds_void_t*)(base + (i * 4 + wave) * 8 * kRowBytes);
-      if (kDual && i >= G::kWLoads / 2)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(wr1, dst, 16, voff, soff, 0, 0);
-      else
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(wr0, dst, 16, voff, soff, 0, 0);
-    } else {
-      const int voff = a_src[i - G::kWLoads];
-      lds_void_t* dst = (lds_void_t*)(base + kWElems * (int)sizeof(bf16) +
-                                      ((i - G::kWLoads) * 4 + wave) * 8 * kRowBytes);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ar, dst, 16, voff, soff, 0, 0);
-    }
+    lds_void_t* dst = (lds_void_t*)(lds_bytes + G::kWRegion + wslot * G::kWSlotBytes +
+                                    (i * 4 + wave) * 8 * kRowBytes);
+    if (kDual && i >= G::kWLoads / 2)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(wr1, dst, 16, voff, soff, 0, 0);
+    else
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(wr0, dst, 16, voff, soff, 0, 0);
+  };
+  auto issue_aload = [&](int stage, int k0, int i) __attribute__((always_inline)) {
+    const int voff = a_src[i];
+    const int soff = k0 * (int)sizeof(bf16);
+    lds_void_t* dst = (lds_void_t*)(lds_bytes + stage * G::kAStageBytes +
+                                    (i * 4 + wave) * 8 * kRowBytes);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(ar, dst, 16, voff, soff, 0, 0);
   };
 
   // Wave tiling.  In the gate/up pass the first half of a wave's weight
@@ -284,8 +285,8 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_gemm_bf16_kernel(
 #pragma unroll
   for (int ks = 0; ks < kBK / 16; ++ks) {
     const int chunk = ks * 2 + lhalf;
-    wbase[ks] = swz(wrow[0] + lrow, chunk) * (int)sizeof(bf16);
-    abase[ks] = (kWElems + swz(arow0 + lrow, chunk)) * (int)sizeof(bf16);
+    wbase[ks] = G::kWRegion + swz(wrow[0] + lrow, chunk) * (int)sizeof(bf16);
+    abase[ks] = swz(arow0 + lrow, chunk) * (int)sizeof(bf16);
   }
 
   // MFMA operands of one 16-wide reduction step, double-buffered in
@@ -293,41 +294,45 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_gemm_bf16_kernel(
   // step ks.
   bf16x8 wf[2][G::kTW], af[2][G::kTM];
   constexpr int kFrags = G::kTW + G::kTM;  // LDS reads per step
-  auto read_frag = [&](int stage, int ks, int buf, int r) __attribute__((always_inline)) {
-    const char* s = reinterpret_cast<const char*>(lds) + stage * G::kStage * (int)sizeof(bf16);
+  auto read_frag = [&](int stage, int wslot, int ks, int buf, int r) __attribute__((always_inline)) {
     if (r < G::kTW)
       wf[buf][r] = *reinterpret_cast<const bf16x8*>(
-          s + wbase[ks] + (wrow[r] - wrow[0]) * kRowBytes);
+          lds_bytes + wslot * G::kWSlotBytes + wbase[ks] + (wrow[r] - wrow[0]) * kRowBytes);
     else
       af[buf][r - G::kTW] = *reinterpret_cast<const bf16x8*>(
-          s + abase[ks] + (r - G::kTW) * 32 * kRowBytes);
+          lds_bytes + stage * G::kAStageBytes + abase[ks] + (r - G::kTW) * 32 * kRowBytes);
   };
-  // MFMAs of weight tiles [I0, I1) on operand buffer `buf`.  If kReads,
-  // the kFrags operand reads of (stage, ks) into buffer rbuf are spread
-  // evenly between them, and so are the loads [L0, L1) of the next tile
-  // (into stage lstage at reduction offset lk0).  A scheduling fence after
-  // every MFMA keeps this exact order: left alone, the compiler sinks each
-  // read next to its first use and bunches the loads, leaving the matrix
-  // cores idle meanwhile.
-  auto mfma_step = [&](auto jn_c, auto i0_c, auto i1_c, auto reads_c, auto l0_c, auto l1_c,
-                       int buf, int stage, int ks, int rbuf, int lstage, int lk0) __attribute__((always_inline)) {
+  // MFMAs of weight tiles [I0, I1) on operand buffer `buf`, for the first
+  // JN token subtiles.  If kReads, the kFrags operand reads of (stage,
+  // wslot, ks) into buffer rbuf are spread evenly between them, and so are
+  // the activation loads [A0, A1) and the weight loads [W0, W1) of later
+  // tiles.  A scheduling fence after every MFMA slot keeps this exact order:
+  // left alone, the compiler sinks each read next to its first use and
+  // bunches the loads, leaving the matrix cores idle meanwhile.
+  auto mfma_step = [&](auto jn_c, auto i0_c, auto i1_c, auto reads_c, auto a0_c, auto a1_c,
+                       auto w0_c, auto w1_c, int buf, int stage, int wslot, int ks, int rbuf,
+                       int astage, int ak0, int wslot_ld, int wk0) __attribute__((always_inline)) {
     constexpr int JN = decltype(jn_c)::value;
     constexpr int I0 = decltype(i0_c)::value;
     constexpr int I1 = decltype(i1_c)::value;
     constexpr bool kReads = decltype(reads_c)::value;
-    constexpr int L0 = decltype(l0_c)::value;
-    constexpr int L1 = decltype(l1_c)::value;
+    constexpr int A0 = decltype(a0_c)::value, A1 = decltype(a1_c)::value;
+    constexpr int W0 = decltype(w0_c)::value, W1 = decltype(w1_c)::value;
     constexpr int n = (I1 - I0) * G::kTM;
 #pragma unroll
     for (int m = 0; m < n; ++m) {
 #pragma unroll
-      for (int l = L0 + (m * (L1 - L0) + n - 1) / n; l < L0 + ((m + 1) * (L1 - L0) + n - 1) / n;
+      for (int l = A0 + (m * (A1 - A0) + n - 1) / n; l < A0 + ((m + 1) * (A1 - A0) + n - 1) / n;
            ++l)
-        issue_load(lstage, lk0, l);
+        issue_aload(astage, ak0, l);
+#pragma unroll
+      for (int l = W0 + (m * (W1 - W0) + n - 1) / n; l < W0 + ((m + 1) * (W1 - W0) + n - 1) / n;
+           ++l)
+        issue_wload(wslot_ld, wk0, l);
       if (kReads) {
 #pragma unroll
         for (int r = (m * kFrags + n - 1) / n; r < ((m + 1) * kFrags + n - 1) / n; ++r)
-          read_frag(stage, ks, rbuf, r);
+          read_frag(stage, wslot, ks, rbuf, r);
       }
       const int i = I0 + m / G::kTM;
       const int j = m % G::kTM;
@@ -340,42 +345,60 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_gemm_bf16_kernel(
   using IC0 = std::integral_constant<int, 0>;
   using ICH = std::integral_constant<int, G::kTW / 2>;
   using ICW = std::integral_constant<int, G::kTW>;
-  using LH = std::integral_constant<int, kLoads / 2>;
-  using LA = std::integral_constant<int, kLoads>;
+  using AA = std::integral_constant<int, G::kALoads>;
+  using WA = std::integral_constant<int, G::kWLoads>;
   using YES = std::true_type;
   using NO = std::false_type;
 
-  // One reduction tile (index kt) on LDS stage S.  The loads of the next
-  // tile go to the other stage (last read by the tile before this one,
-  // which every wave finished ahead of the barrier that closed it) and are
-  // spread over the first two steps; in the middle of the last step this
-  // wave waits for its loads and meets the others at a barrier, after which
-  // every wave's loads are visible, and the next tile's first operands are
-  // read between the last MFMAs.  The body has no branches: after the last
-  // tile the "next" loads repeat the last tile and the reads that follow are
-  // unused.
+  // One reduction tile kt: activations on LDS stage S = kt % 2, weights in
+  // slot u = kt % 3 of a three-slot ring.  Step 0 loads tile kt + 1's
+  // activations into the other stage and step 1 loads tile kt + 2's weights
+  // into slot (u + 2) % 3; both targets were last read by tile kt - 1, which
+  // every wave finished ahead of the barrier that closed it.  Halfway
+  // through the last step this wave waits until only the weight loads of
+  // tile kt + 2 may be outstanding (so tile kt + 1 has landed) and meets the
+  // others at a barrier, after which every wave's loads of tile kt + 1 are
+  // visible; tile kt + 1's first operands are then read between the last
+  // MFMAs.  Weights, which come from HBM more often, thus get two tiles'
+  // time to arrive.  The barrier has no memory fence: a fence would also
+  // wait for the weight loads still in flight.  The body has no branches:
+  // past the last tile the loads repeat the last tile (into buffers no one
+  // reads again) and the trailing reads go unused.
   static_assert(kBK / 16 == 4, "four reduction steps per tile");
+  static_assert(G::kWLoads == 8, "vmcnt immediate");
   const int nk = Kdim / kBK;
-  auto tile_step = [&](auto jn_c, auto stage_c, int kt) __attribute__((always_inline)) {
+  auto tile_step = [&](auto jn_c, auto stage_c, int kt, int u) __attribute__((always_inline)) {
     constexpr int S = decltype(stage_c)::value;
-    const int nk0 = min(kt + 1, nk - 1) * kBK;
-    mfma_step(jn_c, IC0{}, ICW{}, YES{}, IC0{}, LH{}, 0, S, 1, 1, 1 - S, nk0);
-    mfma_step(jn_c, IC0{}, ICW{}, YES{}, LH{}, LA{}, 1, S, 2, 0, 1 - S, nk0);
-    mfma_step(jn_c, IC0{}, ICW{}, YES{}, IC0{}, IC0{}, 0, S, 3, 1, 0, 0);
-    mfma_step(jn_c, IC0{}, ICH{}, NO{}, IC0{}, IC0{}, 1, 0, 0, 0, 0, 0);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    mfma_step(jn_c, ICH{}, ICW{}, YES{}, IC0{}, IC0{}, 1, 1 - S, 0, 0, 0, 0);
+    const int ak0 = min(kt + 1, nk - 1) * kBK;
+    const int wk0 = min(kt + 2, nk - 1) * kBK;
+    const int u1 = u == 2 ? 0 : u + 1;
+    const int u2 = u == 0 ? 2 : u - 1;
+    mfma_step(jn_c, IC0{}, ICW{}, YES{}, IC0{}, AA{}, IC0{}, IC0{}, 0, S, u, 1, 1, 1 - S, ak0, 0, 0);
+    mfma_step(jn_c, IC0{}, ICW{}, YES{}, IC0{}, IC0{}, IC0{}, WA{}, 1, S, u, 2, 0, 0, 0, u2, wk0);
+    mfma_step(jn_c, IC0{}, ICW{}, YES{}, IC0{}, IC0{}, IC0{}, IC0{}, 0, S, u, 3, 1, 0, 0, 0, 0);
+    mfma_step(jn_c, IC0{}, ICH{}, NO{}, IC0{}, IC0{}, IC0{}, IC0{}, 1, 0, 0, 0, 0, 0, 0, 0, 0);
+    asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    mfma_step(jn_c, ICH{}, ICW{}, YES{}, IC0{}, IC0{}, IC0{}, IC0{}, 1, 1 - S, u1, 0, 0, 0, 0, 0,
+              0);
   };
   using St0 = std::integral_constant<int, 0>;
   using St1 = std::integral_constant<int, 1>;
 
+  // prologue: weights of tile 0, activations of tile 0, weights of tile 1;
+  // wait for the first two
 #pragma unroll
-  for (int l = 0; l < kLoads; ++l) issue_load(0, 0, l);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
+  for (int l = 0; l < G::kWLoads; ++l) issue_wload(0, 0, l);
 #pragma unroll
-  for (int r = 0; r < kFrags; ++r) read_frag(0, 0, 0, r);
+  for (int l = 0; l < G::kALoads; ++l) issue_aload(0, 0, l);
+#pragma unroll
+  for (int l = 0; l < G::kWLoads; ++l) issue_wload(1, min(1, nk - 1) * kBK, l);
+  asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+#pragma unroll
+  for (int r = 0; r < kFrags; ++r) read_frag(0, 0, 0, 0, r);
   // Tiles in pairs (stage 0, stage 1); an odd count starts with one tile
   // on stage 0 and pairs (stage 1, stage 0) after it.  JN is the number of
   // this wave's 32-token subtiles that are multiplied: a ragged last tile of
@@ -383,16 +406,23 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_gemm_bf16_kernel(
   // variants that skip them (a run-time test per MFMA would force the
   // accumulators out of registers).
   auto main_loop = [&](auto jn_c) __attribute__((always_inline)) {
+    int u = 0;  // weight slot of the current tile, kt % 3
+    auto next = [](int v) { return v == 2 ? 0 : v + 1; };
     if (nk & 1) {
-      tile_step(jn_c, St0{}, 0);
+      tile_step(jn_c, St0{}, 0, u);
+      u = next(u);
       for (int kt = 1; kt < nk; kt += 2) {
-        tile_step(jn_c, St1{}, kt);
-        tile_step(jn_c, St0{}, kt + 1);
+        tile_step(jn_c, St1{}, kt, u);
+        u = next(u);
+        tile_step(jn_c, St0{}, kt + 1, u);
+        u = next(u);
       }
     } else {
       for (int kt = 0; kt < nk; kt += 2) {
-        tile_step(jn_c, St0{}, kt);
-        tile_step(jn_c, St1{}, kt + 1);
+        tile_step(jn_c, St0{}, kt, u);
+        u = next(u);
+        tile_step(jn_c, St1{}, kt + 1, u);
+        u = next(u);
       }
     }
   };
