@@ -136,7 +136,6 @@ constexpr int kBufferFlags = 0x00020000;
 
 constexpr int kBW = 256;            // weight rows per block tile
 constexpr int kBK = 64;             // reduction elements per stage
-constexpr int kWElems = kBW * kBK;
 constexpr int kRowBytes = kBK * (int)sizeof(bf16);  // 128: one LDS row
 
 typedef __attribute__((address_space(3))) void lds_void_t;
