@@ -21,12 +21,15 @@
 //                  totals over blocks (block_excl) and their sum (demand);
 //                  counts = min(demand, capacity); offsets = exclusive scan
 //                  of counts over experts; rank_offsets[r] = offsets[r*E/W].
-//   scatter kernel (one wave per token): r = block_excl + local rank; kept
+//   scatter kernel (one block per token): r = block_excl + local rank; kept
 //                  iff capacity < 0 or r < capacity; writes dest and
 //                  perm_token, then copies the token's row once from HBM to
-//                  each kept destination row in 16-byte vectors.
+//                  each kept destination row in 16-byte pieces.  When the
+//                  per-block count table is small, every scatter block
+//                  scans it itself and the scan kernel is not launched.
 // Because experts are numbered rank by rank, the (expert, token) order is
 // rank-major: rank r's send slice is rows [rank_offsets[r], rank_offsets[r+1]).
+#include "moe_route.h"
 #include "moe_internal.h"
 #include "block_scan.h"
 
@@ -132,49 +135,86 @@ __global__ __launch_bounds__(kScanThreads) void dispatch_scan_kernel(
   for (int r = tid; r <= W; r += blockDim.x) rank_offsets[r] = kept_s[r * per_rank];
 }
 
-constexpr int kScatterWaves = 4;
-constexpr int kCopyUnroll = 4;
+constexpr int kScatterThreads = 256;
+// Largest per-block count table (blocks x experts) that every scatter block
+// scans for itself instead of waiting for the one-block scan kernel.
+constexpr int kFusedScanMaxCounts = 1024;
 
-__global__ __launch_bounds__(kScatterWaves * kWave) void dispatch_scatter_kernel(
+// One block per token.  Threads 0..K-1 find the token's K rows; then the
+// block copies the row in 16-byte pieces, one piece per thread per round,
+// each piece loaded once and stored to every kept destination.
+//   kFusedScan: the per-block count table is small, so each block computes
+//   the expert offsets (and block 0 writes demand / counts / offsets /
+//   rank_offsets) and its own per-expert bases from block_counts directly;
+//   otherwise block_excl and offsets come from the scan kernel.
+template <bool kFusedScan>
+__global__ __launch_bounds__(kScatterThreads) void dispatch_scatter_kernel(
     const uint4* __restrict__ x, int row_chunks, int N,
-    const int32_t* __restrict__ topk_idx, int E, int K, int64_t capacity,
-    const int32_t* __restrict__ block_excl,
-    const int32_t* __restrict__ local_rank,
-    const int32_t* __restrict__ offsets, uint4* __restrict__ x_perm,
+    const int32_t* __restrict__ topk_idx, int E, int K, int W, int64_t capacity,
+    const int32_t* __restrict__ block_counts, const int32_t* __restrict__ block_excl,
+    const int32_t* __restrict__ local_rank, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ demand, int32_t* __restrict__ counts,
+    int32_t* __restrict__ rank_offsets, uint4* __restrict__ x_perm,
     int32_t* __restrict__ perm_token, int32_t* __restrict__ dest) {
-  const int lane = threadIdx.x & (kWave - 1);
-  const int t = blockIdx.x * kScatterWaves + threadIdx.x / kWave;
-  if (t >= N) return;  // whole wave leaves together
+  __shared__ int rows[MOE_MAX_TOPK];
+  __shared__ int offs[kFusedScan ? kScatterThreads + 1 : 1];
+  __shared__ int wave_sums[kScatterThreads / kWave];
+  const int t = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int b = t / kRankBlockTokens;
 
-  int row = -1;
-  if (lane < K) {
-    const int e = topk_idx[(size_t)t * K + lane];
-    if ((unsigned)e < (unsigned)E) {
-      const int r = block_excl[(size_t)(t / kRankBlockTokens) * E + e] +
-                    local_rank[(size_t)t * K + lane];
-      if (capacity < 0 || (int64_t)r < capacity) row = offsets[e] + r;
+  if constexpr (kFusedScan) {
+    // E <= 256 here: thread e sums its expert's counts over all blocks
+    const int B = (N + kRankBlockTokens - 1) / kRankBlockTokens;
+    int kept = 0;
+    if (tid < E) {
+      int tot = 0;
+      for (int bb = 0; bb < B; ++bb) tot += block_counts[(size_t)bb * E + tid];
+      kept = capacity < 0 ? tot : (int)min((int64_t)tot, capacity);
+      if (t == 0) {
+        demand[tid] = tot;
+        counts[tid] = kept;
+      }
     }
-    dest[(size_t)t * K + lane] = row;
-    if (row >= 0) perm_token[row] = t;
+    int total = 0;
+    const int excl = block_exclusive_scan(tid < E ? kept : 0, wave_sums, &total);
+    if (tid < E) offs[tid] = excl;
+    if (tid == 0) offs[E] = total;
+    __syncthreads();
+    if (t == 0) {
+      for (int e = tid; e <= E; e += kScatterThreads) offsets[e] = offs[e];
+      const int per_rank = E / W;
+      for (int r = tid; r <= W; r += kScatterThreads) rank_offsets[r] = offs[r * per_rank];
+    }
   }
 
-  const uint4* src = x + (size_t)t * row_chunks;
-  for (int c0 = 0; c0 < row_chunks; c0 += kWave * kCopyUnroll) {
-    uint4 v[kCopyUnroll];
-#pragma unroll
-    for (int u = 0; u < kCopyUnroll; ++u) {
-      const int c = c0 + u * kWave + lane;
-      if (c < row_chunks) v[u] = src[c];
-    }
-    for (int k = 0; k < K; ++k) {
-      const int rk = __shfl(row, k);
-      if (rk < 0) continue;  // uniform across the wave
-      uint4* dst = x_perm + (size_t)rk * row_chunks;
-#pragma unroll
-      for (int u = 0; u < kCopyUnroll; ++u) {
-        const int c = c0 + u * kWave + lane;
-        if (c < row_chunks) dst[c] = v[u];
+  if (tid < K) {
+    int row = -1;
+    const int e = topk_idx[(size_t)t * K + tid];
+    if ((unsigned)e < (unsigned)E) {
+      int r = local_rank[(size_t)t * K + tid];
+      int off;
+      if constexpr (kFusedScan) {
+        for (int bb = 0; bb < b; ++bb) r += block_counts[(size_t)bb * E + e];
+        off = offs[e];
+      } else {
+        r += block_excl[(size_t)b * E + e];
+        off = offsets[e];
       }
+      if (capacity < 0 || (int64_t)r < capacity) row = off + r;
+    }
+    rows[tid] = row;
+    dest[(size_t)t * K + tid] = row;
+    if (row >= 0) perm_token[row] = t;
+  }
+  __syncthreads();
+
+  const uint4* src = x + (size_t)t * row_chunks;
+  for (int c = tid; c < row_chunks; c += kScatterThreads) {
+    const uint4 v = src[c];
+    for (int k = 0; k < K; ++k) {
+      const int rk = rows[k];
+      if (rk >= 0) x_perm[(size_t)rk * row_chunks + c] = v;
     }
   }
 }
@@ -212,17 +252,23 @@ hipError_t launch_dispatch(const void* x, size_t row_bytes, int N,
       topk_idx, N, E, K, ws.block_counts, ws.local_rank);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
+  const int row_chunks = (int)(row_bytes / 16);
+  if ((int64_t)B * E <= kFusedScanMaxCounts && E <= kScatterThreads) {
+    dispatch_scatter_kernel<true><<<N, kScatterThreads, 0, stream>>>(
+        static_cast<const uint4*>(x), row_chunks, N, topk_idx, E, K, W, capacity,
+        ws.block_counts, nullptr, ws.local_rank, offsets, demand, counts, rank_offsets,
+        static_cast<uint4*>(x_perm), perm_token, dest);
+    return hipGetLastError();
+  }
   dispatch_scan_kernel<<<1, kScanThreads, 0, stream>>>(
       ws.block_counts, B, E, W, capacity, ws.block_excl, demand, counts,
       offsets, rank_offsets);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
-  const int row_chunks = (int)(row_bytes / 16);
-  const int blocks = (N + kScatterWaves - 1) / kScatterWaves;
-  dispatch_scatter_kernel<<<blocks, kScatterWaves * kWave, 0, stream>>>(
-      static_cast<const uint4*>(x), row_chunks, N, topk_idx, E, K, capacity,
-      ws.block_excl, ws.local_rank, offsets, static_cast<uint4*>(x_perm),
-      perm_token, dest);
+  dispatch_scatter_kernel<false><<<N, kScatterThreads, 0, stream>>>(
+      static_cast<const uint4*>(x), row_chunks, N, topk_idx, E, K, W, capacity,
+      ws.block_counts, ws.block_excl, ws.local_rank, offsets, demand, counts, rank_offsets,
+      static_cast<uint4*>(x_perm), perm_token, dest);
   return hipGetLastError();
 }
 
