@@ -152,11 +152,12 @@ __device__ __forceinline__ int swz(int row, int chunk) {
   return row * kBK + (swz_chunk(row, chunk) << 3);
 }
 
-// Geometry of a block tile of BM token rows x 256 weight rows, 4 waves laid
-// out WM (along tokens) x 4/WM (along weight rows).
-template <int BM, int WM>
+// Geometry of a block tile of BM token rows x 256 weight rows, NW waves laid
+// out WM (along tokens) x NW/WM (along weight rows).
+template <int BM, int WM, int NW>
 struct TileGeo {
-  static constexpr int kWN = 4 / WM;
+  static constexpr int kWaves = NW;
+  static constexpr int kWN = NW / WM;
   static constexpr int kTM = BM / WM / 32;   // 32-token MFMA tiles per wave
   static constexpr int kTW = kBW / kWN / 32; // 32-row weight MFMA tiles per wave
   // LDS: two activation stages, then a ring of three weight slots
@@ -164,20 +165,20 @@ struct TileGeo {
   static constexpr int kWSlotBytes = kBW * kRowBytes;
   static constexpr int kWRegion = 2 * kAStageBytes;
   // one wave-wide direct-to-LDS load moves 64 lanes x 16 bytes = 8 LDS rows;
-  // the 4 waves together fill 32 rows per round
-  static constexpr int kWLoads = kBW / 32;
-  static constexpr int kALoads = BM / 32;
+  // the NW waves together fill 8 NW rows per round
+  static constexpr int kWLoads = kBW / (8 * NW);
+  static constexpr int kALoads = BM / (8 * NW);
   static constexpr size_t kLds = (size_t)kWRegion + 3 * (size_t)kWSlotBytes;
   static_assert(kALoads >= 1 && kTM >= 1 && kTW >= 2, "tile shape");
 };
 
-template <int BM, int WM, bool kDual>
-__global__ __launch_bounds__(kThreads, 1) void ffn_gemm_bf16_kernel(
+template <int BM, int WM, int NW, bool kDual>
+__global__ __launch_bounds__(NW * kWave, 1) void ffn_gemm_bf16_kernel(
     const bf16* __restrict__ act, int Kdim, const bf16* __restrict__ w0,
     const bf16* __restrict__ w1, int Nout, bf16* __restrict__ out,
     const int4* __restrict__ tiles, const int* __restrict__ tile_start,
     const int* __restrict__ num_tiles, int E, int n_tiles) {
-  using G = TileGeo<BM, WM>;
+  using G = TileGeo<BM, WM, NW>;
   extern __shared__ __attribute__((aligned(16))) bf16 lds[];
   int slot, n_tile;
   if (!map_block(tile_start, num_tiles, E, n_tiles, &slot, &n_tile)) return;
@@ -215,14 +216,14 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_gemm_bf16_kernel(
   int w_src[G::kWLoads];
 #pragma unroll
   for (int i = 0; i < G::kWLoads; ++i) {
-    const int lr = (i * 4 + wave) * 8 + grow;
+    const int lr = (i * NW + wave) * 8 + grow;
     const int n = kDual ? n0 + (lr & (kBW / 2 - 1)) : n0 + lr;
     w_src[i] = (n * Kdim + swz_chunk(lr, lane & 7) * 8) * (int)sizeof(bf16);
   }
   int a_src[G::kALoads];
 #pragma unroll
   for (int i = 0; i < G::kALoads; ++i) {
-    const int lr = (i * 4 + wave) * 8 + grow;
+    const int lr = (i * NW + wave) * 8 + grow;
     a_src[i] = (lr * Kdim + swz_chunk(lr, lane & 7) * 8) * (int)sizeof(bf16);
   }
   char* const lds_bytes = reinterpret_cast<char*>(lds);
@@ -233,7 +234,7 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_gemm_bf16_kernel(
     const int voff = w_src[i];
     const int soff = k0 * (int)sizeof(bf16);
     lds_void_t* dst = (lds_void_t*)(lds_bytes + G::kWRegion + wslot * G::kWSlotBytes +
-                                    (i * 4 + wave) * 8 * kRowBytes);
+                                    (i * NW + wave) * 8 * kRowBytes);
     if (kDual && i >= G::kWLoads / 2)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(wr1, dst, 16, voff, soff, 0, 0);
     else
@@ -243,7 +244,7 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_gemm_bf16_kernel(
     const int voff = a_src[i];
     const int soff = k0 * (int)sizeof(bf16);
     lds_void_t* dst = (lds_void_t*)(lds_bytes + stage * G::kAStageBytes +
-                                    (i * 4 + wave) * 8 * kRowBytes);
+                                    (i * NW + wave) * 8 * kRowBytes);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(ar, dst, 16, voff, soff, 0, 0);
   };
 
@@ -364,7 +365,7 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_gemm_bf16_kernel(
   // past the last tile the loads repeat the last tile (into buffers no one
   // reads again) and the trailing reads go unused.
   static_assert(kBK / 16 == 4, "four reduction steps per tile");
-  static_assert(G::kWLoads == 8, "vmcnt immediate");
+  static_assert(G::kWLoads == 8 || G::kWLoads == 4, "vmcnt immediate");
   const int nk = Kdim / kBK;
   auto tile_step = [&](auto jn_c, auto stage_c, int kt, int u) __attribute__((always_inline)) {
     constexpr int S = decltype(stage_c)::value;
@@ -376,7 +377,10 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_gemm_bf16_kernel(
     mfma_step(jn_c, IC0{}, ICW{}, YES{}, IC0{}, IC0{}, IC0{}, WA{}, 1, S, u, 2, 0, 0, 0, u2, wk0);
     mfma_step(jn_c, IC0{}, ICW{}, YES{}, IC0{}, IC0{}, IC0{}, IC0{}, 0, S, u, 3, 1, 0, 0, 0, 0);
     mfma_step(jn_c, IC0{}, ICH{}, NO{}, IC0{}, IC0{}, IC0{}, IC0{}, 1, 0, 0, 0, 0, 0, 0, 0, 0);
-    asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    if constexpr (G::kWLoads == 8)
+      asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     mfma_step(jn_c, ICH{}, ICW{}, YES{}, IC0{}, IC0{}, IC0{}, IC0{}, 1, 1 - S, u1, 0, 0, 0, 0, 0,
@@ -393,7 +397,10 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_gemm_bf16_kernel(
   for (int l = 0; l < G::kALoads; ++l) issue_aload(0, 0, l);
 #pragma unroll
   for (int l = 0; l < G::kWLoads; ++l) issue_wload(1, min(1, nk - 1) * kBK, l);
-  asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+  if constexpr (G::kWLoads == 8)
+    asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+  else
+    asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 #pragma unroll
@@ -556,17 +563,17 @@ __global__ __launch_bounds__(kThreads) void ffn_gemm_f32_kernel(
   }
 }
 
-template <int BM, int WM, bool kDual>
+template <int BM, int WM, int NW, bool kDual>
 hipError_t launch_bf16_gemm(const bf16* act, int Kdim, const bf16* w0,
                             const bf16* w1, int Nout, bf16* out,
                             const FfnWorkspace& ws, int E, int max_tiles,
                             hipStream_t stream) {
-  using G = TileGeo<BM, WM>;
+  using G = TileGeo<BM, WM, NW>;
   static std::once_flag once;
   static hipError_t attr = hipSuccess;
   std::call_once(once, [] {
     attr = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&ffn_gemm_bf16_kernel<BM, WM, kDual>),
+        reinterpret_cast<const void*>(&ffn_gemm_bf16_kernel<BM, WM, NW, kDual>),
         hipFuncAttributeMaxDynamicSharedMemorySize, (int)G::kLds);
   });
   if (attr != hipSuccess) return attr;
@@ -574,24 +581,24 @@ hipError_t launch_bf16_gemm(const bf16* act, int Kdim, const bf16* w0,
   const int n_tiles = (Nout + kNOut - 1) / kNOut;
   const long long blocks = (long long)n_tiles * max_tiles;
   const int grid = (int)((blocks + 7) / 8 * 8);
-  ffn_gemm_bf16_kernel<BM, WM, kDual><<<grid, kThreads, G::kLds, stream>>>(
+  ffn_gemm_bf16_kernel<BM, WM, NW, kDual><<<grid, NW * kWave, G::kLds, stream>>>(
       act, Kdim, w0, w1, Nout, out, ws.tiles, ws.tile_start, ws.num_tiles, E,
       n_tiles);
   return hipGetLastError();
 }
 
-template <int BM, int WM>
+template <int BM, int WM, int NW>
 hipError_t launch_bf16_ffn(const void* x_perm, int d, int ffn, int E,
                            const void* w_gate, const void* w_up,
                            const void* w_down, void* h, void* y_perm,
                            const FfnWorkspace& ws, int max_tiles,
                            hipStream_t stream) {
-  hipError_t err = launch_bf16_gemm<BM, WM, true>(
+  hipError_t err = launch_bf16_gemm<BM, WM, NW, true>(
       static_cast<const bf16*>(x_perm), d, static_cast<const bf16*>(w_gate),
       static_cast<const bf16*>(w_up), ffn, static_cast<bf16*>(h), ws, E,
       max_tiles, stream);
   if (err != hipSuccess) return err;
-  return launch_bf16_gemm<BM, WM, false>(
+  return launch_bf16_gemm<BM, WM, NW, false>(
       static_cast<const bf16*>(h), ffn, static_cast<const bf16*>(w_down),
       nullptr, d, static_cast<bf16*>(y_perm), ws, E, max_tiles, stream);
 }
@@ -634,12 +641,12 @@ hipError_t launch_grouped_ffn(const void* x_perm, bool bf16_data, int d,
 
   if (bf16_data) {
     if (tr == 256)
-      return launch_bf16_ffn<256, 2>(x_perm, d, ffn, E, w_gate, w_up, w_down, h,
+      return launch_bf16_ffn<256, 2, 4>(x_perm, d, ffn, E, w_gate, w_up, w_down, h,
                                      y_perm, ws, max_tiles, stream);
     if (tr == 128)
-      return launch_bf16_ffn<128, 2>(x_perm, d, ffn, E, w_gate, w_up, w_down, h,
+      return launch_bf16_ffn<128, 2, 4>(x_perm, d, ffn, E, w_gate, w_up, w_down, h,
                                      y_perm, ws, max_tiles, stream);
-    return launch_bf16_ffn<32, 1>(x_perm, d, ffn, E, w_gate, w_up, w_down, h,
+    return launch_bf16_ffn<32, 1, 4>(x_perm, d, ffn, E, w_gate, w_up, w_down, h,
                                   y_perm, ws, max_tiles, stream);
   }
   const int n_up = (ffn + kFN - 1) / kFN;
