@@ -12,7 +12,10 @@ from .binding import (  # noqa: F401
     moe_combine,
     moe_dispatch,
     moe_dispatch_workspace_bytes,
+    moe_exchange_plan,
+    moe_exchange_workspace_bytes,
     moe_grouped_ffn,
     moe_grouped_ffn_workspace_bytes,
     moe_route_topk,
+    moe_rows_permute,
 )

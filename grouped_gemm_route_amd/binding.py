@@ -36,6 +36,10 @@ SIGNATURES = [
     ("moe_grouped_ffn", ctypes.c_int,
      [_P, _I32, _I32, _I32, _I32, _P, _I64, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     ("moe_combine", ctypes.c_int, [_P, _I32, _I32, _I32, _I32, _P, _P, _P, _P]),
+    ("moe_exchange_workspace_bytes", _SZ, [_I32, _I32]),
+    ("moe_exchange_plan", ctypes.c_int,
+     [_P, _P, _P, _P, _I32, _I32, _I32, _I32, _I64, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    ("moe_rows_permute", ctypes.c_int, [_P, _P, _P, _P, _I64, _I32, _I32, _P]),
 ]
 
 _lib = None
@@ -251,6 +255,69 @@ def moe_combine(y_perm, dest, topk_w, out=None):
     _check("moe_combine", load_library().moe_combine(
         _ptr(y_perm), code, N, d, K, _ptr(dest), _ptr(topk_w), _ptr(out), _stream(y_perm)))
     return out
+
+
+def moe_exchange_workspace_bytes(E, W):
+    return int(load_library().moe_exchange_workspace_bytes(E, W))
+
+
+def moe_exchange_plan(topk_idx, disp, E, W, out=None):
+    """Plan of the virtual W-source exchange from a dispatch's outputs.
+
+    Returns a dict with src_counts [W, E], traffic [W, W], send_row [N, K]
+    and the gather maps send_token, a2a_src, regroup_src [max_rows]."""
+    dev = topk_idx.device
+    _need(topk_idx, "topk_idx", torch.int32, dev)
+    N, K = topk_idx.shape
+    max_rows = N * K
+    for k in ("dest", "perm_token", "offsets"):
+        _need(disp[k], k, torch.int32, dev)
+    if out is None:
+        out = {
+            "src_counts": torch.empty(W, E, dtype=torch.int32, device=dev),
+            "traffic": torch.empty(W, W, dtype=torch.int32, device=dev),
+            "send_row": torch.empty(N, K, dtype=torch.int32, device=dev),
+            "send_token": torch.empty(max_rows, dtype=torch.int32, device=dev),
+            "a2a_src": torch.empty(max_rows, dtype=torch.int32, device=dev),
+            "regroup_src": torch.empty(max_rows, dtype=torch.int32, device=dev),
+            "workspace": torch.empty(max(1, moe_exchange_workspace_bytes(E, W)),
+                                     dtype=torch.uint8, device=dev),
+        }
+    sizes = {"src_counts": W * E, "traffic": W * W, "send_row": N * K, "send_token": max_rows,
+             "a2a_src": max_rows, "regroup_src": max_rows}
+    for k, n in sizes.items():
+        _need(out[k], k, torch.int32, dev)
+        if out[k].numel() < n:
+            raise ValueError(f"{k} must hold at least {n} elements")
+    ws = out["workspace"]
+    _need(ws, "workspace", None, dev)
+    _check("moe_exchange_plan", load_library().moe_exchange_plan(
+        _ptr(topk_idx), _ptr(disp["dest"]), _ptr(disp["perm_token"]), _ptr(disp["offsets"]),
+        N, E, K, W, max_rows, _ptr(out["src_counts"]), _ptr(out["traffic"]),
+        _ptr(out["send_row"]), _ptr(out["send_token"]), _ptr(out["a2a_src"]),
+        _ptr(out["regroup_src"]), _ptr(ws), ws.numel() * ws.element_size(), _stream(topk_idx)))
+    return out
+
+
+def moe_rows_permute(src, dst, row_map, n_rows, scatter=False, max_rows=None):
+    """dst[i] = src[map[i]] (gather) or dst[map[i]] = src[i] (scatter) for
+    i < min(n_rows[0], max_rows); n_rows is a one-element int32 device tensor."""
+    dev = src.device
+    _need(src, "src", None, dev)
+    _need(dst, "dst", src.dtype, dev)
+    _need(row_map, "map", torch.int32, dev)
+    _need(n_rows, "n_rows", torch.int32, dev)
+    if src.dim() != 2 or dst.dim() != 2 or src.shape[1] != dst.shape[1]:
+        raise ValueError("src and dst must be 2-D with the same row length")
+    if max_rows is None:
+        max_rows = row_map.numel()
+    if row_map.numel() < max_rows:
+        raise ValueError("map shorter than max_rows")
+    row_bytes = src.shape[1] * src.element_size()
+    _check("moe_rows_permute", load_library().moe_rows_permute(
+        _ptr(src), _ptr(dst), _ptr(row_map), _ptr(n_rows), int(max_rows), row_bytes,
+        int(bool(scatter)), _stream(src)))
+    return dst
 
 
 class MoeLayer:

@@ -203,4 +203,52 @@ int moe_combine(const void* y_perm, int32_t dtype, int32_t N, int32_t d,
                     "moe_combine");
 }
 
+size_t moe_exchange_workspace_bytes(int32_t E, int32_t W) {
+  if (E < 1 || W < 1) return 0;
+  return moe::exchange_workspace_bytes(E, W);
+}
+
+int moe_exchange_plan(const int32_t* topk_idx, const int32_t* dest,
+                      const int32_t* perm_token, const int32_t* offsets, int32_t N,
+                      int32_t E, int32_t K, int32_t W, int64_t max_rows,
+                      int32_t* src_counts, int32_t* traffic, int32_t* send_row,
+                      int32_t* send_token, int32_t* a2a_src, int32_t* regroup_src,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  if (!topk_idx || !dest || !perm_token || !offsets || !src_counts || !traffic || !send_row ||
+      !send_token || !a2a_src || !regroup_src)
+    return fail(MOE_ERR_INVALID_ARG, "moe_exchange_plan: null pointer");
+  if (N < 1 || K < 1 || K > E || W < 1 || E % W != 0 || max_rows < 0)
+    return fail(MOE_ERR_INVALID_ARG,
+                "moe_exchange_plan: need N >= 1, 1 <= K <= E, W >= 1, E %% W == 0, max_rows >= 0 "
+                "(N=%d E=%d K=%d W=%d)", N, E, K, W);
+  if ((int64_t)N * K >= ((int64_t)1 << 31) || max_rows >= ((int64_t)1 << 31))
+    return fail(MOE_ERR_INVALID_ARG, "moe_exchange_plan: N*K and max_rows must be below 2^31");
+  if (E > MOE_MAX_EXPERTS || K > MOE_MAX_TOPK || W > MOE_MAX_RANKS)
+    return fail(MOE_ERR_UNSUPPORTED, "moe_exchange_plan: E <= %d, K <= %d, W <= %d supported",
+                MOE_MAX_EXPERTS, MOE_MAX_TOPK, MOE_MAX_RANKS);
+  const size_t need = moe::exchange_workspace_bytes(E, W);
+  if (!workspace || workspace_bytes < need)
+    return fail(MOE_ERR_WORKSPACE, "moe_exchange_plan: workspace needs %zu bytes", need);
+  return hip_status(moe::launch_exchange_plan(topk_idx, dest, perm_token, offsets, N, E, K, W,
+                                              (int)max_rows, src_counts, traffic, send_row,
+                                              send_token, a2a_src, regroup_src, workspace,
+                                              as_stream(stream)),
+                    "moe_exchange_plan");
+}
+
+int moe_rows_permute(const void* src, void* dst, const int32_t* map, const int32_t* n_rows,
+                     int64_t max_rows, int32_t row_bytes, int32_t scatter, void* stream) {
+  if (!src || !dst || !map || !n_rows)
+    return fail(MOE_ERR_INVALID_ARG, "moe_rows_permute: null pointer");
+  if (max_rows < 0 || row_bytes < 16 || row_bytes % 16 != 0)
+    return fail(MOE_ERR_INVALID_ARG, "moe_rows_permute: need max_rows >= 0 and row_bytes a positive multiple of 16");
+  if (max_rows >= ((int64_t)1 << 31))
+    return fail(MOE_ERR_INVALID_ARG, "moe_rows_permute: max_rows must be below 2^31");
+  if (src == dst)
+    return fail(MOE_ERR_INVALID_ARG, "moe_rows_permute: src and dst must not be the same buffer");
+  return hip_status(moe::launch_rows_permute(src, dst, map, n_rows, (int)max_rows, row_bytes,
+                                             scatter != 0, as_stream(stream)),
+                    "moe_rows_permute");
+}
+
 }  // extern "C"

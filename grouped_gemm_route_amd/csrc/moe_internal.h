@@ -62,4 +62,17 @@ hipError_t launch_grouped_ffn(const void* x_perm, bool bf16_data, int d,
                               void* y_perm, void* workspace,
                               hipStream_t stream);
 
+size_t exchange_workspace_bytes(int E, int W);
+
+hipError_t launch_exchange_plan(const int32_t* topk_idx, const int32_t* dest,
+                                const int32_t* perm_token, const int32_t* offsets, int N,
+                                int E, int K, int W, int max_rows, int32_t* src_counts,
+                                int32_t* traffic, int32_t* send_row, int32_t* send_token,
+                                int32_t* a2a_src, int32_t* regroup_src, void* workspace,
+                                hipStream_t stream);
+
+hipError_t launch_rows_permute(const void* src, void* dst, const int32_t* map,
+                               const int32_t* n_rows, int max_rows, int row_bytes, bool scatter,
+                               hipStream_t stream);
+
 }  // namespace moe

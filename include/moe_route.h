@@ -53,6 +53,7 @@ typedef enum { MOE_DTYPE_F32 = 0, MOE_DTYPE_BF16 = 1 } moe_dtype_t;
 #define MOE_ABI_VERSION 1
 #define MOE_MAX_EXPERTS 1024
 #define MOE_MAX_TOPK 16
+#define MOE_MAX_RANKS 64
 
 /* Version of this ABI (MOE_ABI_VERSION). */
 int moe_abi_version(void);
@@ -188,6 +189,64 @@ int moe_grouped_ffn(const void* x_perm, int32_t dtype, int32_t d, int32_t ffn,
 int moe_combine(const void* y_perm, int32_t dtype, int32_t N, int32_t d,
                 int32_t K, const int32_t* dest, const float* topk_w, void* out,
                 void* stream);
+
+/* Bytes of device workspace moe_exchange_plan needs for these sizes. */
+size_t moe_exchange_workspace_bytes(int32_t E, int32_t W);
+
+/*
+ * Plan of the virtual multi-source exchange: the two local permutations on
+ * either side of the expert-parallel all-to-all, for W source ranks on one
+ * GPU.  "MoE 专家并行的 All-to-All 通信瓶颈", section "All-to-All 分发与回收的
+ * 机制": each card packs its tokens by destination card, the all-to-all
+ * moves them, and each card groups what it received by expert.  Source rank
+ * s owns tokens [floor(s*N/W), floor((s+1)*N/W)); rank r owns experts
+ * [r*E/W, (r+1)*E/W).  Layouts of the kept pairs:
+ *   send       [source][expert][token] (hence grouped by destination);
+ *   receive    [destination][source][expert][token] (after the all-to-all);
+ *   regrouped  [destination][expert][source][token], which is the
+ *              expert-contiguous order moe_dispatch produces.
+ * "MoE Inference Communication", Aurora, Theorem 4.2: the traffic matrix
+ * bounds the all-to-all time from below.
+ *
+ *   topk_idx, dest, perm_token, offsets  moe_dispatch's inputs/outputs for
+ *              the whole batch (device).
+ *   max_rows   row bound of the map arrays (N*K for a dispatch output).
+ *   src_counts [W, E] int32 out: kept pairs per (source, expert).
+ *   traffic    [W, W] int32 out: D[s][r], kept pairs source s sends to rank r.
+ *   send_row   [N, K] int32 out: send-buffer row of each kept pair, -1 if
+ *              dropped.
+ *   send_token [max_rows] int32 out: send row -> token (gather map that
+ *              packs the send buffer from x).
+ *   a2a_src    [max_rows] int32 out: receive row -> send row (the
+ *              all-to-all as a gather).
+ *   regroup_src [max_rows] int32 out: regrouped row -> receive row.
+ *   Rows at and beyond offsets[E] of the three maps are not written.
+ * Checks: pointers non-null; N >= 1; 1 <= K <= E; W >= 1, E % W == 0;
+ *         N*K, max_rows < 2^31 (INVALID_ARG); E, K, W <= MOE_MAX_RANKS
+ *         limits (UNSUPPORTED); workspace (WORKSPACE).
+ */
+int moe_exchange_plan(const int32_t* topk_idx, const int32_t* dest,
+                      const int32_t* perm_token, const int32_t* offsets, int32_t N,
+                      int32_t E, int32_t K, int32_t W, int64_t max_rows,
+                      int32_t* src_counts, int32_t* traffic, int32_t* send_row,
+                      int32_t* send_token, int32_t* a2a_src, int32_t* regroup_src,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Move whole rows by a map: dst[i] = src[map[i]] (scatter == 0, a gather)
+ * or dst[map[i]] = src[i] (scatter != 0), for i < min(*n_rows, max_rows),
+ * where n_rows is a DEVICE pointer (e.g. offsets + E, so the row count
+ * never reaches the host).  Used with the maps of moe_exchange_plan to pack
+ * send buffers, emulate the all-to-all and regroup, and (as scatters) to run
+ * the same permutations backwards for the combine direction.
+ *   src, dst   row-major buffers of row_bytes per row; must not overlap.
+ *   map        int32 row indices, each a valid row of the other buffer
+ *              (unchecked precondition).
+ * Checks: pointers non-null; max_rows >= 0 and < 2^31; row_bytes a positive
+ *         multiple of 16; src != dst (INVALID_ARG).
+ */
+int moe_rows_permute(const void* src, void* dst, const int32_t* map, const int32_t* n_rows,
+                     int64_t max_rows, int32_t row_bytes, int32_t scatter, void* stream);
 
 #ifdef __cplusplus
 }

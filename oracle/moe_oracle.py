@@ -66,6 +66,9 @@ __all__ = [
     "combine",
     "layer",
     "token_outputs",
+    "shard_bounds",
+    "exchange",
+    "tau_min",
 ]
 
 
@@ -385,3 +388,102 @@ def token_outputs(tokens, x_tokens, topk_idx, topk_w, dest, expert_weights, act)
             if dest[t, k] >= 0:
                 out[i] += w[t, k] * y_rows[(t, k)]
     return y_rows, round_storage(out, act)
+
+
+# --------------------------------------------------------------------------
+# virtual multi-source exchange (W source ranks on one GPU)
+# --------------------------------------------------------------------------
+
+def shard_bounds(N, W):
+    """Token shards of the W virtual source ranks: shard s owns tokens
+    [lo[s], lo[s+1]) with lo[s] = floor(s*N/W) (contiguous, nearly equal)."""
+    return [(s * N) // W for s in range(W + 1)]
+
+
+def exchange(topk_idx, dest, E, W):
+    """The two local permutations on either side of the all-to-all, for W
+    source ranks that each own a contiguous shard of the tokens.
+
+    "MoE 专家并行的 All-to-All 通信瓶颈", section "All-to-All 分发与回收的
+    机制": each card packs its tokens by destination card, the all-to-all
+    moves them, and each card groups what it received by expert; rank r owns
+    experts [r*E/W, (r+1)*E/W).  Built here by walking the layouts in order:
+
+      send buffer   sources s = 0..W-1 one after another; inside a source,
+                    experts in order (so destinations in order), inside an
+                    expert its kept pairs in token order;
+      receive side  destinations r = 0..W-1 one after another; inside r, the
+                    chunk of each source s in order, each chunk being source
+                    s's send rows for rank r (the all-to-all);
+      regrouped     inside r, experts in order, inside an expert the sources
+                    in order, inside a source its rows in token order.
+
+    topk_idx [N, K] and dest [N, K] (row of each kept pair in the one-source
+    dispatch, -1 when dropped).  Returns a dict: C [W, E] kept pairs per
+    (source, expert); D [W, W] pairs per (source, destination rank); and
+    three gather maps over rows, each a list of source-row indices:
+    send_token (send row -> token), a2a_src (receive row -> send row),
+    regroup_src (regrouped row -> receive row); plus send_row [N, K] (send
+    row of each kept pair, -1 when dropped).
+    """
+    idx = np.asarray(topk_idx)
+    dest = np.asarray(dest)
+    N, K = idx.shape
+    per_rank = E // W
+    lo = shard_bounds(N, W)
+    shard = [0] * N
+    for s in range(W):
+        for t in range(lo[s], lo[s + 1]):
+            shard[t] = s
+    # kept pairs by (source, expert), each list in token order
+    pairs = [[[] for _ in range(E)] for _ in range(W)]
+    for t in range(N):
+        for k in range(K):
+            if dest[t, k] >= 0:
+                pairs[shard[t]][int(idx[t, k])].append((t, k))
+    C = np.array([[len(pairs[s][e]) for e in range(E)] for s in range(W)], dtype=np.int64)
+    D = np.array([[int(C[s][r * per_rank:(r + 1) * per_rank].sum()) for r in range(W)]
+                  for s in range(W)], dtype=np.int64)
+
+    send_token, send_row = [], np.full((N, K), -1, dtype=np.int64)
+    send_pos = {}
+    for s in range(W):
+        for e in range(E):
+            for (t, k) in pairs[s][e]:
+                send_pos[(t, k)] = len(send_token)
+                send_row[t, k] = len(send_token)
+                send_token.append(t)
+    a2a_src, recv_pos = [], {}
+    for r in range(W):
+        for s in range(W):
+            for e in range(r * per_rank, (r + 1) * per_rank):
+                for (t, k) in pairs[s][e]:
+                    recv_pos[(t, k)] = len(a2a_src)
+                    a2a_src.append(send_pos[(t, k)])
+    regroup_src, regroup_pair = [], []
+    for r in range(W):
+        for e in range(r * per_rank, (r + 1) * per_rank):
+            for s in range(W):
+                for (t, k) in pairs[s][e]:
+                    regroup_src.append(recv_pos[(t, k)])
+                    regroup_pair.append((t, k))
+    return {
+        "C": C.astype(np.int32),
+        "D": D.astype(np.int32),
+        "send_token": np.array(send_token, dtype=np.int32),
+        "send_row": send_row.astype(np.int32),
+        "a2a_src": np.array(a2a_src, dtype=np.int32),
+        "regroup_src": np.array(regroup_src, dtype=np.int32),
+        "regroup_pair": regroup_pair,
+    }
+
+
+def tau_min(D, bandwidth=1.0):
+    """Lower bound on the all-to-all time for traffic matrix D (rows sent by
+    source i to destination j): the busiest sender's or receiver's volume
+    over the per-GPU bandwidth ("MoE Inference Communication", Aurora,
+    Theorem 4.2).  Only traffic that leaves a rank counts: the diagonal
+    (a rank's pairs for its own experts) moves no data over a link."""
+    D = np.asarray(D, dtype=np.float64)
+    off = D - np.diag(np.diag(D))
+    return max(off.sum(axis=1).max(), off.sum(axis=0).max()) / bandwidth

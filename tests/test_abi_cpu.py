@@ -156,3 +156,27 @@ def test_binding_refuses_cpu_tensors():
     import torch
     with pytest.raises(ValueError):
         B.moe_route_topk(torch.zeros(4, 8), 2)
+
+
+def test_exchange_plan_rejects_bad_arguments(lib):
+    f = lib.moe_exchange_plan
+    args = [FAKE] * 4 + [8, 8, 2, 4, 16] + [FAKE] * 7 + [1 << 20, NUL]
+    a = list(args); a[0] = NUL
+    assert f(*a) == 1                                   # null pointer
+    a = list(args); a[7] = 3
+    assert f(*a) == 1                                   # E % W != 0
+    a = list(args); a[6] = 9
+    assert f(*a) == 1                                   # K > E
+    a = list(args); a[7] = 128; a[5] = 128
+    assert f(*a) == 2                                   # W beyond the limit
+    a = list(args); a[16] = 1
+    assert f(*a) == 3                                   # workspace too small
+    assert lib.moe_exchange_workspace_bytes(8, 4) > 0
+
+
+def test_rows_permute_rejects_bad_arguments(lib):
+    f = lib.moe_rows_permute
+    assert f(NUL, FAKE, FAKE, FAKE, 4, 64, 0, NUL) == 1
+    assert f(FAKE, ctypes.c_void_p(8192), FAKE, FAKE, 4, 24, 0, NUL) == 1   # row bytes
+    assert f(FAKE, FAKE, FAKE, FAKE, 4, 64, 0, NUL) == 1                   # src == dst
+    assert f(FAKE, ctypes.c_void_p(8192), FAKE, FAKE, -1, 64, 0, NUL) == 1
