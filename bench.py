@@ -47,6 +47,8 @@ def parse():
     p.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"))
     p.add_argument("--cold-reps", type=int, default=10,
                    help="reps of the cold-cache dispatch/combine timing (0 skips it)")
+    p.add_argument("--no-exchange", action="store_true",
+                   help="skip the virtual multi-source exchange measurements")
     p.add_argument("--copy-ref-mib", type=int, default=0,
                    help="run one plain device-to-device copy of this many MiB first "
                         "(the reference kernel for scaling HBM byte counters)")
@@ -250,9 +252,94 @@ def main():
         "stages": stages,
     }
 
+    result["metrics"] = routing_metrics(layer, cfg, cap, M)
+    if not args.no_exchange:
+        result["exchange"] = exchange_block(B, layer, inp["x"], cfg, M, b, stream)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_sample_tokens)
     print(json.dumps(result))
+
+
+XGMI_EGRESS_GBPS = 7 * 153.0   # MI355X: 7 xGMI links of about 153 GB/s each
+
+
+def routing_metrics(layer, cfg, cap, M):
+    """Load and drop metrics of the dispatch ("MoE 推理服务工程真相 2026",
+    section 5.1: expert load per card std/mean, overflow rate, token drops),
+    from the library's demand / counts outputs."""
+    import numpy as np
+
+    E, W, N, K = cfg["E"], cfg["W"], cfg["N"], cfg["K"]
+    demand = layer.disp["demand"].cpu().numpy().astype(np.int64)
+    counts = layer.disp["counts"].cpu().numpy().astype(np.int64)
+    per_rank = counts.reshape(W, E // W).sum(axis=1)
+    return {
+        "kept_rows": M,
+        "dropped_pairs": int(N * K - M),
+        "drop_rate": float((N * K - M) / (N * K)),
+        "experts_overflowing": int((demand > cap).sum()) if cap >= 0 else 0,
+        "expert_overflow_rate": float((demand > cap).mean()) if cap >= 0 else 0.0,
+        "nonempty_experts": int((counts > 0).sum()),
+        "max_rows_per_expert": int(counts.max()),
+        "rank_load_std_over_mean": float(per_rank.std() / max(per_rank.mean(), 1e-9)),
+        "rank_load_max_over_min": float(per_rank.max() / max(per_rank.min(), 1)),
+    }
+
+
+def exchange_block(B, layer, src_x, cfg, M, b, stream):
+    """The virtual W-source exchange around the all-to-all: plan, pack,
+    all-to-all (as a local gather), regroup; the W x W traffic matrix and
+    Aurora's lower bound on the all-to-all time ("MoE Inference
+    Communication", Theorem 4.2), in rows, bytes and at MI355X xGMI egress.
+    Timed alone on warm buffers, outside the timed steps."""
+    import numpy as np
+    import torch
+
+    E, W, d = cfg["E"], cfg["W"], cfg["d"]
+    x = layer.disp["x_perm"]
+    dev = x.device
+    plan = B.moe_exchange_plan(layer.topk_idx, layer.disp, E, W)
+    n_rows = layer.disp["offsets"][E:E + 1]
+    send = torch.empty_like(x)
+    recv = torch.empty_like(x)
+    regrouped = torch.empty_like(x)
+
+    def timed(fn, reps=5):
+        fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        e1.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    t_plan = timed(lambda: B.moe_exchange_plan(layer.topk_idx, layer.disp, E, W, plan))
+    t_pack = timed(lambda: B.moe_rows_permute(src_x, send, plan["send_token"], n_rows))
+    t_a2a = timed(lambda: B.moe_rows_permute(send, recv, plan["a2a_src"], n_rows))
+    t_reg = timed(lambda: B.moe_rows_permute(recv, regrouped, plan["regroup_src"], n_rows))
+    torch.cuda.synchronize()
+    same = bool(torch.equal(regrouped[:M], layer.disp["x_perm"][:M]))
+    D = plan["traffic"].cpu().numpy().astype(np.int64)
+    off = D - np.diag(np.diag(D))
+    tau_rows = int(max(off.sum(axis=1).max(), off.sum(axis=0).max()))
+    row_bytes = d * b
+    moved = 2.0 * M * row_bytes   # each permutation reads and writes M rows
+    return {
+        "plan_us": t_plan * 1e3,
+        "pack_us": t_pack * 1e3,
+        "a2a_local_us": t_a2a * 1e3,
+        "regroup_us": t_reg * 1e3,
+        "permute_GBps": moved / (t_a2a * 1e-3) / 1e9,
+        "regrouped_equals_dispatch": same,
+        "traffic_matrix_rows": D.tolist(),
+        "cross_rank_fraction": float(off.sum() / max(D.sum(), 1)),
+        "tau_min_rows": tau_rows,
+        "tau_min_bytes": tau_rows * row_bytes,
+        "tau_min_us_at_xgmi_egress": tau_rows * row_bytes / (XGMI_EGRESS_GBPS * 1e9) * 1e6,
+    }
 
 
 def cpu_baseline(cfg, inp, n_tok):
