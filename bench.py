@@ -255,6 +255,7 @@ def main():
     result["metrics"] = routing_metrics(layer, cfg, cap, M)
     if not args.no_exchange:
         result["exchange"] = exchange_block(B, layer, inp["x"], cfg, M, b, stream)
+        result["router_projection"] = router_block(B, synth, inp["x"], cfg, b, stream)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_sample_tokens)
     print(json.dumps(result))
@@ -340,6 +341,30 @@ def exchange_block(B, layer, src_x, cfg, M, b, stream):
         "tau_min_bytes": tau_rows * row_bytes,
         "tau_min_us_at_xgmi_egress": tau_rows * row_bytes / (XGMI_EGRESS_GBPS * 1e9) * 1e6,
     }
+
+
+def router_block(B, synth, x, cfg, b, stream):
+    """Router projection logits = x @ w_router^T (fp32), timed alone on warm
+    buffers: HBM bytes (x, w_router, logits) and flops."""
+    import torch
+
+    N, d, E = cfg["N"], cfg["d"], cfg["E"]
+    wr = synth.make_router(cfg, x.device)
+    logits = torch.empty(N, E, dtype=torch.float32, device=x.device)
+    B.moe_router_logits(x, wr, logits)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    reps = 10
+    e0.record(stream)
+    for _ in range(reps):
+        B.moe_router_logits(x, wr, logits)
+    e1.record(stream)
+    e1.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    nbytes = N * d * b + E * d * b + N * E * 4
+    return {"us": ms * 1e3, "GBps": nbytes / (ms * 1e-3) / 1e9,
+            "TFLOPs": 2.0 * N * d * E / (ms * 1e-3) / 1e12}
 
 
 def cpu_baseline(cfg, inp, n_tok):

@@ -17,5 +17,6 @@ from .binding import (  # noqa: F401
     moe_grouped_ffn,
     moe_grouped_ffn_workspace_bytes,
     moe_route_topk,
+    moe_router_logits,
     moe_rows_permute,
 )

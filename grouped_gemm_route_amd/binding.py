@@ -36,6 +36,7 @@ SIGNATURES = [
     ("moe_grouped_ffn", ctypes.c_int,
      [_P, _I32, _I32, _I32, _I32, _P, _I64, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     ("moe_combine", ctypes.c_int, [_P, _I32, _I32, _I32, _I32, _P, _P, _P, _P]),
+    ("moe_router_logits", ctypes.c_int, [_P, _I32, _I32, _I32, _P, _I32, _P, _P]),
     ("moe_exchange_workspace_bytes", _SZ, [_I32, _I32]),
     ("moe_exchange_plan", ctypes.c_int,
      [_P, _P, _P, _P, _I32, _I32, _I32, _I32, _I64, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
@@ -141,6 +142,26 @@ def moe_route_topk(logits, K, renormalize=False, topk_idx=None, topk_w=None):
         _ptr(logits), N, E, K, int(bool(renormalize)), _ptr(topk_idx), _ptr(topk_w),
         _stream(logits)))
     return topk_idx, topk_w
+
+
+def moe_router_logits(x, w_router, logits=None):
+    """Router projection: returns fp32 logits [N, E] = x @ w_router^T."""
+    _need(x, "x")
+    code = _act_code(x, "x")
+    N, d = x.shape
+    dev = x.device
+    _need(w_router, "w_router", x.dtype, dev)
+    E, d2 = w_router.shape
+    if d2 != d:
+        raise ValueError("w_router must be [E, d]")
+    if logits is None:
+        logits = torch.empty(N, E, dtype=torch.float32, device=dev)
+    _need(logits, "logits", torch.float32, dev)
+    if logits.numel() < N * E:
+        raise ValueError("logits too small")
+    _check("moe_router_logits", load_library().moe_router_logits(
+        _ptr(x), code, N, d, _ptr(w_router), E, _ptr(logits), _stream(x)))
+    return logits
 
 
 def moe_dispatch_workspace_bytes(N, E, K):

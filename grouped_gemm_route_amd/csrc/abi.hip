@@ -203,6 +203,25 @@ int moe_combine(const void* y_perm, int32_t dtype, int32_t N, int32_t d,
                     "moe_combine");
 }
 
+int moe_router_logits(const void* x, int32_t dtype, int32_t N, int32_t d,
+                      const void* w_router, int32_t E, float* logits, void* stream) {
+  if (!x || !w_router || !logits)
+    return fail(MOE_ERR_INVALID_ARG, "moe_router_logits: null pointer");
+  const int es = elem_size(dtype);
+  if (es == 0) return fail(MOE_ERR_UNSUPPORTED, "moe_router_logits: dtype %d", dtype);
+  if (N < 1 || d < 1 || E < 1)
+    return fail(MOE_ERR_INVALID_ARG, "moe_router_logits: need N, d, E >= 1");
+  if (E > MOE_MAX_EXPERTS)
+    return fail(MOE_ERR_UNSUPPORTED, "moe_router_logits: E <= %d supported", MOE_MAX_EXPERTS);
+  if (dtype == MOE_DTYPE_BF16 && d % 64 != 0)
+    return fail(MOE_ERR_UNSUPPORTED, "moe_router_logits: bf16 needs d a multiple of 64 (d=%d)", d);
+  if ((int64_t)N * E >= ((int64_t)1 << 31) || (int64_t)256 * d * es >= ((int64_t)1 << 31))
+    return fail(MOE_ERR_UNSUPPORTED, "moe_router_logits: sizes too large");
+  return hip_status(moe::launch_router_logits(x, dtype == MOE_DTYPE_BF16, N, d, w_router, E,
+                                              logits, as_stream(stream)),
+                    "moe_router_logits");
+}
+
 size_t moe_exchange_workspace_bytes(int32_t E, int32_t W) {
   if (E < 1 || W < 1) return 0;
   return moe::exchange_workspace_bytes(E, W);

@@ -62,6 +62,10 @@ hipError_t launch_grouped_ffn(const void* x_perm, bool bf16_data, int d,
                               void* y_perm, void* workspace,
                               hipStream_t stream);
 
+hipError_t launch_router_logits(const void* x, bool bf16_data, int N, int d,
+                                const void* w_router, int E, float* logits,
+                                hipStream_t stream);
+
 size_t exchange_workspace_bytes(int E, int W);
 
 hipError_t launch_exchange_plan(const int32_t* topk_idx, const int32_t* dest,

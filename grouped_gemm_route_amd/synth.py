@@ -132,6 +132,13 @@ def make_weights(cfg, device="cpu"):
     return wg, wu, wd
 
 
+def make_router(cfg, device="cpu"):
+    """Router weights w_router [E, d], N(0, std = 1/sqrt(d)), activation type."""
+    g = _gen(cfg, "w_router", 0, device)
+    z = torch.randn(cfg["E"], cfg["d"], generator=g, device=device, dtype=torch.float32)
+    return (z * (1.0 / math.sqrt(cfg["d"]))).to(TORCH_DTYPE[cfg["act"]])
+
+
 def make_inputs(cfg, device="cpu", weights=True):
     """logits, x and (optionally) the three weight tensors of a config."""
     res = {"logits": make_logits(cfg, device), "x": make_x(cfg, device)}

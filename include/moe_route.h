@@ -95,6 +95,23 @@ int moe_route_topk(const float* logits, int32_t N, int32_t E, int32_t K,
                    int32_t renormalize, int32_t* topk_idx, float* topk_w,
                    void* stream);
 
+/*
+ * Router projection: logits[t, e] = sum_i x[t, i] * w_router[e, i] for all
+ * N tokens and E experts, accumulated in fp32 and stored as fp32 (the input
+ * of moe_route_topk).  The router turns each token's hidden state into
+ * expert scores before the Top-K choice ("MoE 推理服务工程真相 2026",
+ * section 一; "MoE 专家并行的 All-to-All 通信瓶颈", flowchart step
+ * "路由器选 Top-K 专家").  Summation order differs from any reference, so
+ * logits agree with an exact sum to within the fp32 summation bound and
+ * near-ties may order differently.
+ *   x          [N, d] of dtype; w_router [E, d] of dtype; logits [N, E] fp32 out.
+ * Checks: pointers non-null; N, d, E >= 1 (INVALID_ARG); dtype; E <=
+ *         MOE_MAX_EXPERTS; bf16 needs d a multiple of 64; N*E < 2^31
+ *         (UNSUPPORTED).
+ */
+int moe_router_logits(const void* x, int32_t dtype, int32_t N, int32_t d,
+                      const void* w_router, int32_t E, float* logits, void* stream);
+
 /* Bytes of device workspace moe_dispatch needs for these sizes. */
 size_t moe_dispatch_workspace_bytes(int32_t N, int32_t E, int32_t K);
 

@@ -66,6 +66,8 @@ __all__ = [
     "combine",
     "layer",
     "token_outputs",
+    "router_logits",
+    "router_logits_error_bound",
     "shard_bounds",
     "exchange",
     "tau_min",
@@ -134,6 +136,41 @@ def capacity(C, N, K, E):
         raise ValueError("capacity factor must be finite and > 0")
     v = Fraction(C) * N * K / E
     return int(math.ceil(v))
+
+
+# --------------------------------------------------------------------------
+# router projection
+# --------------------------------------------------------------------------
+
+def router_logits(x, w_router):
+    """Router logits of every token: logits[t, e] = sum_i x[t, i] * w[e, i].
+
+    The router yields each token's expert scores from its hidden state ("MoE
+    推理服务工程真相 2026", section 一: the token passes through the router
+    network before top-k selection; "MoE 专家并行的 All-to-All 通信瓶颈",
+    flowchart step "路由器选 Top-K 专家").  Computed exactly in float64 (the
+    products of bf16 or fp32 inputs and their sums up to d terms are exact
+    or nearly so) and rounded once to fp32, the logits' storage type.
+    x [N, d], w_router [E, d] hold values of the activation type.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    w = np.asarray(w_router, dtype=np.float64)
+    return (x @ w.T).astype(np.float32)
+
+
+def router_logits_error_bound(x, w_router):
+    """Per-logit bound on |fp32-accumulated sum - exact sum| for any order of
+    the d-term summation: gamma_{d} * sum_i |x_i w_i| with gamma_n =
+    n u / (1 - n u), u = 2**-24 (the standard bound for floating-point
+    summation, products being exact), plus half an ulp for the final fp32
+    rounding of the reference."""
+    x = np.abs(np.asarray(x, dtype=np.float64))
+    w = np.abs(np.asarray(w_router, dtype=np.float64))
+    d = x.shape[1]
+    u = 2.0 ** -24
+    gamma = d * u / (1 - d * u)
+    mag = x @ w.T
+    return gamma * mag + u * mag
 
 
 # --------------------------------------------------------------------------

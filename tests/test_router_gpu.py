@@ -1,0 +1,67 @@
+"""Router projection on the GPU vs the oracle: logits within the fp32
+summation bound of the exact sums; Top-K on the GPU's logits bit-exact with
+the oracle's route of those logits, and equal to the route of the exact
+logits wherever the K-th / (K+1)-th gap exceeds twice the bound."""
+import numpy as np
+import pytest
+import torch
+
+from grouped_gemm_route_amd import binding as B
+from grouped_gemm_route_amd import synth
+from oracle import moe_oracle as O
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+CASES = {
+    "tiny_f32": (synth.config("tiny_f32"), None),
+    "dense8": (synth.config("dense8"), 512),
+    "fine128": (synth.config("fine128_zipf_c1.25"), 512),
+    "decode256": (synth.config("decode256"), None),
+    "prefill256": (synth.config("prefill256_hot"), 256),
+    "ragged_n_e": (synth.config("rt_ragged", N=333, d=192, ffn=64, E=70, K=3, W=2,
+                                act="bf16"), None),
+    "e1024": (synth.config("rt_e1024", N=97, d=128, ffn=64, E=1024, K=16, W=8, act="bf16"),
+              None),
+}
+
+
+def _np(t):
+    return (t.float() if t.dtype == torch.bfloat16 else t).detach().cpu().numpy()
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_router_logits_and_route(name):
+    cfg, sample = CASES[name]
+    print(f"[router] {name}", flush=True)
+    x = synth.make_x(cfg, DEV)
+    wr = synth.make_router(cfg, DEV)
+    logits = B.moe_router_logits(x, wr)
+    idx, w = B.moe_route_topk(logits, cfg["K"])
+    torch.cuda.synchronize()
+    N = cfg["N"]
+    rows = np.arange(N) if sample is None else np.unique(
+        np.concatenate([[0, N - 1], np.random.default_rng(1).choice(N, sample, replace=False)]))
+    xs = _np(x)[rows]
+    wn = _np(wr)
+    exact = xs.astype(np.float64) @ wn.astype(np.float64).T
+    got = _np(logits)[rows].astype(np.float64)
+    bound = O.router_logits_error_bound(xs, wn)
+    assert (np.abs(got - exact) <= bound).all(), float((np.abs(got - exact) - bound).max())
+    ref32 = O.router_logits(xs, wn)
+    assert (np.abs(got - ref32) <= bound + np.abs(ref32) * 2.0 ** -24).all()
+    # route of the GPU's logits: bit-exact with the oracle's route of them
+    gi, gw = O.route(_np(logits)[rows], cfg["K"])
+    assert np.array_equal(_np(idx)[rows], gi)
+    assert np.abs(_np(w)[rows] - gw).max() <= 1e-6
+    # where the exact top-K is separated by more than the error, it is the same
+    ei, _ = O.route(ref32, cfg["K"])
+    srt = -np.sort(-exact, axis=1)
+    K, E = cfg["K"], cfg["E"]
+    if K < E:
+        gap = srt[:, K - 1] - srt[:, K]
+        clear = gap > 2 * bound.max(axis=1)
+        assert clear.any()  # the check below must cover some tokens
+        assert np.array_equal(np.sort(_np(idx)[rows][clear], 1), np.sort(ei[clear], 1))
+    print(f"[router] {name}: rows checked {len(rows)} max err {np.abs(got - exact).max():.3e}",
+          flush=True)
