@@ -51,28 +51,76 @@ constexpr int kThreads = 256;
 // tile schedule
 // ---------------------------------------------------------------------------
 
-// Workspace layout: [num_tiles | pad to 256 B][tile_start[E+1] | pad][tiles].
+// Split reduction.  A block-tile grid rarely divides evenly among the
+// resident block slots (one block per CU): the 576 blocks of an 8-expert
+// down projection over 8192 rows with d = 4096 fill 256 CUs twice and then a
+// quarter of them.  The tiles of such a last, partial round are split along
+// the reduction into up to kMaxSplit pieces, so that the round fills the
+// chip; each piece writes its fp32 accumulators to a workspace slot and the
+// last piece to finish adds the pieces up in piece order (a fixed order, so
+// results do not depend on which piece finishes last) and stores the tile.
+constexpr int kMaxSplitUnits = 256;  // split pieces per launch (block slots)
+constexpr int kMaxSplit = 8;         // pieces per tile
+constexpr int kMinSplitTiles = 8;    // reduction tiles per piece, at least
+
+// Workspace layout: [num_tiles | pad to 256 B][split counters: 2 x
+// kMaxSplitUnits ints][XCD block tables: 2 passes x 8 XCDs x (E+1) ints |
+// pad][tile_start[E+1] | pad][tiles | pad][split partials].
 struct FfnWorkspace {
   int* num_tiles;
+  int* split_cnt;   // arrival counters of split tiles: gate/up pass, then down
+  int* xcd_start;   // [pass][xcd][E+1]: the XCD's blocks for experts < e
   int* tile_start;  // tiles of expert e are slots [tile_start[e], tile_start[e+1])
   int4* tiles;      // (expert, first row, end row, 0)
+  float* partial;   // kMaxSplitUnits fp32 accumulator tiles of BM x 256
 };
 
-inline FfnWorkspace ffn_workspace(void* base, int E) {
+constexpr int kXcds = 8;  // block b runs on XCD b % 8
+constexpr size_t kSplitCntBytes = 2 * kMaxSplitUnits * sizeof(int);
+
+inline size_t ffn_xcd_table_bytes(int E) {
+  return align_up((size_t)2 * kXcds * (E + 1) * sizeof(int), 256);
+}
+
+inline size_t ffn_tiles_offset(int E) {
+  return 256 + kSplitCntBytes + ffn_xcd_table_bytes(E) +
+         align_up((size_t)(E + 1) * sizeof(int), 256);
+}
+
+inline FfnWorkspace ffn_workspace(void* base, int E, int max_tiles) {
   char* p = static_cast<char*>(base);
   FfnWorkspace ws;
   ws.num_tiles = reinterpret_cast<int*>(p);
-  ws.tile_start = reinterpret_cast<int*>(p + 256);
-  ws.tiles = reinterpret_cast<int4*>(p + 256 + align_up((size_t)(E + 1) * sizeof(int), 256));
+  ws.split_cnt = reinterpret_cast<int*>(p + 256);
+  ws.xcd_start = reinterpret_cast<int*>(p + 256 + kSplitCntBytes);
+  ws.tile_start = reinterpret_cast<int*>(p + 256 + kSplitCntBytes + ffn_xcd_table_bytes(E));
+  ws.tiles = reinterpret_cast<int4*>(p + ffn_tiles_offset(E));
+  ws.partial = reinterpret_cast<float*>(
+      p + ffn_tiles_offset(E) + align_up((size_t)max_tiles * sizeof(int4), 256));
   return ws;
+}
+
+// Column tiles n of expert e that XCD x runs: n = xcd_first_n(e, x, n) + 8 k.
+// Expert e's column tiles are dealt round-robin over the XCDs, continuing
+// where expert e - 1 stopped, so every XCD gets about the same share of
+// every expert (of its thin and full row tiles alike).
+__device__ __forceinline__ int xcd_first_n(int e, int x, int n_tiles) {
+  const int start = ((e % kXcds) * (n_tiles % kXcds)) % kXcds;  // (e * n_tiles) % 8
+  return (x - start + kXcds) % kXcds;
+}
+__device__ __forceinline__ int xcd_groups(int e, int x, int n_tiles) {
+  const int f = xcd_first_n(e, x, n_tiles);
+  return f < n_tiles ? (n_tiles - f + kXcds - 1) / kXcds : 0;
 }
 
 __global__ __launch_bounds__(1024) void ffn_schedule_kernel(
     const int32_t* __restrict__ offsets, int E, int tile_rows, int max_rows,
-    int max_tiles, int4* __restrict__ tiles, int* __restrict__ tile_start,
-    int* __restrict__ num_tiles) {
+    int max_tiles, int n_up, int n_dn, int4* __restrict__ tiles,
+    int* __restrict__ tile_start, int* __restrict__ num_tiles,
+    int* __restrict__ split_cnt, int* __restrict__ xcd_start) {
   __shared__ int wave_sums[1024 / kWave];
   const int e = threadIdx.x;
+  if (e < 2 * kMaxSplitUnits) split_cnt[e] = 0;
   int a = 0, b = 0, nt = 0;
   if (e < E) {
     a = min(max(offsets[e], 0), max_rows);
@@ -91,6 +139,32 @@ __global__ __launch_bounds__(1024) void ffn_schedule_kernel(
     }
   }
   if (e == 0) *num_tiles = min(total, max_tiles);
+  // Per pass and XCD, the exclusive scan over experts of the XCD's blocks:
+  // wave w < 16 scans the table of pass w / 8 and XCD w % 8, 64 experts at
+  // a time.
+  __shared__ int cnt_s[1024];
+  cnt_s[e] = e < E ? min(base + nt, max_tiles) - min(base, max_tiles) : 0;
+  __syncthreads();
+  const int wave = e / kWave, lane = e % kWave;
+  if (wave < 2 * kXcds) {
+    const int x = wave % kXcds;
+    const int n_tiles = wave < kXcds ? n_up : n_dn;
+    int* P = xcd_start + wave * (E + 1);
+    int run = 0;
+    for (int c = 0; c < E; c += kWave) {
+      const int ee = c + lane;
+      const int v = ee < E ? xcd_groups(ee, x, n_tiles) * cnt_s[ee] : 0;
+      int incl = v;
+#pragma unroll
+      for (int off = 1; off < kWave; off <<= 1) {
+        const int o = __shfl_up(incl, off);
+        if (lane >= off) incl += o;
+      }
+      if (ee < E) P[ee] = run + incl - v;
+      run += __shfl(incl, kWave - 1);
+    }
+    if (lane == 0) P[E] = run;
+  }
 }
 
 inline int max_tiles_for(int64_t max_rows, int E, int tile_rows) {
@@ -124,6 +198,67 @@ __device__ __forceinline__ bool map_block(const int* __restrict__ tile_start,
   const int r = L - n_tiles * first;
   *n_tile = r / cnt;
   *slot = first + r % cnt;
+  return true;
+}
+
+// Work unit of a bf16 GEMM block: a tile slot and column tile, and the range
+// [kb, ke) of reduction tiles.  For a piece of a split tile, split >= 0
+// numbers the tile's arrival counter, the tile is piece `piece` of `parts`
+// and its pieces' partials go to workspace slots pslot0 + 0 .. parts - 1.
+struct Unit {
+  int slot, n_tile, kb, ke, split, piece, parts, pslot0;
+};
+
+// Block -> work unit.  Block b runs on XCD x = b % 8 as that XCD's block
+// i = b / 8.  XCD x works through its own list: expert by expert, its share
+// of the expert's column tiles (dealt round-robin, see xcd_first_n), and
+// for each column tile all of the expert's row tiles, so that the blocks an
+// XCD runs together share one weight tile and a few activation tiles
+// through its L2.  xcd_start (the XCD's row of the schedule's table) gives
+// the list position of each expert's first block.
+//
+// With cps blocks resident per XCD, the first B - R entries of a list of B
+// (R = B mod cps, the XCD's partial last round) are whole tiles; each of the
+// last R tiles becomes s = min(cps / R, kMaxSplit, nk / kMinSplitTiles)
+// pieces of consecutive reduction tiles, which take the XCD's block numbers
+// after the whole tiles and so fill its last round.  s < 2 leaves every
+// tile whole.
+__device__ __forceinline__ bool map_unit(const int* __restrict__ tile_start,
+                                         const int* __restrict__ xcd_start, int E,
+                                         int n_tiles, int nk, int cps, Unit* w) {
+  const int x = blockIdx.x % kXcds;
+  const int i = blockIdx.x / kXcds;
+  const int* __restrict__ P = xcd_start + x * (E + 1);
+  const int B = P[E];
+  const int R = B % cps;
+  int s = R > 0 ? min(min(cps / R, kMaxSplit), nk / kMinSplitTiles) : 1;
+  if (s < 2) s = 1;
+  const int whole = s > 1 ? B - R : B;
+  // (fields are set once, at the end: per-branch stores to a struct through
+  // a pointer can end up in scratch memory)
+  const bool is_piece = i >= whole;
+  const int p = i - whole;
+  if (is_piece && (s == 1 || p >= R * s)) return false;
+  const int t = is_piece ? p / s : 0;
+  const int piece = is_piece ? p % s : 0;
+  const int parts = is_piece ? s : 1;
+  const int entry = is_piece ? whole + t : i;
+  int lo = 0, hi = E;  // P[lo] <= entry < P[hi]: expert lo has blocks here
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (P[mid] <= entry) lo = mid; else hi = mid;
+  }
+  const int first = tile_start[lo];
+  const int cnt = tile_start[lo + 1] - first;
+  const int r = entry - P[lo];
+  *w = Unit{first + r % cnt,
+            xcd_first_n(lo, x, n_tiles) + kXcds * (r / cnt),
+            piece * nk / parts,
+            (piece + 1) * nk / parts,
+            is_piece ? x * cps + t : -1,
+            piece,
+            parts,
+            x * cps + t * s};
   return true;
 }
 
@@ -168,7 +303,17 @@ struct TileGeo {
   // the NW waves together fill 8 NW rows per round
   static constexpr int kWLoads = kBW / (8 * NW);
   static constexpr int kALoads = BM / (8 * NW);
-  static constexpr size_t kLds = (size_t)kWRegion + 3 * (size_t)kWSlotBytes;
+  static constexpr size_t kMainLds = (size_t)kWRegion + 3 * (size_t)kWSlotBytes;
+  // Thin tiles (at most 32 token rows: an expert's ragged last tile, or every
+  // tile of a decode-sized layer) do a few MFMAs per reduction tile and would
+  // wait on load latency, so they use rings four deep for both operands,
+  // loaded three reduction tiles ahead: 32-row activation slots, then
+  // four weight slots.  A thin activation slot is one load per wave.
+  static constexpr bool kThin = NW * 8 == 32;
+  static constexpr int kThinABytes = 32 * kRowBytes;
+  static constexpr int kThinWRegion = 4 * kThinABytes;
+  static constexpr size_t kThinLds = (size_t)kThinWRegion + 4 * (size_t)kWSlotBytes;
+  static constexpr size_t kLds = kThin && kThinLds > kMainLds ? kThinLds : kMainLds;
   static_assert(kALoads >= 1 && kTM >= 1 && kTW >= 2, "tile shape");
 };
 
@@ -177,11 +322,15 @@ __global__ __launch_bounds__(NW * kWave, 1) void ffn_gemm_bf16_kernel(
     const bf16* __restrict__ act, int Kdim, const bf16* __restrict__ w0,
     const bf16* __restrict__ w1, int Nout, bf16* __restrict__ out,
     const int4* __restrict__ tiles, const int* __restrict__ tile_start,
-    const int* __restrict__ num_tiles, int E, int n_tiles) {
+    const int* __restrict__ xcd_start, int E, int n_tiles, int cps,
+    float* __restrict__ partial, int* __restrict__ split_cnt) {
   using G = TileGeo<BM, WM, NW>;
   extern __shared__ __attribute__((aligned(16))) bf16 lds[];
-  int slot, n_tile;
-  if (!map_block(tile_start, num_tiles, E, n_tiles, &slot, &n_tile)) return;
+  Unit unit;
+  if (!map_unit(tile_start, xcd_start, E, n_tiles, Kdim / kBK, cps, &unit)) return;
+  const int slot = unit.slot;
+  const int n_tile = unit.n_tile;
+  const int kofs = unit.kb * kBK;  // first reduction element of this unit
   const int4 tile = tiles[slot];
   const int e = tile.x;
   const int row0 = tile.y;
@@ -230,21 +379,20 @@ __global__ __launch_bounds__(NW * kWave, 1) void ffn_gemm_bf16_kernel(
   // (offsets go through locals and each descriptor has its own call: an
   // array element or a conditional expression of descriptor type as a
   // builtin argument here drops the kernel's host-side stub)
-  auto issue_wload = [&](int wslot, int k0, int i) __attribute__((always_inline)) {
+  // (LDS destinations and operand sources are byte offsets of a ring slot)
+  auto issue_wload = [&](int woff, int k0, int i) __attribute__((always_inline)) {
     const int voff = w_src[i];
-    const int soff = k0 * (int)sizeof(bf16);
-    lds_void_t* dst = (lds_void_t*)(lds_bytes + G::kWRegion + wslot * G::kWSlotBytes +
-                                    (i * NW + wave) * 8 * kRowBytes);
+    const int soff = (kofs + k0) * (int)sizeof(bf16);
+    lds_void_t* dst = (lds_void_t*)(lds_bytes + woff + (i * NW + wave) * 8 * kRowBytes);
     if (kDual && i >= G::kWLoads / 2)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(wr1, dst, 16, voff, soff, 0, 0);
     else
       __builtin_amdgcn_raw_ptr_buffer_load_lds(wr0, dst, 16, voff, soff, 0, 0);
   };
-  auto issue_aload = [&](int stage, int k0, int i) __attribute__((always_inline)) {
+  auto issue_aload = [&](int aoff, int k0, int i) __attribute__((always_inline)) {
     const int voff = a_src[i];
-    const int soff = k0 * (int)sizeof(bf16);
-    lds_void_t* dst = (lds_void_t*)(lds_bytes + stage * G::kAStageBytes +
-                                    (i * NW + wave) * 8 * kRowBytes);
+    const int soff = (kofs + k0) * (int)sizeof(bf16);
+    lds_void_t* dst = (lds_void_t*)(lds_bytes + aoff + (i * NW + wave) * 8 * kRowBytes);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(ar, dst, 16, voff, soff, 0, 0);
   };
 
@@ -285,7 +433,7 @@ __global__ __launch_bounds__(NW * kWave, 1) void ffn_gemm_bf16_kernel(
 #pragma unroll
   for (int ks = 0; ks < kBK / 16; ++ks) {
     const int chunk = ks * 2 + lhalf;
-    wbase[ks] = G::kWRegion + swz(wrow[0] + lrow, chunk) * (int)sizeof(bf16);
+    wbase[ks] = swz(wrow[0] + lrow, chunk) * (int)sizeof(bf16);
     abase[ks] = swz(arow0 + lrow, chunk) * (int)sizeof(bf16);
   }
 
@@ -294,28 +442,30 @@ __global__ __launch_bounds__(NW * kWave, 1) void ffn_gemm_bf16_kernel(
   // step ks.
   bf16x8 wf[2][G::kTW], af[2][G::kTM];
   constexpr int kFrags = G::kTW + G::kTM;  // LDS reads per step
-  auto read_frag = [&](int stage, int wslot, int ks, int buf, int r) __attribute__((always_inline)) {
+  auto read_frag = [&](int aoff, int woff, int ks, int buf, int r) __attribute__((always_inline)) {
     if (r < G::kTW)
       wf[buf][r] = *reinterpret_cast<const bf16x8*>(
-          lds_bytes + wslot * G::kWSlotBytes + wbase[ks] + (wrow[r] - wrow[0]) * kRowBytes);
+          lds_bytes + woff + wbase[ks] + (wrow[r] - wrow[0]) * kRowBytes);
     else
       af[buf][r - G::kTW] = *reinterpret_cast<const bf16x8*>(
-          lds_bytes + stage * G::kAStageBytes + abase[ks] + (r - G::kTW) * 32 * kRowBytes);
+          lds_bytes + aoff + abase[ks] + (r - G::kTW) * 32 * kRowBytes);
   };
   // MFMAs of weight tiles [I0, I1) on operand buffer `buf`, for the first
-  // JN token subtiles.  If kReads, the kFrags operand reads of (stage,
-  // wslot, ks) into buffer rbuf are spread evenly between them, and so are
-  // the activation loads [A0, A1) and the weight loads [W0, W1) of later
-  // tiles.  A scheduling fence after every MFMA slot keeps this exact order:
-  // left alone, the compiler sinks each read next to its first use and
-  // bunches the loads, leaving the matrix cores idle meanwhile.
+  // JN token subtiles.  If kReads, the operand reads of reduction step ks
+  // from the ring slots at byte offsets (aoff, woff) into buffer rbuf are
+  // spread evenly between them (reads of subtiles that are skipped are left
+  // out), and so are the activation loads [A0, A1) into the slot at aoff_ld
+  // and the weight loads [W0, W1) into the slot at woff_ld of later tiles.
+  // A scheduling fence after every MFMA slot keeps this exact order: left
+  // alone, the compiler sinks each read next to its first use and bunches
+  // the loads, leaving the matrix cores idle meanwhile.
   auto mfma_step = [&](auto jn_c, auto i0_c, auto i1_c, auto reads_c, auto a0_c, auto a1_c,
-                       auto w0_c, auto w1_c, int buf, int stage, int wslot, int ks, int rbuf,
-                       int astage, int ak0, int wslot_ld, int wk0) __attribute__((always_inline)) {
+                       auto w0_c, auto w1_c, int buf, int aoff, int woff, int ks, int rbuf,
+                       int aoff_ld, int ak0, int woff_ld, int wk0) __attribute__((always_inline)) {
     constexpr int JN = decltype(jn_c)::value;
     constexpr int I0 = decltype(i0_c)::value;
     constexpr int I1 = decltype(i1_c)::value;
-    constexpr bool kReads = decltype(reads_c)::value;
+    constexpr bool kReads = decltype(reads_c)::value && JN > 0;
     constexpr int A0 = decltype(a0_c)::value, A1 = decltype(a1_c)::value;
     constexpr int W0 = decltype(w0_c)::value, W1 = decltype(w1_c)::value;
     constexpr int n = (I1 - I0) * G::kTM;
@@ -324,15 +474,15 @@ __global__ __launch_bounds__(NW * kWave, 1) void ffn_gemm_bf16_kernel(
 #pragma unroll
       for (int l = A0 + (m * (A1 - A0) + n - 1) / n; l < A0 + ((m + 1) * (A1 - A0) + n - 1) / n;
            ++l)
-        issue_aload(astage, ak0, l);
+        issue_aload(aoff_ld, ak0, l);
 #pragma unroll
       for (int l = W0 + (m * (W1 - W0) + n - 1) / n; l < W0 + ((m + 1) * (W1 - W0) + n - 1) / n;
            ++l)
-        issue_wload(wslot_ld, wk0, l);
+        issue_wload(woff_ld, wk0, l);
       if (kReads) {
 #pragma unroll
         for (int r = (m * kFrags + n - 1) / n; r < ((m + 1) * kFrags + n - 1) / n; ++r)
-          read_frag(stage, wslot, ks, rbuf, r);
+          if (r < G::kTW + JN) read_frag(aoff, woff, ks, rbuf, r);
       }
       const int i = I0 + m / G::kTM;
       const int j = m % G::kTM;
@@ -343,12 +493,20 @@ __global__ __launch_bounds__(NW * kWave, 1) void ffn_gemm_bf16_kernel(
     }
   };
   using IC0 = std::integral_constant<int, 0>;
+  using IC1 = std::integral_constant<int, 1>;
   using ICH = std::integral_constant<int, G::kTW / 2>;
   using ICW = std::integral_constant<int, G::kTW>;
   using AA = std::integral_constant<int, G::kALoads>;
   using WA = std::integral_constant<int, G::kWLoads>;
   using YES = std::true_type;
   using NO = std::false_type;
+  auto wslot_off = [](int u) __attribute__((always_inline)) {
+    return G::kWRegion + u * G::kWSlotBytes;
+  };
+  auto fence_free_barrier = []() __attribute__((always_inline)) {
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
 
   // One reduction tile kt: activations on LDS stage S = kt % 2, weights in
   // slot u = kt % 3 of a three-slot ring.  Step 0 loads tile kt + 1's
@@ -366,45 +524,30 @@ __global__ __launch_bounds__(NW * kWave, 1) void ffn_gemm_bf16_kernel(
   // reads again) and the trailing reads go unused.
   static_assert(kBK / 16 == 4, "four reduction steps per tile");
   static_assert(G::kWLoads == 8 || G::kWLoads == 4, "vmcnt immediate");
-  const int nk = Kdim / kBK;
+  const int nk = unit.ke - unit.kb;  // reduction tiles of this unit
   auto tile_step = [&](auto jn_c, auto stage_c, int kt, int u) __attribute__((always_inline)) {
     constexpr int S = decltype(stage_c)::value;
+    constexpr int ao = S * G::kAStageBytes, ao1 = (1 - S) * G::kAStageBytes;
     const int ak0 = min(kt + 1, nk - 1) * kBK;
     const int wk0 = min(kt + 2, nk - 1) * kBK;
-    const int u1 = u == 2 ? 0 : u + 1;
-    const int u2 = u == 0 ? 2 : u - 1;
-    mfma_step(jn_c, IC0{}, ICW{}, YES{}, IC0{}, AA{}, IC0{}, IC0{}, 0, S, u, 1, 1, 1 - S, ak0, 0, 0);
-    mfma_step(jn_c, IC0{}, ICW{}, YES{}, IC0{}, IC0{}, IC0{}, WA{}, 1, S, u, 2, 0, 0, 0, u2, wk0);
-    mfma_step(jn_c, IC0{}, ICW{}, YES{}, IC0{}, IC0{}, IC0{}, IC0{}, 0, S, u, 3, 1, 0, 0, 0, 0);
+    const int wo = wslot_off(u);
+    const int wo1 = wslot_off(u == 2 ? 0 : u + 1);
+    const int wo2 = wslot_off(u == 0 ? 2 : u - 1);
+    mfma_step(jn_c, IC0{}, ICW{}, YES{}, IC0{}, AA{}, IC0{}, IC0{}, 0, ao, wo, 1, 1, ao1, ak0, 0, 0);
+    mfma_step(jn_c, IC0{}, ICW{}, YES{}, IC0{}, IC0{}, IC0{}, WA{}, 1, ao, wo, 2, 0, 0, 0, wo2, wk0);
+    mfma_step(jn_c, IC0{}, ICW{}, YES{}, IC0{}, IC0{}, IC0{}, IC0{}, 0, ao, wo, 3, 1, 0, 0, 0, 0);
     mfma_step(jn_c, IC0{}, ICH{}, NO{}, IC0{}, IC0{}, IC0{}, IC0{}, 1, 0, 0, 0, 0, 0, 0, 0, 0);
     if constexpr (G::kWLoads == 8)
       asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
     else
       asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    mfma_step(jn_c, ICH{}, ICW{}, YES{}, IC0{}, IC0{}, IC0{}, IC0{}, 1, 1 - S, u1, 0, 0, 0, 0, 0,
+    fence_free_barrier();
+    mfma_step(jn_c, ICH{}, ICW{}, YES{}, IC0{}, IC0{}, IC0{}, IC0{}, 1, ao1, wo1, 0, 0, 0, 0, 0,
               0);
   };
   using St0 = std::integral_constant<int, 0>;
   using St1 = std::integral_constant<int, 1>;
 
-  // prologue: weights of tile 0, activations of tile 0, weights of tile 1;
-  // wait for the first two
-#pragma unroll
-  for (int l = 0; l < G::kWLoads; ++l) issue_wload(0, 0, l);
-#pragma unroll
-  for (int l = 0; l < G::kALoads; ++l) issue_aload(0, 0, l);
-#pragma unroll
-  for (int l = 0; l < G::kWLoads; ++l) issue_wload(1, min(1, nk - 1) * kBK, l);
-  if constexpr (G::kWLoads == 8)
-    asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-  else
-    asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-#pragma unroll
-  for (int r = 0; r < kFrags; ++r) read_frag(0, 0, 0, 0, r);
   // Tiles in pairs (stage 0, stage 1); an odd count starts with one tile
   // on stage 0 and pairs (stage 1, stage 0) after it.  JN is the number of
   // this wave's 32-token subtiles that are multiplied: a ragged last tile of
@@ -412,6 +555,23 @@ __global__ __launch_bounds__(NW * kWave, 1) void ffn_gemm_bf16_kernel(
   // variants that skip them (a run-time test per MFMA would force the
   // accumulators out of registers).
   auto main_loop = [&](auto jn_c) __attribute__((always_inline)) {
+    // prologue: weights of tile 0, activations of tile 0, weights of tile
+    // 1; wait for the first two
+#pragma unroll
+    for (int l = 0; l < G::kWLoads; ++l) issue_wload(wslot_off(0), 0, l);
+#pragma unroll
+    for (int l = 0; l < G::kALoads; ++l) issue_aload(0, 0, l);
+#pragma unroll
+    for (int l = 0; l < G::kWLoads; ++l) issue_wload(wslot_off(1), min(1, nk - 1) * kBK, l);
+    if constexpr (G::kWLoads == 8)
+      asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+    fence_free_barrier();
+    constexpr int JN = decltype(jn_c)::value;
+#pragma unroll
+    for (int r = 0; r < kFrags; ++r)
+      if (JN > 0 && r < G::kTW + JN) read_frag(0, wslot_off(0), 0, 0, r);
     int u = 0;  // weight slot of the current tile, kt % 3
     auto next = [](int v) { return v == 2 ? 0 : v + 1; };
     if (nk & 1) {
@@ -432,15 +592,126 @@ __global__ __launch_bounds__(NW * kWave, 1) void ffn_gemm_bf16_kernel(
       }
     }
   };
+
+  // Thin tiles: reduction tile kt has both operands in slot u = kt % 4 of
+  // four-slot rings.  Steps 0 and 1 load tile kt + 3's activations and
+  // weights into slot (u + 3) % 4, last read by tile kt - 1; halfway through
+  // the last step the wave waits until only the loads of tiles kt + 2 and
+  // kt + 3 may be outstanding, then meets the others at the barrier, as
+  // above.
+  auto thin_step = [&](auto jn_c, int kt, int u) __attribute__((always_inline)) {
+    const int k3 = min(kt + 3, nk - 1) * kBK;
+    const int ao = u * G::kThinABytes, wo = G::kThinWRegion + u * G::kWSlotBytes;
+    const int u1 = (u + 1) & 3, u3 = (u + 3) & 3;
+    const int ao3 = u3 * G::kThinABytes, wo3 = G::kThinWRegion + u3 * G::kWSlotBytes;
+    mfma_step(jn_c, IC0{}, ICW{}, YES{}, IC0{}, IC1{}, IC0{}, IC0{}, 0, ao, wo, 1, 1, ao3, k3, 0, 0);
+    mfma_step(jn_c, IC0{}, ICW{}, YES{}, IC0{}, IC0{}, IC0{}, WA{}, 1, ao, wo, 2, 0, 0, 0, wo3, k3);
+    mfma_step(jn_c, IC0{}, ICW{}, YES{}, IC0{}, IC0{}, IC0{}, IC0{}, 0, ao, wo, 3, 1, 0, 0, 0, 0);
+    mfma_step(jn_c, IC0{}, ICH{}, NO{}, IC0{}, IC0{}, IC0{}, IC0{}, 1, 0, 0, 0, 0, 0, 0, 0, 0);
+    asm volatile("s_waitcnt vmcnt(18)" ::: "memory");  // 2 tiles x (1 + 8) loads
+    fence_free_barrier();
+    mfma_step(jn_c, ICH{}, ICW{}, YES{}, IC0{}, IC0{}, IC0{}, IC0{}, 1, u1 * G::kThinABytes,
+              G::kThinWRegion + u1 * G::kWSlotBytes, 0, 0, 0, 0, 0, 0);
+  };
+  auto thin_loop = [&](auto jn_c) __attribute__((always_inline)) {
+    static_assert(G::kWLoads == 8, "vmcnt immediate");
+    // prologue: tiles 0, 1 and 2 (activations, then weights); wait for tile 0
+#pragma unroll
+    for (int t = 0; t < 3; ++t) {
+      const int k0 = min(t, nk - 1) * kBK;
+      issue_aload(t * G::kThinABytes, k0, 0);
+#pragma unroll
+      for (int l = 0; l < G::kWLoads; ++l)
+        issue_wload(G::kThinWRegion + t * G::kWSlotBytes, k0, l);
+    }
+    asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
+    fence_free_barrier();
+    constexpr int JN = decltype(jn_c)::value;
+#pragma unroll
+    for (int r = 0; r < kFrags; ++r)
+      if (JN > 0 && r < G::kTW + JN) read_frag(0, G::kThinWRegion, 0, 0, r);
+    for (int kt = 0; kt < nk; ++kt) thin_step(jn_c, kt, kt & 3);
+  };
+
   constexpr int kTM = G::kTM;
-  if (jlim >= kTM || (kTM > 2 && jlim > 2))
-    main_loop(std::integral_constant<int, kTM>{});
-  else if (kTM > 2 && jlim == 2)
-    main_loop(std::integral_constant<int, (kTM > 2 ? 2 : kTM)>{});
-  else if (kTM > 1 && jlim == 1)
-    main_loop(std::integral_constant<int, (kTM > 1 ? 1 : kTM)>{});
-  else
-    main_loop(std::integral_constant<int, 0>{});
+  if constexpr (G::kThin) {
+    if (rows <= 32) {
+      // only the first 32-token subtile of wave row 0 holds rows
+      if (jlim >= 1)
+        thin_loop(IC1{});
+      else
+        thin_loop(IC0{});
+    } else if constexpr (kTM > 1) {
+      if (jlim >= kTM || (kTM > 2 && jlim > 2))
+        main_loop(std::integral_constant<int, kTM>{});
+      else if (kTM > 2 && jlim == 2)
+        main_loop(std::integral_constant<int, (kTM > 2 ? 2 : kTM)>{});
+      else if (jlim == 1)
+        main_loop(IC1{});
+      else
+        main_loop(IC0{});
+    }
+  } else {
+    if (jlim >= kTM || (kTM > 2 && jlim > 2))
+      main_loop(std::integral_constant<int, kTM>{});
+    else if (kTM > 2 && jlim == 2)
+      main_loop(std::integral_constant<int, (kTM > 2 ? 2 : kTM)>{});
+    else if (kTM > 1 && jlim == 1)
+      main_loop(std::integral_constant<int, (kTM > 1 ? 1 : kTM)>{});
+    else
+      main_loop(IC0{});
+  }
+
+  // A piece of a split tile.  Its accumulators go to its workspace slot in
+  // register order (lane-contiguous 64-byte runs); every thread makes its
+  // stores visible device-wide (other XCDs' L2s included) before the block
+  // counts itself in, so the piece that arrives last sees every piece, adds
+  // them in piece order into its accumulators, re-arms the counter for the
+  // next launch and goes on to the ordinary epilogue.  No block waits on
+  // another.
+  if (unit.parts > 1) {
+    constexpr int kUnitFloats = NW * G::kTW * G::kTM * kWave * 16;
+    float* const base = partial + (size_t)unit.pslot0 * kUnitFloats +
+                        (size_t)wave * (G::kTW * G::kTM * kWave * 16) + lane * 16;
+    float* const mine = base + (size_t)unit.piece * kUnitFloats;
+#pragma unroll
+    for (int i = 0; i < G::kTW; ++i)
+#pragma unroll
+      for (int j = 0; j < G::kTM; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          f32x4 v;
+#pragma unroll
+          for (int c = 0; c < 4; ++c) v[c] = acc[i][j][q * 4 + c];
+          *reinterpret_cast<f32x4*>(mine + (i * G::kTM + j) * kWave * 16 + q * 4) = v;
+        }
+    __threadfence();
+    __syncthreads();  // also: every wave is done reading operand LDS
+    int* const flag = reinterpret_cast<int*>(lds);
+    if (threadIdx.x == 0) *flag = atomicAdd(&split_cnt[unit.split], 1);
+    __syncthreads();
+    if (*flag != unit.parts - 1) return;
+    __threadfence();
+#pragma unroll
+    for (int i = 0; i < G::kTW; ++i)
+#pragma unroll
+      for (int j = 0; j < G::kTM; ++j) {
+        f32x16 sum;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sum[r] = 0.0f;
+        for (int p = 0; p < unit.parts; ++p) {
+          const float* src = base + (size_t)p * kUnitFloats + (i * G::kTM + j) * kWave * 16;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const f32x4 v = *reinterpret_cast<const f32x4*>(src + q * 4);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) sum[q * 4 + c] += v[c];
+          }
+        }
+        acc[i][j] = sum;
+      }
+    if (threadIdx.x == 0) split_cnt[unit.split] = 0;
+  }
 
   // Epilogue.  Accumulator register r of lane l holds weight row
   // (r / 4) * 8 + (l / 32) * 4 + r % 4 of its 32-row weight tile and token
@@ -563,6 +834,24 @@ __global__ __launch_bounds__(kThreads) void ffn_gemm_f32_kernel(
   }
 }
 
+// Blocks of a bf16 GEMM resident at once on the current device: one per CU
+// (the kernels take all of a CU's LDS), capped at kMaxSplitUnits.  Cached per
+// device.
+int resident_blocks() {
+  constexpr int kMaxDevices = 64;
+  static int cache[kMaxDevices] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return kMaxSplitUnits;
+  if (dev < kMaxDevices && cache[dev] > 0) return cache[dev];
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0)
+    cus = kMaxSplitUnits;
+  cus = cus < kMaxSplitUnits ? cus : kMaxSplitUnits;
+  if (dev < kMaxDevices) cache[dev] = cus;
+  return cus;
+}
+
 template <int BM, int WM, int NW, bool kDual>
 hipError_t launch_bf16_gemm(const bf16* act, int Kdim, const bf16* w0,
                             const bf16* w1, int Nout, bf16* out,
@@ -579,11 +868,15 @@ hipError_t launch_bf16_gemm(const bf16* act, int Kdim, const bf16* w0,
   if (attr != hipSuccess) return attr;
   constexpr int kNOut = kDual ? kBW / 2 : kBW;
   const int n_tiles = (Nout + kNOut - 1) / kNOut;
-  const long long blocks = (long long)n_tiles * max_tiles;
-  const int grid = (int)((blocks + 7) / 8 * 8);
+  // an XCD's list holds at most max_tiles x ceil(n_tiles / 8) whole tiles,
+  // and its split pieces take at most cps more blocks
+  const int cps = resident_blocks() / kXcds > 0 ? resident_blocks() / kXcds : 1;
+  const long long per_xcd = (long long)max_tiles * ((n_tiles + kXcds - 1) / kXcds) + cps;
+  const int grid = (int)(per_xcd * kXcds);
+  const int* xcd_start = ws.xcd_start + (kDual ? 0 : kXcds * (E + 1));
   ffn_gemm_bf16_kernel<BM, WM, NW, kDual><<<grid, NW * kWave, G::kLds, stream>>>(
-      act, Kdim, w0, w1, Nout, out, ws.tiles, ws.tile_start, ws.num_tiles, E,
-      n_tiles);
+      act, Kdim, w0, w1, Nout, out, ws.tiles, ws.tile_start, xcd_start, E, n_tiles,
+      cps, ws.partial, ws.split_cnt + (kDual ? 0 : kMaxSplitUnits));
   return hipGetLastError();
 }
 
@@ -617,10 +910,13 @@ int bf16_tile_rows(int64_t max_rows, int E) {
 }  // namespace
 
 size_t grouped_ffn_workspace_bytes(int64_t max_rows, int E, bool bf16_data) {
-  // sized for the smallest row tile, so it covers every tile choice
+  // the tile table is sized for the smallest row tile, so it covers every
+  // tile choice; split partials hold kMaxSplitUnits fp32 tiles of BM x 256
   const int tr = bf16_data ? 32 : kF32TileRows;
-  return 256 + align_up((size_t)(E + 1) * sizeof(int), 256) +
-         (size_t)max_tiles_for(max_rows, E, tr) * sizeof(int4);
+  const size_t table = ffn_tiles_offset(E) +
+                       align_up((size_t)max_tiles_for(max_rows, E, tr) * sizeof(int4), 256);
+  if (!bf16_data) return table;
+  return table + (size_t)kMaxSplitUnits * bf16_tile_rows(max_rows, E) * kBW * sizeof(float);
 }
 
 hipError_t launch_grouped_ffn(const void* x_perm, bool bf16_data, int d,
@@ -632,10 +928,13 @@ hipError_t launch_grouped_ffn(const void* x_perm, bool bf16_data, int d,
   if (max_rows == 0) return hipSuccess;
   const int tr = bf16_data ? bf16_tile_rows(max_rows, E) : kF32TileRows;
   const int max_tiles = max_tiles_for(max_rows, E, tr);
-  const FfnWorkspace ws = ffn_workspace(workspace, E);
-  ffn_schedule_kernel<<<1, 1024, 0, stream>>>(offsets, E, tr, (int)max_rows,
-                                              max_tiles, ws.tiles,
-                                              ws.tile_start, ws.num_tiles);
+  const FfnWorkspace ws = ffn_workspace(workspace, E, max_tiles);
+  // column tiles of the bf16 passes (the XCD tables serve only those)
+  const int n_up = (ffn + kBW / 2 - 1) / (kBW / 2);
+  const int n_dn = (d + kBW - 1) / kBW;
+  ffn_schedule_kernel<<<1, 1024, 0, stream>>>(offsets, E, tr, (int)max_rows, max_tiles,
+                                              n_up, n_dn, ws.tiles, ws.tile_start,
+                                              ws.num_tiles, ws.split_cnt, ws.xcd_start);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
 
@@ -649,20 +948,20 @@ hipError_t launch_grouped_ffn(const void* x_perm, bool bf16_data, int d,
     return launch_bf16_ffn<32, 1, 4>(x_perm, d, ffn, E, w_gate, w_up, w_down, h,
                                   y_perm, ws, max_tiles, stream);
   }
-  const int n_up = (ffn + kFN - 1) / kFN;
-  const int g_up = (int)(((long long)n_up * max_tiles + 7) / 8 * 8);
+  const int f_up = (ffn + kFN - 1) / kFN;
+  const int g_up = (int)(((long long)f_up * max_tiles + 7) / 8 * 8);
   ffn_gemm_f32_kernel<true><<<g_up, kThreads, 0, stream>>>(
       static_cast<const float*>(x_perm), d, static_cast<const float*>(w_gate),
       static_cast<const float*>(w_up), ffn, static_cast<float*>(h), ws.tiles,
-      ws.tile_start, ws.num_tiles, E, n_up);
+      ws.tile_start, ws.num_tiles, E, f_up);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
-  const int n_dn = (d + kFN - 1) / kFN;
-  const int g_dn = (int)(((long long)n_dn * max_tiles + 7) / 8 * 8);
+  const int f_dn = (d + kFN - 1) / kFN;
+  const int g_dn = (int)(((long long)f_dn * max_tiles + 7) / 8 * 8);
   ffn_gemm_f32_kernel<false><<<g_dn, kThreads, 0, stream>>>(
       static_cast<const float*>(h), ffn, static_cast<const float*>(w_down),
       nullptr, d, static_cast<float*>(y_perm), ws.tiles, ws.tile_start,
-      ws.num_tiles, E, n_dn);
+      ws.num_tiles, E, f_dn);
   return hipGetLastError();
 }
 
