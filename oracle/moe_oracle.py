@@ -31,6 +31,18 @@ stage list is "Gate -> dispatch -> Expert FFN -> combine -> Aggregation" in
             y = h Wd^T (SwiGLU, no biases).
   combine   out[t] = sum over kept slots k (ascending) of w[t,k] * y[row(t,k)].
 
+Routing variants (section 2.3 of "MoE 推理服务工程真相 2026" names sigmoid
+routing as a balance remedy and re-maps overflowing expert ids in its
+dispatch pseudocode; its section 4.3 sends an over-capacity token to a
+next-best expert instead of dropping it):
+
+  gate      "sigmoid": the gate score of expert e is 1 / (1 + exp(-l_e))
+            instead of the softmax probability; the top-K choice is the same
+            (both scores rise with the logit).
+  reroute   one round of re-routing after the capacity check: a token's
+            j-th overflowing slot is offered its (K + j)-th best expert and
+            takes it if that expert still has room, in token order.
+
 Where the pages say nothing (the gate function, the tie-break, the order
 inside an expert, the capacity formula, the FFN form) the oracle takes the
 plain reading: fp32-input softmax, lowest index wins ties, ascending token
@@ -57,7 +69,9 @@ __all__ = [
     "round_bf16",
     "round_storage",
     "capacity",
+    "gate_scores",
     "route",
+    "reroute_overflow",
     "dispatch",
     "pack",
     "silu",
@@ -177,7 +191,25 @@ def router_logits_error_bound(x, w_router):
 # route
 # --------------------------------------------------------------------------
 
-def route(logits, K, renormalize=False):
+def gate_scores(logits, gate="softmax"):
+    """Gate score of every expert for every token, float64 [N, E].
+
+    "softmax": exp(l_e - max) / sum_e' exp(l_e' - max), the default gate.
+    "sigmoid": 1 / (1 + exp(-l_e)), the sigmoid routing that "MoE 推理服务工程
+    真相 2026", section 2.3, names as a remedy for router-level imbalance;
+    each expert's score is independent of the others'.
+    """
+    l = np.asarray(logits, dtype=np.float32).astype(np.float64)
+    if gate == "softmax":
+        m = l.max(axis=1, keepdims=True)
+        ex = np.exp(l - m)
+        return ex / ex.sum(axis=1, keepdims=True)
+    if gate == "sigmoid":
+        return 1.0 / (1.0 + np.exp(-l))
+    raise ValueError("gate must be 'softmax' or 'sigmoid'")
+
+
+def route(logits, K, renormalize=False, gate="softmax"):
     """Top-K routing of every token.
 
     "MoE 专家并行的 All-to-All 通信瓶颈", section "一个反直觉的扩容结果": the
@@ -187,8 +219,10 @@ def route(logits, K, renormalize=False):
     logits: float32 [N, E] (finite).  Returns (topk_idx int32 [N, K],
     topk_w float32 [N, K]).  Slot 0 is the best expert.  A larger logit wins;
     equal logits go to the lower expert index.  The weight of slot k is the
-    softmax probability of its expert over all E logits (max-subtracted,
-    float64), optionally divided by the sum of the K selected probabilities.
+    gate score of its expert (gate_scores: the softmax probability over all E
+    logits, or the sigmoid of its logit), optionally divided by the sum of
+    the K selected scores.  Both gates rise with the logit, so the choice is
+    the same for either.
     """
     l32 = np.asarray(logits, dtype=np.float32)
     N, E = l32.shape
@@ -196,10 +230,7 @@ def route(logits, K, renormalize=False):
         raise ValueError("need 1 <= K <= E")
     if not np.all(np.isfinite(l32)):
         raise ValueError("logits must be finite")
-    l = l32.astype(np.float64)
-    m = l.max(axis=1, keepdims=True)
-    ex = np.exp(l - m)
-    p = ex / ex.sum(axis=1, keepdims=True)
+    p = gate_scores(l32, gate)
     # Stable sort on the negated fp32 logit: descending logit, and among
     # equal logits the original (ascending expert) order survives.
     order = np.argsort(-l32, axis=1, kind="stable")
@@ -208,6 +239,84 @@ def route(logits, K, renormalize=False):
     if renormalize:
         w = w / w.sum(axis=1, keepdims=True)
     return idx, w.astype(np.float32)
+
+
+def reroute_overflow(logits, topk_idx, cap, gate="softmax", renormalize=False):
+    """One round of token re-routing of capacity overflow.
+
+    "MoE 推理服务工程真相 2026", section 2.3: the dispatch pseudocode counts
+    each expert's tokens, compares them with the capacity and re-maps the
+    expert ids of the overflow before the all-to-all; section 4.3 ("Token
+    drop"): an over-capacity token is sent to a next-best expert rather than
+    losing that expert's output.  The pages fix neither which expert nor
+    what happens when it is full; the reading here:
+
+      1. Overflow: walk t = 0..N-1 and k = 0..K-1; slot (t, k) with expert
+         e = topk_idx[t, k] overflows iff cap >= 0 and e has already been
+         named by cap earlier slots (the same rule that drops it in
+         ``dispatch``).  kept1[e] = min(demand[e], cap).
+      2. Candidate: token t's j-th overflowing slot (j = 0, 1, .. in slot
+         order) is offered the expert at position K + j of the token's full
+         order (descending logit, ties to the lower index), i.e. its best
+         experts outside its own top K; there is none if K + j >= E.
+      3. Admission: walk the candidates in the same (t, k) order; expert c
+         admits a candidate while it has admitted fewer than cap - kept1[c],
+         so admitted slots only fill room the first pass left.
+      4. An admitted slot takes expert c and weight score(c) (gate_scores),
+         divided by the sum of the scores of the token's original K experts
+         if renormalize.  Every other slot is left as it was: a slot that
+         overflowed and was not admitted keeps its expert, and ``dispatch``
+         with the same cap drops it again.
+
+    With these rules ``dispatch(new_idx, E, W, cap)`` keeps exactly the
+    first-pass survivors plus the admitted slots (an expert that overflowed
+    has no room, and an expert with room had no overflow).
+
+    Returns (new_idx int32 [N, K], new_w float32 [N, K], rerouted int32 [E]:
+    admitted slots per expert).  topk_idx: int32 [N, K] as ``route`` gives.
+    """
+    l32 = np.asarray(logits, dtype=np.float32)
+    idx = np.asarray(topk_idx).astype(np.int64)
+    N, E = l32.shape
+    K = idx.shape[1]
+    p = gate_scores(l32, gate)
+    # original weights (as route computes them) for the slots left alone
+    w = np.take_along_axis(p, idx, axis=1)
+    norm = w.sum(axis=1) if renormalize else np.ones(N)
+    new_idx = idx.copy()
+    new_w = (w / norm[:, None]).astype(np.float32)
+    rerouted = np.zeros(E, dtype=np.int64)
+    if cap < 0:
+        return new_idx.astype(np.int32), new_w, rerouted.astype(np.int32)
+
+    # 1. overflow in token order
+    seen = [0] * E
+    over = [[False] * K for _ in range(N)]
+    for t in range(N):
+        for k in range(K):
+            e = int(idx[t, k])
+            over[t][k] = seen[e] >= cap
+            seen[e] += 1
+    room = [cap - min(seen[e], cap) for e in range(E)]
+
+    # 2 + 3. candidates and admission, in token order
+    order = np.argsort(-l32, axis=1, kind="stable")
+    for t in range(N):
+        j = 0
+        for k in range(K):
+            if not over[t][k]:
+                continue
+            pos = K + j
+            j += 1
+            if pos >= E:
+                continue
+            c = int(order[t, pos])
+            if room[c] > 0:
+                room[c] -= 1
+                rerouted[c] += 1
+                new_idx[t, k] = c
+                new_w[t, k] = np.float32(p[t, c] / norm[t])
+    return new_idx.astype(np.int32), new_w, rerouted.astype(np.int32)
 
 
 # --------------------------------------------------------------------------
@@ -380,16 +489,22 @@ def combine(y_perm, dest, topk_w, act):
 # the whole layer
 # --------------------------------------------------------------------------
 
-def layer(logits, x, expert_weights, K, W, cap, act, renormalize=False):
-    """Route, dispatch, FFN and combine; returns every intermediate."""
+def layer(logits, x, expert_weights, K, W, cap, act, renormalize=False, gate="softmax",
+          reroute=False):
+    """Route (optionally re-routing overflow), dispatch, FFN and combine;
+    returns every intermediate."""
     N, E = np.asarray(logits).shape
-    idx, w = route(logits, K, renormalize)
+    idx, w = route(logits, K, renormalize, gate)
+    rerouted = np.zeros(E, dtype=np.int32)
+    if reroute:
+        idx, w, rerouted = reroute_overflow(logits, idx, cap, gate, renormalize)
     disp = dispatch(idx, E, W, cap)
     x_perm = pack(x, disp["perm_token"])
     h, y = grouped_ffn(x_perm, disp["offsets"], expert_weights, act)
     out = combine(y, disp["dest"], w, act)
     res = dict(disp)
-    res.update(topk_idx=idx, topk_w=w, x_perm=x_perm, h=h, y_perm=y, out=out)
+    res.update(topk_idx=idx, topk_w=w, x_perm=x_perm, h=h, y_perm=y, out=out,
+               rerouted=rerouted)
     return res
 
 

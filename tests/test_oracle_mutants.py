@@ -6,15 +6,18 @@ import pytest
 
 from oracle import moe_oracle as O
 import test_oracle as P
+import test_oracle_reroute as PR
 
 _route = O.route
 _dispatch = O.dispatch
 _expert_ffn = O.expert_ffn
 _combine = O.combine
+_reroute = O.reroute_overflow
+_gate_scores = O.gate_scores
 
 
-def _route_tie_high(logits, K, renormalize=False):
-    idx, w = _route(logits, K, renormalize)
+def _route_tie_high(logits, K, renormalize=False, gate="softmax"):
+    idx, w = _route(logits, K, renormalize, gate)
     l = np.asarray(logits, np.float32)
     # ties broken toward the higher index
     order = np.argsort(-l[:, ::-1], axis=1, kind="stable")
@@ -24,8 +27,61 @@ def _route_tie_high(logits, K, renormalize=False):
     return idx2, np.take_along_axis(p, idx2.astype(np.int64), 1).astype(np.float32)
 
 
-def _route_renorm_always(logits, K, renormalize=False):
-    return _route(logits, K, True)
+def _route_renorm_always(logits, K, renormalize=False, gate="softmax"):
+    return _route(logits, K, True, gate)
+
+
+def _gate_sigmoid_sign(logits, gate="softmax"):
+    if gate == "sigmoid":
+        return 1.0 / (1.0 + np.exp(np.asarray(logits, np.float64)))
+    return _gate_scores(logits, gate)
+
+
+def _reroute_candidate_off_by_one(logits, topk_idx, cap, gate="softmax", renormalize=False):
+    # offers position K + j - 1: the token's own worst top-K expert first
+    l = np.asarray(logits, np.float32)
+    idx = np.asarray(topk_idx)
+    shifted = np.concatenate([idx[:, :-1], idx[:, -1:]], axis=1)
+    ni, nw, rr = _reroute(l, shifted, cap, gate, renormalize)
+    if cap >= 0 and idx.shape[1] < l.shape[1]:
+        order = np.argsort(-l, axis=1, kind="stable")
+        for t in range(l.shape[0]):
+            for k in range(idx.shape[1]):
+                if ni[t, k] != idx[t, k]:
+                    ni[t, k] = order[t, idx.shape[1] - 1]
+    return ni, nw, rr
+
+
+def _reroute_ignores_room(logits, topk_idx, cap, gate="softmax", renormalize=False):
+    # admits every candidate: the first pass's survivors are not counted
+    if cap <= 0:
+        return _reroute(logits, topk_idx, cap, gate, renormalize)
+    return _reroute_unbounded(logits, topk_idx, cap, gate, renormalize)
+
+
+def _reroute_unbounded(logits, topk_idx, cap, gate, renormalize):
+    l = np.asarray(logits, np.float32)
+    idx = np.asarray(topk_idx).astype(np.int64)
+    N, E = l.shape
+    K = idx.shape[1]
+    ni, nw, _ = _reroute(l, idx, -1, gate, renormalize)
+    rr = np.zeros(E, np.int64)
+    seen = [0] * E
+    order = np.argsort(-l, axis=1, kind="stable")
+    p = O.gate_scores(l, gate)
+    for t in range(N):
+        j = 0
+        for k in range(K):
+            e = int(idx[t, k])
+            if seen[e] >= cap and K + j < E:
+                c = int(order[t, K + j])
+                ni[t, k] = c
+                nw[t, k] = np.float32(p[t, c])
+                rr[c] += 1
+            if seen[e] >= cap:
+                j += 1
+            seen[e] += 1
+    return ni.astype(np.int32), nw, rr.astype(np.int32)
 
 
 def _dispatch_drop_earlier(topk_idx, E, W, cap):
@@ -70,6 +126,9 @@ MUTANTS = {
     "ffn_no_silu": ("expert_ffn", _ffn_no_silu),
     "combine_unweighted": ("combine", _combine_unweighted),
     "combine_includes_dropped": ("combine", _combine_includes_dropped),
+    "gate_sigmoid_sign": ("gate_scores", _gate_sigmoid_sign),
+    "reroute_candidate_off_by_one": ("reroute_overflow", _reroute_candidate_off_by_one),
+    "reroute_ignores_room": ("reroute_overflow", _reroute_ignores_room),
 }
 
 PINS = [
@@ -81,6 +140,12 @@ PINS = [
     lambda: P.test_single_expert_is_textbook_swiglu(),
     lambda: P.test_dispatch_then_combine_with_identity_ffn_is_identity(),
     lambda: P.test_hand_example(),
+    lambda: PR.test_sigmoid_scores_match_library(),
+    lambda: PR.test_sigmoid_route_special_cases(),
+    lambda: PR.test_reroute_hand_example(),
+    lambda: [PR.test_reroute_uniform_closed_form(*c) for c in ((10, 3, 2, 6), (12, 4, 3, 6))],
+    lambda: PR.test_reroute_is_a_no_op_without_overflow(),
+    lambda: [PR.test_reroute_against_brute_force(s) for s in range(4)],
 ]
 
 
