@@ -16,6 +16,8 @@ from .binding import (  # noqa: F401
     moe_exchange_workspace_bytes,
     moe_grouped_ffn,
     moe_grouped_ffn_workspace_bytes,
+    moe_reroute_overflow,
+    moe_reroute_workspace_bytes,
     moe_route_topk,
     moe_router_logits,
     moe_rows_permute,

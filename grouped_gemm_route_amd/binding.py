@@ -17,6 +17,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_rout
 
 MOE_OK = 0
 DTYPE_CODE = {torch.float32: 0, torch.bfloat16: 1}
+GATE_CODE = {"softmax": 0, "sigmoid": 1}
 
 # (name, restype, argtypes) of every exported function in include/moe_route.h
 _P = ctypes.c_void_p
@@ -29,6 +30,10 @@ SIGNATURES = [
     ("moe_last_error", ctypes.c_char_p, []),
     ("moe_capacity", _I64, [ctypes.c_double, _I64, _I32, _I32]),
     ("moe_route_topk", ctypes.c_int, [_P, _I32, _I32, _I32, _I32, _P, _P, _P]),
+    ("moe_route_topk_gated", ctypes.c_int, [_P, _I32, _I32, _I32, _I32, _I32, _P, _P, _P]),
+    ("moe_reroute_workspace_bytes", _SZ, [_I32, _I32, _I32]),
+    ("moe_reroute_overflow", ctypes.c_int,
+     [_P, _I32, _I32, _I32, _I32, _I32, _I64, _P, _P, _P, _P, _SZ, _P]),
     ("moe_dispatch_workspace_bytes", _SZ, [_I32, _I32, _I32]),
     ("moe_dispatch", ctypes.c_int,
      [_P, _I32, _I32, _I32, _P, _I32, _I32, _I32, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
@@ -125,8 +130,15 @@ def moe_capacity(C, N, K, E):
     return int(v)
 
 
-def moe_route_topk(logits, K, renormalize=False, topk_idx=None, topk_w=None):
-    """Top-K routing: returns (topk_idx int32 [N,K], topk_w fp32 [N,K])."""
+def _gate(gate):
+    if gate not in GATE_CODE:
+        raise ValueError(f"gate must be one of {sorted(GATE_CODE)}")
+    return GATE_CODE[gate]
+
+
+def moe_route_topk(logits, K, renormalize=False, topk_idx=None, topk_w=None, gate="softmax"):
+    """Top-K routing: returns (topk_idx int32 [N,K], topk_w fp32 [N,K]).
+    gate "softmax" calls moe_route_topk, "sigmoid" moe_route_topk_gated."""
     _need(logits, "logits", torch.float32)
     N, E = logits.shape
     dev = logits.device
@@ -138,10 +150,47 @@ def moe_route_topk(logits, K, renormalize=False, topk_idx=None, topk_w=None):
     _need(topk_w, "topk_w", torch.float32, dev)
     if topk_idx.numel() != N * K or topk_w.numel() != N * K:
         raise ValueError("topk_idx/topk_w must hold N*K elements")
-    _check("moe_route_topk", load_library().moe_route_topk(
-        _ptr(logits), N, E, K, int(bool(renormalize)), _ptr(topk_idx), _ptr(topk_w),
-        _stream(logits)))
+    if gate == "softmax":
+        _check("moe_route_topk", load_library().moe_route_topk(
+            _ptr(logits), N, E, K, int(bool(renormalize)), _ptr(topk_idx), _ptr(topk_w),
+            _stream(logits)))
+    else:
+        _check("moe_route_topk_gated", load_library().moe_route_topk_gated(
+            _ptr(logits), N, E, K, _gate(gate), int(bool(renormalize)), _ptr(topk_idx),
+            _ptr(topk_w), _stream(logits)))
     return topk_idx, topk_w
+
+
+def moe_reroute_workspace_bytes(N, E, K):
+    return int(load_library().moe_reroute_workspace_bytes(N, E, K))
+
+
+def moe_reroute_overflow(logits, topk_idx, topk_w, capacity, gate="softmax", renormalize=False,
+                         rerouted=None, workspace=None):
+    """Re-route capacity overflow to next-best experts, updating topk_idx and
+    topk_w in place; returns rerouted int32 [E] (admitted slots per expert)."""
+    _need(logits, "logits", torch.float32)
+    N, E = logits.shape
+    dev = logits.device
+    _need(topk_idx, "topk_idx", torch.int32, dev)
+    _need(topk_w, "topk_w", torch.float32, dev)
+    K = topk_idx.shape[1]
+    if tuple(topk_idx.shape) != (N, K) or tuple(topk_w.shape) != (N, K):
+        raise ValueError("topk_idx / topk_w must be [N, K]")
+    if rerouted is None:
+        rerouted = torch.empty(E, dtype=torch.int32, device=dev)
+    _need(rerouted, "rerouted", torch.int32, dev)
+    if rerouted.numel() < E:
+        raise ValueError("rerouted must hold E elements")
+    if workspace is None:
+        workspace = torch.empty(max(1, moe_reroute_workspace_bytes(N, E, K)),
+                                dtype=torch.uint8, device=dev)
+    _need(workspace, "workspace", None, dev)
+    _check("moe_reroute_overflow", load_library().moe_reroute_overflow(
+        _ptr(logits), N, E, K, _gate(gate), int(bool(renormalize)), int(capacity),
+        _ptr(topk_idx), _ptr(topk_w), _ptr(rerouted), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(logits)))
+    return rerouted
 
 
 def moe_router_logits(x, w_router, logits=None):
@@ -346,13 +395,19 @@ class MoeLayer:
 
     Buffers are sized once for (N, d, ffn, E, K, W, dtype); ``forward`` then
     enqueues route -> dispatch -> grouped FFN -> combine on the current
-    stream with no host synchronisation and no allocation.
+    stream with no host synchronisation and no allocation.  gate picks the
+    router's gate function; reroute=True re-routes capacity overflow to
+    next-best experts between route and dispatch.
     """
 
-    def __init__(self, N, d, ffn, E, K, W, capacity, dtype, device, renormalize=False):
+    def __init__(self, N, d, ffn, E, K, W, capacity, dtype, device, renormalize=False,
+                 gate="softmax", reroute=False):
         self.N, self.d, self.ffn_dim, self.E, self.K, self.W = N, d, ffn, E, K, W
         self.capacity = int(capacity)
         self.renormalize = renormalize
+        self.gate = gate
+        _gate(gate)
+        self.reroute = reroute
         self.max_rows = N * K
         dev = torch.device(device)
         self.topk_idx = torch.empty(N, K, dtype=torch.int32, device=dev)
@@ -363,9 +418,16 @@ class MoeLayer:
         self.ffn_ws = torch.empty(max(1, moe_grouped_ffn_workspace_bytes(self.max_rows, E, dtype)),
                                   dtype=torch.uint8, device=dev)
         self.out = torch.empty(N, d, dtype=dtype, device=dev)
+        self.rerouted = torch.zeros(E, dtype=torch.int32, device=dev)
+        self.reroute_ws = (torch.empty(max(1, moe_reroute_workspace_bytes(N, E, K)),
+                                       dtype=torch.uint8, device=dev) if reroute else None)
 
     def route(self, logits):
-        return moe_route_topk(logits, self.K, self.renormalize, self.topk_idx, self.topk_w)
+        moe_route_topk(logits, self.K, self.renormalize, self.topk_idx, self.topk_w, self.gate)
+        if self.reroute:
+            moe_reroute_overflow(logits, self.topk_idx, self.topk_w, self.capacity, self.gate,
+                                 self.renormalize, self.rerouted, self.reroute_ws)
+        return self.topk_idx, self.topk_w
 
     def dispatch(self, x):
         return moe_dispatch(x, self.topk_idx, self.E, self.W, self.capacity, self.disp)

@@ -93,20 +93,65 @@ int64_t moe_capacity(double C, int64_t N, int32_t K, int32_t E) {
   return (int64_t)q;
 }
 
+namespace {
+
+int route_checks(const char* fn, const float* logits, int32_t N, int32_t E, int32_t K,
+                 const void* a, const void* b) {
+  if (!logits || !a || !b) return fail(MOE_ERR_INVALID_ARG, "%s: null pointer", fn);
+  if (N < 0 || E < 1 || K < 1 || K > E)
+    return fail(MOE_ERR_INVALID_ARG, "%s: need N >= 0 and 1 <= K <= E (N=%d E=%d K=%d)", fn,
+                N, E, K);
+  if (E > MOE_MAX_EXPERTS || K > MOE_MAX_TOPK)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: E <= %d and K <= %d supported", fn, MOE_MAX_EXPERTS,
+                MOE_MAX_TOPK);
+  if ((int64_t)N * E >= ((int64_t)1 << 31) * 4 || (int64_t)N * K >= ((int64_t)1 << 31))
+    return fail(MOE_ERR_UNSUPPORTED, "%s: N too large", fn);
+  return MOE_OK;
+}
+
+}  // namespace
+
 int moe_route_topk(const float* logits, int32_t N, int32_t E, int32_t K,
                    int32_t renormalize, int32_t* topk_idx, float* topk_w,
                    void* stream) {
-  if (!logits || !topk_idx || !topk_w)
-    return fail(MOE_ERR_INVALID_ARG, "moe_route_topk: null pointer");
-  if (N < 0 || E < 1 || K < 1 || K > E)
-    return fail(MOE_ERR_INVALID_ARG, "moe_route_topk: need N >= 0 and 1 <= K <= E (N=%d E=%d K=%d)", N, E, K);
-  if (E > MOE_MAX_EXPERTS || K > MOE_MAX_TOPK)
-    return fail(MOE_ERR_UNSUPPORTED, "moe_route_topk: E <= %d and K <= %d supported", MOE_MAX_EXPERTS, MOE_MAX_TOPK);
-  if ((int64_t)N * E >= ((int64_t)1 << 31) * 4 || (int64_t)N * K >= ((int64_t)1 << 31))
-    return fail(MOE_ERR_UNSUPPORTED, "moe_route_topk: N too large");
-  return hip_status(moe::launch_route_topk(logits, N, E, K, renormalize,
-                                           topk_idx, topk_w, as_stream(stream)),
+  return moe_route_topk_gated(logits, N, E, K, MOE_GATE_SOFTMAX, renormalize, topk_idx,
+                              topk_w, stream);
+}
+
+int moe_route_topk_gated(const float* logits, int32_t N, int32_t E, int32_t K, int32_t gate,
+                         int32_t renormalize, int32_t* topk_idx, float* topk_w, void* stream) {
+  const int st = route_checks("moe_route_topk", logits, N, E, K, topk_idx, topk_w);
+  if (st != MOE_OK) return st;
+  if (gate != MOE_GATE_SOFTMAX && gate != MOE_GATE_SIGMOID)
+    return fail(MOE_ERR_INVALID_ARG, "moe_route_topk: gate %d is not a moe_gate_t", gate);
+  return hip_status(moe::launch_route_topk(logits, N, E, K, gate == MOE_GATE_SIGMOID,
+                                           renormalize, topk_idx, topk_w, as_stream(stream)),
                     "moe_route_topk");
+}
+
+size_t moe_reroute_workspace_bytes(int32_t N, int32_t E, int32_t K) {
+  if (N < 1 || E < 1 || K < 1) return 0;
+  return moe::reroute_workspace_bytes(N, E, K);
+}
+
+int moe_reroute_overflow(const float* logits, int32_t N, int32_t E, int32_t K, int32_t gate,
+                         int32_t renormalize, int64_t capacity, int32_t* topk_idx,
+                         float* topk_w, int32_t* rerouted, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  const int st = route_checks("moe_reroute_overflow", logits, N, E, K, topk_idx, topk_w);
+  if (st != MOE_OK) return st;
+  if (N < 1 || capacity < -1)
+    return fail(MOE_ERR_INVALID_ARG, "moe_reroute_overflow: need N >= 1 and capacity >= -1 "
+                "(N=%d capacity=%lld)", N, (long long)capacity);
+  if (gate != MOE_GATE_SOFTMAX && gate != MOE_GATE_SIGMOID)
+    return fail(MOE_ERR_INVALID_ARG, "moe_reroute_overflow: gate %d is not a moe_gate_t", gate);
+  const size_t need = moe::reroute_workspace_bytes(N, E, K);
+  if (!workspace || workspace_bytes < need)
+    return fail(MOE_ERR_WORKSPACE, "moe_reroute_overflow: workspace needs %zu bytes", need);
+  return hip_status(moe::launch_reroute(logits, N, E, K, gate == MOE_GATE_SIGMOID, renormalize,
+                                        capacity, topk_idx, topk_w, rerouted, workspace,
+                                        as_stream(stream)),
+                    "moe_reroute_overflow");
 }
 
 size_t moe_dispatch_workspace_bytes(int32_t N, int32_t E, int32_t K) {

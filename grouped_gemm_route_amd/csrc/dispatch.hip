@@ -272,4 +272,20 @@ hipError_t launch_dispatch(const void* x, size_t row_bytes, int N,
   return hipGetLastError();
 }
 
+hipError_t launch_rank_scan(const int32_t* idx, int N, int E, int K, int64_t capacity,
+                            int32_t* block_counts, int32_t* block_excl,
+                            int32_t* local_rank, int32_t* demand, int32_t* counts,
+                            int32_t* offsets, int32_t* rank_offsets, hipStream_t stream) {
+  const int B = (N + kRankBlockTokens - 1) / kRankBlockTokens;
+  const size_t lds = (size_t)kRankWaves * E * sizeof(unsigned long long);
+  dispatch_rank_kernel<<<B, kRankBlockTokens, lds, stream>>>(idx, N, E, K, block_counts,
+                                                             local_rank);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  dispatch_scan_kernel<<<1, kScanThreads, 0, stream>>>(block_counts, B, E, 1, capacity,
+                                                       block_excl, demand, counts, offsets,
+                                                       rank_offsets);
+  return hipGetLastError();
+}
+
 }  // namespace moe

@@ -28,9 +28,9 @@ inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 // ---- launchers (each returns the hipError_t of its launches) -------------
 
-hipError_t launch_route_topk(const float* logits, int N, int E, int K,
-                             int renormalize, int32_t* topk_idx,
-                             float* topk_w, hipStream_t stream);
+hipError_t launch_route_topk(const float* logits, int N, int E, int K, bool sigmoid,
+                             int renormalize, int32_t* topk_idx, float* topk_w,
+                             hipStream_t stream);
 
 // Workspace carve-up of moe_dispatch.
 struct DispatchWorkspace {
@@ -48,6 +48,22 @@ hipError_t launch_dispatch(const void* x, size_t row_bytes, int N,
                            int32_t* demand, int32_t* counts,
                            int32_t* offsets, int32_t* rank_offsets,
                            const DispatchWorkspace& ws, hipStream_t stream);
+
+// Stable per-(token, slot) ranks of a [N, K] expert-id table (entries
+// outside [0, E) are skipped) and their per-expert scan with one rank:
+// block_counts / block_excl [B, E], local_rank [N, K], demand / counts [E],
+// offsets [E + 1], rank_offsets [2], as in moe_dispatch.
+hipError_t launch_rank_scan(const int32_t* idx, int N, int E, int K, int64_t capacity,
+                            int32_t* block_counts, int32_t* block_excl,
+                            int32_t* local_rank, int32_t* demand, int32_t* counts,
+                            int32_t* offsets, int32_t* rank_offsets, hipStream_t stream);
+
+size_t reroute_workspace_bytes(int N, int E, int K);
+
+hipError_t launch_reroute(const float* logits, int N, int E, int K, bool sigmoid,
+                          int renormalize, int64_t capacity, int32_t* topk_idx,
+                          float* topk_w, int32_t* rerouted, void* workspace,
+                          hipStream_t stream);
 
 hipError_t launch_combine(const void* y_perm, bool bf16_data, int N, int d,
                           int K, const int32_t* dest, const float* topk_w,

@@ -50,6 +50,9 @@ typedef enum {
 
 typedef enum { MOE_DTYPE_F32 = 0, MOE_DTYPE_BF16 = 1 } moe_dtype_t;
 
+/* Gate function of the router scores (moe_route_topk_gated). */
+typedef enum { MOE_GATE_SOFTMAX = 0, MOE_GATE_SIGMOID = 1 } moe_gate_t;
+
 #define MOE_ABI_VERSION 1
 #define MOE_MAX_EXPERTS 1024
 #define MOE_MAX_TOPK 16
@@ -94,6 +97,59 @@ int64_t moe_capacity(double C, int64_t N, int32_t K, int32_t E);
 int moe_route_topk(const float* logits, int32_t N, int32_t E, int32_t K,
                    int32_t renormalize, int32_t* topk_idx, float* topk_w,
                    void* stream);
+
+/*
+ * Top-K routing with a choice of gate.  "MoE 推理服务工程真相 2026", section
+ * 2.3, names sigmoid routing as a remedy for router-level imbalance.
+ *   gate == MOE_GATE_SOFTMAX: as moe_route_topk.
+ *   gate == MOE_GATE_SIGMOID: topk_w[t, k] = 1 / (1 + exp(-logit)) of the
+ *   chosen expert (each expert's score independent of the others); if
+ *   renormalize != 0, divided by the sum of the K chosen scores.
+ * The choice of experts (topk_idx) is the same for both gates.
+ * Checks: as moe_route_topk; gate a moe_gate_t value (INVALID_ARG).
+ */
+int moe_route_topk_gated(const float* logits, int32_t N, int32_t E, int32_t K, int32_t gate,
+                         int32_t renormalize, int32_t* topk_idx, float* topk_w, void* stream);
+
+/* Bytes of device workspace moe_reroute_overflow needs for these sizes. */
+size_t moe_reroute_workspace_bytes(int32_t N, int32_t E, int32_t K);
+
+/*
+ * One round of token re-routing of capacity overflow, between routing and
+ * dispatch.  "MoE 推理服务工程真相 2026", section 2.3: the dispatch
+ * pseudocode counts each expert's tokens against the capacity and re-maps
+ * the expert ids of the overflow; section 4.3 ("Token drop"): an
+ * over-capacity token goes to a next-best expert instead of losing that
+ * expert's output.  The pages leave the rule open; this call takes:
+ *   1. slot (t, k) overflows iff its expert was named by `capacity` slots
+ *      earlier in (token, slot) order -- the slots moe_dispatch drops;
+ *   2. token t's j-th overflowing slot (j = 0, 1, .. in slot order) is
+ *      offered the expert at position K + j of the token's order (larger
+ *      logit first, ties to the lower index): its best experts outside its
+ *      own top K; none if K + j >= E;
+ *   3. candidates are admitted in (token, slot) order while their expert
+ *      has room left by step 1 (capacity minus its surviving slots);
+ *   4. an admitted slot gets the new expert in topk_idx and its gate score
+ *      (as moe_route_topk_gated computes it, including renormalize's
+ *      divisor of the token's original K scores) in topk_w.
+ * Other slots are left unchanged; moe_dispatch with the same capacity then
+ * keeps the step-1 survivors plus every admitted slot and drops the rest.
+ *   logits       [N, E] fp32, the routing input (finite).
+ *   topk_idx     [N, K] int32 in/out, as moe_route_topk(_gated) wrote it
+ *                (distinct experts, best first: unchecked precondition).
+ *   topk_w       [N, K] fp32 in/out.
+ *   gate, renormalize  as given to the routing call.
+ *   capacity     per-expert budget; -1 (dropless) makes the call a no-op.
+ *   rerouted     [E] int32 out, admitted slots per expert; may be NULL.
+ *   workspace    device scratch of moe_reroute_workspace_bytes(N, E, K).
+ * Results are deterministic (no atomics decide anything).
+ * Checks: as moe_route_topk_gated; N >= 1, capacity >= -1 (INVALID_ARG);
+ *         workspace (WORKSPACE).
+ */
+int moe_reroute_overflow(const float* logits, int32_t N, int32_t E, int32_t K, int32_t gate,
+                         int32_t renormalize, int64_t capacity, int32_t* topk_idx,
+                         float* topk_w, int32_t* rerouted, void* workspace,
+                         size_t workspace_bytes, void* stream);
 
 /*
  * Router projection: logits[t, e] = sum_i x[t, i] * w_router[e, i] for all

@@ -88,6 +88,35 @@ def test_route_rejects_bad_arguments(lib):
     assert "K" in lib.moe_last_error().decode()
 
 
+def test_gated_route_and_reroute_reject_bad_arguments(lib):
+    g = lib.moe_route_topk_gated
+    assert g(FAKE, 4, 8, 2, 2, 0, FAKE, FAKE, NUL) == 1        # gate not a moe_gate_t
+    assert g(FAKE, 4, 8, 2, -1, 0, FAKE, FAKE, NUL) == 1
+    assert g(NUL, 4, 8, 2, 1, 0, FAKE, FAKE, NUL) == 1
+    assert g(FAKE, 4, 8, 9, 1, 0, FAKE, FAKE, NUL) == 1        # K > E
+    assert g(FAKE, 4, 1025, 2, 1, 0, FAKE, FAKE, NUL) == 2     # E limit
+
+    def rr(**kw):
+        a = dict(l=FAKE, N=16, E=8, K=2, gate=0, renorm=0, cap=3, idx=FAKE, w=FAKE,
+                 out=FAKE, ws=FAKE, ws_bytes=1 << 30)
+        a.update(kw)
+        return lib.moe_reroute_overflow(a["l"], a["N"], a["E"], a["K"], a["gate"], a["renorm"],
+                                        a["cap"], a["idx"], a["w"], a["out"], a["ws"],
+                                        a["ws_bytes"], NUL)
+    assert rr(l=NUL) == 1
+    assert rr(idx=NUL) == 1
+    assert rr(N=0) == 1
+    assert rr(K=9) == 1
+    assert rr(cap=-2) == 1
+    assert rr(gate=7) == 1
+    assert rr(E=2048) == 2
+    need = lib.moe_reroute_workspace_bytes(16, 8, 2)
+    assert need > 0
+    assert rr(ws_bytes=need - 1) == 3
+    assert rr(ws=NUL) == 3
+    assert "workspace" in lib.moe_last_error().decode()
+
+
 def _dispatch(lib, **kw):
     a = dict(x=FAKE, dtype=1, N=16, d=64, idx=FAKE, E=8, K=2, W=4, cap=-1, x_perm=FAKE,
              perm=FAKE, dest=FAKE, demand=FAKE, counts=FAKE, offsets=FAKE, roff=FAKE,
