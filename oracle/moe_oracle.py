@@ -43,6 +43,14 @@ next-best expert instead of dropping it):
             j-th overflowing slot is offered its (K + j)-th best expert and
             takes it if that expert still has room, in token order.
 
+FP8 payload ("MoE 推理服务工程真相 2026", section 6.3: the all-to-all token
+data goes as FP8 instead of BF16, halving the bytes):
+
+  fp8       rows are cut into groups of 128 columns; each group is stored
+            as OCP e4m3 codes of x * (448 / amax) (fp32 arithmetic,
+            round-to-nearest-even) with the fp32 scale amax / 448, and read
+            back as code value * scale.
+
 Where the pages say nothing (the gate function, the tie-break, the order
 inside an expert, the capacity formula, the FFN form) the oracle takes the
 plain reading: fp32-input softmax, lowest index wins ties, ascending token
@@ -82,6 +90,10 @@ __all__ = [
     "token_outputs",
     "router_logits",
     "router_logits_error_bound",
+    "e4m3_value",
+    "e4m3_encode",
+    "quantize_fp8",
+    "dequantize_fp8",
     "shard_bounds",
     "exchange",
     "tau_min",
@@ -489,10 +501,91 @@ def combine(y_perm, dest, topk_w, act):
 # the whole layer
 # --------------------------------------------------------------------------
 
+# --------------------------------------------------------------------------
+# fp8 payload
+# --------------------------------------------------------------------------
+
+FP8_GROUP = 128
+E4M3_MAX = 448.0
+
+
+def e4m3_value(code):
+    """Value of OCP FP8 E4M3 codes (uint8 array) as float64, from the format's
+    definition: sign bit, 4-bit exponent with bias 7, 3-bit mantissa;
+    exponent 0 holds the subnormals m * 2**-9; S.1111.111 is NaN (there are
+    no infinities), so the largest finite value is 1.75 * 2**8 = 448."""
+    c = np.asarray(code).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = c & 0x7
+    mag = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * 2.0 ** (e - 7.0))
+    mag = np.where((e == 0xF) & (m == 0x7), np.nan, mag)
+    return sign * mag
+
+
+def e4m3_encode(v):
+    """E4M3 code nearest to each value (|v| <= 448), ties to the even code.
+
+    The 127 non-negative finite codes 0x00..0x7E have increasing values, so
+    the nearest code is found by search over that table; the sign goes to bit 7
+    (so -0.0 and +0.0 both encode as their sign with a zero magnitude)."""
+    v = np.asarray(v, dtype=np.float64)
+    if np.any(np.abs(v) > E4M3_MAX) or np.any(~np.isfinite(v)):
+        raise ValueError("e4m3_encode takes finite |v| <= 448")
+    table = e4m3_value(np.arange(0x7F))
+    a = np.abs(v)
+    hi = np.clip(np.searchsorted(table, a, side="left"), 0, 0x7E)
+    lo = np.clip(hi - 1, 0, 0x7E)
+    d_lo = a - table[lo]
+    d_hi = table[hi] - a
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
+    code = np.where(pick_hi, hi, lo)
+    code = np.where(a == table[hi], hi, code)
+    return (code | np.where(np.signbit(v), 0x80, 0)).astype(np.uint8)
+
+
+def quantize_fp8(x, group=FP8_GROUP):
+    """Rows of x [R, d] (d a multiple of group) -> (codes uint8 [R, d],
+    scales float32 [R, d / group]).
+
+    Per group of `group` columns, in fp32 as a GPU computes it: amax = max
+    |x|; r = 448 / amax (0 when amax = 0); code = e4m3_encode(clamp(x * r,
+    -448, 448)); scale = amax / 448.  Each quotient and product is one fp32
+    operation, so the codes are exact functions of the inputs."""
+    x32 = np.asarray(x, dtype=np.float32)
+    R, d = x32.shape
+    if d % group:
+        raise ValueError("d must be a multiple of the group size")
+    g = x32.reshape(R, d // group, group)
+    amax = np.abs(g).max(axis=2)
+    f448 = np.float32(E4M3_MAX)
+    with np.errstate(divide="ignore"):
+        r = np.where(amax > 0, f448 / np.where(amax > 0, amax, np.float32(1)), np.float32(0))
+    r = r.astype(np.float32)
+    v = (g * r[:, :, None]).astype(np.float32)
+    v = np.clip(v, -f448, f448)
+    codes = e4m3_encode(v.astype(np.float64)).reshape(R, d)
+    scales = (amax / f448).astype(np.float32)
+    return codes, scales
+
+
+def dequantize_fp8(codes, scales, group=FP8_GROUP):
+    """float32 [R, d]: the value of each code times its group's scale (one
+    fp32 multiply)."""
+    c = np.asarray(codes)
+    R, d = c.shape
+    val = e4m3_value(c).astype(np.float32).reshape(R, d // group, group)
+    s = np.asarray(scales, dtype=np.float32)[:, :, None]
+    return (val * s).astype(np.float32).reshape(R, d)
+
+
 def layer(logits, x, expert_weights, K, W, cap, act, renormalize=False, gate="softmax",
-          reroute=False):
+          reroute=False, fp8=False):
     """Route (optionally re-routing overflow), dispatch, FFN and combine;
-    returns every intermediate."""
+    returns every intermediate.  fp8=True sends both exchanges as fp8: the
+    packed rows are quantized (x8, x_scale) and read back as bf16 for the
+    FFN; its output rows are quantized (y8, y_scale) and combined from their
+    fp8 values."""
     N, E = np.asarray(logits).shape
     idx, w = route(logits, K, renormalize, gate)
     rerouted = np.zeros(E, dtype=np.int32)
@@ -500,9 +593,18 @@ def layer(logits, x, expert_weights, K, W, cap, act, renormalize=False, gate="so
         idx, w, rerouted = reroute_overflow(logits, idx, cap, gate, renormalize)
     disp = dispatch(idx, E, W, cap)
     x_perm = pack(x, disp["perm_token"])
-    h, y = grouped_ffn(x_perm, disp["offsets"], expert_weights, act)
-    out = combine(y, disp["dest"], w, act)
     res = dict(disp)
+    if fp8:
+        x8, xs = quantize_fp8(x_perm)
+        x_perm = round_storage(dequantize_fp8(x8, xs).astype(np.float64), act)
+        res.update(x8=x8, x_scale=xs)
+    h, y = grouped_ffn(x_perm, disp["offsets"], expert_weights, act)
+    y_in = y
+    if fp8:
+        y8, ys = quantize_fp8(y)
+        y_in = dequantize_fp8(y8, ys).astype(np.float64)
+        res.update(y8=y8, y_scale=ys)
+    out = combine(y_in, disp["dest"], w, act)
     res.update(topk_idx=idx, topk_w=w, x_perm=x_perm, h=h, y_perm=y, out=out,
                rerouted=rerouted)
     return res

@@ -7,6 +7,7 @@ import pytest
 from oracle import moe_oracle as O
 import test_oracle as P
 import test_oracle_reroute as PR
+import test_oracle_fp8 as PF
 
 _route = O.route
 _dispatch = O.dispatch
@@ -14,6 +15,8 @@ _expert_ffn = O.expert_ffn
 _combine = O.combine
 _reroute = O.reroute_overflow
 _gate_scores = O.gate_scores
+_e4m3_encode = O.e4m3_encode
+_quantize_fp8 = O.quantize_fp8
 
 
 def _route_tie_high(logits, K, renormalize=False, gate="softmax"):
@@ -35,6 +38,23 @@ def _gate_sigmoid_sign(logits, gate="softmax"):
     if gate == "sigmoid":
         return 1.0 / (1.0 + np.exp(np.asarray(logits, np.float64)))
     return _gate_scores(logits, gate)
+
+
+def _e4m3_ties_away(v):
+    # rounds halfway cases away from zero instead of to the even code
+    v = np.asarray(v, np.float64)
+    code = _e4m3_encode(v)
+    table = O.e4m3_value(np.arange(0x7F))
+    mids = (table[1:] + table[:-1]) / 2
+    a = np.abs(v)
+    tie = np.isin(a, mids)
+    up = np.searchsorted(table, a)
+    return np.where(tie, (up | np.where(np.signbit(v), 0x80, 0)).astype(np.uint8), code)
+
+
+def _quantize_scale_447(x, group=128):
+    codes, scales = _quantize_fp8(x, group)
+    return codes, (scales * np.float32(448) / np.float32(447)).astype(np.float32)
 
 
 def _reroute_candidate_off_by_one(logits, topk_idx, cap, gate="softmax", renormalize=False):
@@ -129,6 +149,8 @@ MUTANTS = {
     "gate_sigmoid_sign": ("gate_scores", _gate_sigmoid_sign),
     "reroute_candidate_off_by_one": ("reroute_overflow", _reroute_candidate_off_by_one),
     "reroute_ignores_room": ("reroute_overflow", _reroute_ignores_room),
+    "e4m3_ties_away": ("e4m3_encode", _e4m3_ties_away),
+    "quantize_scale_447": ("quantize_fp8", _quantize_scale_447),
 }
 
 PINS = [
@@ -146,6 +168,10 @@ PINS = [
     lambda: [PR.test_reroute_uniform_closed_form(*c) for c in ((10, 3, 2, 6), (12, 4, 3, 6))],
     lambda: PR.test_reroute_is_a_no_op_without_overflow(),
     lambda: [PR.test_reroute_against_brute_force(s) for s in range(4)],
+    lambda: PF.test_e4m3_closed_forms(),
+    lambda: PF.test_e4m3_encode_matches_torch_cast(),
+    lambda: PF.test_quantize_group_properties(),
+    lambda: PF.test_quantize_is_exact_on_representable_groups(),
 ]
 
 
