@@ -10,10 +10,14 @@ from .binding import (  # noqa: F401
     moe_abi_version,
     moe_capacity,
     moe_combine,
+    moe_combine_fp8,
     moe_dispatch,
+    moe_dispatch_fp8,
     moe_dispatch_workspace_bytes,
     moe_exchange_plan,
     moe_exchange_workspace_bytes,
+    moe_fp8_dequantize_rows,
+    moe_fp8_quantize_rows,
     moe_grouped_ffn,
     moe_grouped_ffn_workspace_bytes,
     moe_reroute_overflow,

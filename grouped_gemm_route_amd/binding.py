@@ -46,7 +46,14 @@ SIGNATURES = [
     ("moe_exchange_plan", ctypes.c_int,
      [_P, _P, _P, _P, _I32, _I32, _I32, _I32, _I64, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     ("moe_rows_permute", ctypes.c_int, [_P, _P, _P, _P, _I64, _I32, _I32, _P]),
+    ("moe_dispatch_fp8", ctypes.c_int,
+     [_P, _I32, _I32, _P, _I32, _I32, _I32, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    ("moe_combine_fp8", ctypes.c_int, [_P, _P, _I32, _I32, _I32, _P, _P, _P, _P]),
+    ("moe_fp8_quantize_rows", ctypes.c_int, [_P, _P, _I64, _I32, _P, _P, _P]),
+    ("moe_fp8_dequantize_rows", ctypes.c_int, [_P, _P, _P, _I64, _I32, _P, _P]),
 ]
+
+FP8_GROUP = 128  # columns per fp32 scale of the fp8 payload
 
 _lib = None
 
@@ -264,6 +271,113 @@ def moe_dispatch(x, topk_idx, E, W, capacity, out=None):
     return out
 
 
+def alloc_dispatch_fp8_outputs(N, d, E, K, W, device):
+    out = alloc_dispatch_outputs(N, 16, E, K, W, torch.bfloat16, device)
+    del out["x_perm"]
+    out["x8"] = torch.empty(N * K, d, dtype=torch.uint8, device=device)
+    out["x_scale"] = torch.empty(N * K, d // FP8_GROUP, dtype=torch.float32, device=device)
+    return out
+
+
+def moe_dispatch_fp8(x, topk_idx, E, W, capacity, out=None):
+    """moe_dispatch with an fp8 payload: returns the dict of outputs with x8
+    (uint8 e4m3 codes [N*K, d]) and x_scale (fp32 [N*K, d/128]) in place of
+    x_perm."""
+    _need(x, "x", torch.bfloat16)
+    N, d = x.shape
+    dev = x.device
+    _need(topk_idx, "topk_idx", torch.int32, dev)
+    K = topk_idx.shape[1]
+    if topk_idx.shape[0] != N:
+        raise ValueError("topk_idx must be [N, K]")
+    if out is None:
+        out = alloc_dispatch_fp8_outputs(N, d, E, K, W, dev)
+    sizes = {"perm_token": N * K, "dest": N * K, "demand": E, "counts": E,
+             "offsets": E + 1, "rank_offsets": W + 1}
+    for k, n in sizes.items():
+        _need(out[k], k, torch.int32, dev)
+        if out[k].numel() < n:
+            raise ValueError(f"{k} must hold at least {n} elements")
+    _need(out["x8"], "x8", torch.uint8, dev)
+    _need(out["x_scale"], "x_scale", torch.float32, dev)
+    if out["x8"].numel() < N * K * d or out["x_scale"].numel() < N * K * (d // FP8_GROUP):
+        raise ValueError("x8 / x_scale too small")
+    ws = out["workspace"]
+    _need(ws, "workspace", None, dev)
+    _check("moe_dispatch_fp8", load_library().moe_dispatch_fp8(
+        _ptr(x), N, d, _ptr(topk_idx), E, K, W, int(capacity), _ptr(out["x8"]),
+        _ptr(out["x_scale"]), _ptr(out["perm_token"]), _ptr(out["dest"]), _ptr(out["demand"]),
+        _ptr(out["counts"]), _ptr(out["offsets"]), _ptr(out["rank_offsets"]), _ptr(ws),
+        ws.numel() * ws.element_size(), _stream(x)))
+    return out
+
+
+def moe_combine_fp8(y8, y_scale, dest, topk_w, out=None):
+    """Weighted merge of fp8 expert outputs back to token order (bf16 out)."""
+    _need(y8, "y8", torch.uint8)
+    dev = y8.device
+    _need(y_scale, "y_scale", torch.float32, dev)
+    _need(dest, "dest", torch.int32, dev)
+    _need(topk_w, "topk_w", torch.float32, dev)
+    N, K = dest.shape
+    d = y8.shape[1]
+    if tuple(topk_w.shape) != (N, K):
+        raise ValueError("topk_w must match dest [N, K]")
+    if out is None:
+        out = torch.empty(N, d, dtype=torch.bfloat16, device=dev)
+    _need(out, "out", torch.bfloat16, dev)
+    _check("moe_combine_fp8", load_library().moe_combine_fp8(
+        _ptr(y8), _ptr(y_scale), N, d, K, _ptr(dest), _ptr(topk_w), _ptr(out), _stream(y8)))
+    return out
+
+
+def moe_fp8_quantize_rows(src, n_rows, max_rows=None, q=None, scale=None):
+    """fp8 codes and scales of rows [0, min(n_rows[0], max_rows)) of a bf16
+    [rows, d] tensor; n_rows is a one-element int32 device tensor."""
+    _need(src, "src", torch.bfloat16)
+    dev = src.device
+    _need(n_rows, "n_rows", torch.int32, dev)
+    R, d = src.shape
+    if max_rows is None:
+        max_rows = R
+    if max_rows > R:
+        raise ValueError("max_rows exceeds src rows")
+    if q is None:
+        q = torch.empty(R, d, dtype=torch.uint8, device=dev)
+    if scale is None:
+        scale = torch.empty(R, d // FP8_GROUP, dtype=torch.float32, device=dev)
+    _need(q, "q", torch.uint8, dev)
+    _need(scale, "scale", torch.float32, dev)
+    if q.numel() < max_rows * d or scale.numel() < max_rows * (d // FP8_GROUP):
+        raise ValueError("q / scale too small")
+    _check("moe_fp8_quantize_rows", load_library().moe_fp8_quantize_rows(
+        _ptr(src), _ptr(n_rows), int(max_rows), d, _ptr(q), _ptr(scale), _stream(src)))
+    return q, scale
+
+
+def moe_fp8_dequantize_rows(q, scale, n_rows, max_rows=None, dst=None):
+    """bf16 rows (code value * scale) of rows [0, min(n_rows[0], max_rows))."""
+    _need(q, "q", torch.uint8)
+    dev = q.device
+    _need(scale, "scale", torch.float32, dev)
+    _need(n_rows, "n_rows", torch.int32, dev)
+    R, d = q.shape
+    if max_rows is None:
+        max_rows = R
+    if max_rows > R:
+        raise ValueError("max_rows exceeds q rows")
+    if scale.numel() < max_rows * (d // FP8_GROUP):
+        raise ValueError("scale too small")
+    if dst is None:
+        dst = torch.empty(R, d, dtype=torch.bfloat16, device=dev)
+    _need(dst, "dst", torch.bfloat16, dev)
+    if dst.numel() < max_rows * d:
+        raise ValueError("dst too small")
+    _check("moe_fp8_dequantize_rows", load_library().moe_fp8_dequantize_rows(
+        _ptr(q), _ptr(scale), _ptr(n_rows), int(max_rows), d, _ptr(dst), _stream(q)))
+    return dst
+
+
 def moe_grouped_ffn_workspace_bytes(max_rows, E, dtype):
     return int(load_library().moe_grouped_ffn_workspace_bytes(max_rows, E, DTYPE_CODE[dtype]))
 
@@ -397,17 +511,23 @@ class MoeLayer:
     enqueues route -> dispatch -> grouped FFN -> combine on the current
     stream with no host synchronisation and no allocation.  gate picks the
     router's gate function; reroute=True re-routes capacity overflow to
-    next-best experts between route and dispatch.
+    next-best experts between route and dispatch.  fp8=True (bf16 layers)
+    sends both exchanges as fp8: dispatch packs e4m3 codes, the rows are
+    turned back into bf16 for the FFN, its output rows are quantized and
+    the combine reads them as fp8.
     """
 
     def __init__(self, N, d, ffn, E, K, W, capacity, dtype, device, renormalize=False,
-                 gate="softmax", reroute=False):
+                 gate="softmax", reroute=False, fp8=False):
         self.N, self.d, self.ffn_dim, self.E, self.K, self.W = N, d, ffn, E, K, W
         self.capacity = int(capacity)
         self.renormalize = renormalize
         self.gate = gate
         _gate(gate)
         self.reroute = reroute
+        self.fp8 = fp8
+        if fp8 and (dtype != torch.bfloat16 or d % FP8_GROUP):
+            raise ValueError("the fp8 payload needs bf16 rows with d a multiple of 128")
         self.max_rows = N * K
         dev = torch.device(device)
         self.topk_idx = torch.empty(N, K, dtype=torch.int32, device=dev)
@@ -421,6 +541,13 @@ class MoeLayer:
         self.rerouted = torch.zeros(E, dtype=torch.int32, device=dev)
         self.reroute_ws = (torch.empty(max(1, moe_reroute_workspace_bytes(N, E, K)),
                                        dtype=torch.uint8, device=dev) if reroute else None)
+        if fp8:
+            self.disp8 = alloc_dispatch_fp8_outputs(N, d, E, K, W, dev)
+            self.disp8["x_perm"] = self.disp["x_perm"]     # receive-side bf16 rows
+            self.disp = self.disp8
+            self.y8 = torch.empty(self.max_rows, d, dtype=torch.uint8, device=dev)
+            self.y_scale = torch.empty(self.max_rows, d // FP8_GROUP, dtype=torch.float32,
+                                       device=dev)
 
     def route(self, logits):
         moe_route_topk(logits, self.K, self.renormalize, self.topk_idx, self.topk_w, self.gate)
@@ -430,14 +557,24 @@ class MoeLayer:
         return self.topk_idx, self.topk_w
 
     def dispatch(self, x):
-        return moe_dispatch(x, self.topk_idx, self.E, self.W, self.capacity, self.disp)
+        if not self.fp8:
+            return moe_dispatch(x, self.topk_idx, self.E, self.W, self.capacity, self.disp)
+        moe_dispatch_fp8(x, self.topk_idx, self.E, self.W, self.capacity, self.disp)
+        n_rows = self.disp["offsets"][self.E:]
+        moe_fp8_dequantize_rows(self.disp["x8"], self.disp["x_scale"], n_rows, self.max_rows,
+                                self.disp["x_perm"])
+        return self.disp
 
     def ffn(self, w_gate, w_up, w_down):
         return moe_grouped_ffn(self.disp["x_perm"], self.disp["offsets"], w_gate, w_up, w_down,
                                self.max_rows, self.h, self.y_perm, self.ffn_ws)
 
     def combine(self):
-        return moe_combine(self.y_perm, self.disp["dest"], self.topk_w, self.out)
+        if not self.fp8:
+            return moe_combine(self.y_perm, self.disp["dest"], self.topk_w, self.out)
+        n_rows = self.disp["offsets"][self.E:]
+        moe_fp8_quantize_rows(self.y_perm, n_rows, self.max_rows, self.y8, self.y_scale)
+        return moe_combine_fp8(self.y8, self.y_scale, self.disp["dest"], self.topk_w, self.out)
 
     def forward(self, logits, x, w_gate, w_up, w_down):
         self.route(logits)

@@ -159,37 +159,121 @@ size_t moe_dispatch_workspace_bytes(int32_t N, int32_t E, int32_t K) {
   return moe::dispatch_workspace_bytes(N, E, K);
 }
 
+namespace {
+
+// Checks shared by moe_dispatch and moe_dispatch_fp8 (es: bytes per element).
+int dispatch_checks(const char* fn, const void* x, int es, int32_t N, int32_t d,
+                    const int32_t* topk_idx, int32_t E, int32_t K, int32_t W, int64_t capacity,
+                    const void* x_perm, const int32_t* perm_token, const int32_t* dest,
+                    const int32_t* demand, const int32_t* counts, const int32_t* offsets,
+                    const int32_t* rank_offsets, const void* workspace, size_t workspace_bytes) {
+  if (!x || !topk_idx || !x_perm || !perm_token || !dest || !demand || !counts || !offsets ||
+      !rank_offsets)
+    return fail(MOE_ERR_INVALID_ARG, "%s: null pointer", fn);
+  if (N < 1 || d < 1 || K < 1 || K > E || W < 1 || E % W != 0 || capacity < -1)
+    return fail(MOE_ERR_INVALID_ARG,
+                "%s: need N >= 1, d >= 1, 1 <= K <= E, W >= 1, E %% W == 0, "
+                "capacity >= -1 (N=%d d=%d E=%d K=%d W=%d capacity=%lld)",
+                fn, N, d, E, K, W, (long long)capacity);
+  if (((int64_t)d * es) % 16 != 0)
+    return fail(MOE_ERR_INVALID_ARG, "%s: row bytes d*%d must be a multiple of 16", fn, es);
+  if ((int64_t)N * K >= ((int64_t)1 << 31))
+    return fail(MOE_ERR_INVALID_ARG, "%s: N*K must be below 2^31", fn);
+  if (E > MOE_MAX_EXPERTS || K > MOE_MAX_TOPK)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: E <= %d and K <= %d supported", fn, MOE_MAX_EXPERTS,
+                MOE_MAX_TOPK);
+  const size_t need = moe::dispatch_workspace_bytes(N, E, K);
+  if (!workspace || workspace_bytes < need)
+    return fail(MOE_ERR_WORKSPACE, "%s: workspace needs %zu bytes", fn, need);
+  return MOE_OK;
+}
+
+int fp8_row_checks(const char* fn, int32_t d) {
+  if (d < 1 || d % 128 != 0)
+    return fail(MOE_ERR_INVALID_ARG, "%s: d must be a positive multiple of 128 (d=%d)", fn, d);
+  return MOE_OK;
+}
+
+}  // namespace
+
 int moe_dispatch(const void* x, int32_t dtype, int32_t N, int32_t d,
                  const int32_t* topk_idx, int32_t E, int32_t K, int32_t W,
                  int64_t capacity, void* x_perm, int32_t* perm_token,
                  int32_t* dest, int32_t* demand, int32_t* counts,
                  int32_t* offsets, int32_t* rank_offsets, void* workspace,
                  size_t workspace_bytes, void* stream) {
-  if (!x || !topk_idx || !x_perm || !perm_token || !dest || !demand ||
-      !counts || !offsets || !rank_offsets)
-    return fail(MOE_ERR_INVALID_ARG, "moe_dispatch: null pointer");
   const int es = elem_size(dtype);
-  if (es == 0) return fail(MOE_ERR_UNSUPPORTED, "moe_dispatch: dtype %d", dtype);
-  if (N < 1 || d < 1 || K < 1 || K > E || W < 1 || E % W != 0 || capacity < -1)
-    return fail(MOE_ERR_INVALID_ARG,
-                "moe_dispatch: need N >= 1, d >= 1, 1 <= K <= E, W >= 1, E %% W == 0, "
-                "capacity >= -1 (N=%d d=%d E=%d K=%d W=%d capacity=%lld)",
-                N, d, E, K, W, (long long)capacity);
-  if (((int64_t)d * es) % 16 != 0)
-    return fail(MOE_ERR_INVALID_ARG, "moe_dispatch: row bytes d*%d must be a multiple of 16", es);
-  if ((int64_t)N * K >= ((int64_t)1 << 31))
-    return fail(MOE_ERR_INVALID_ARG, "moe_dispatch: N*K must be below 2^31");
-  if (E > MOE_MAX_EXPERTS || K > MOE_MAX_TOPK)
-    return fail(MOE_ERR_UNSUPPORTED, "moe_dispatch: E <= %d and K <= %d supported", MOE_MAX_EXPERTS, MOE_MAX_TOPK);
-  const size_t need = moe::dispatch_workspace_bytes(N, E, K);
-  if (!workspace || workspace_bytes < need)
-    return fail(MOE_ERR_WORKSPACE, "moe_dispatch: workspace needs %zu bytes", need);
+  if (x && es == 0) return fail(MOE_ERR_UNSUPPORTED, "moe_dispatch: dtype %d", dtype);
+  const int st = dispatch_checks("moe_dispatch", x, es ? es : 1, N, d, topk_idx, E, K, W,
+                                 capacity, x_perm, perm_token, dest, demand, counts, offsets,
+                                 rank_offsets, workspace, workspace_bytes);
+  if (st != MOE_OK) return st;
   const moe::DispatchWorkspace ws = moe::dispatch_workspace(workspace, N, E, K);
   return hip_status(
       moe::launch_dispatch(x, (size_t)d * es, N, topk_idx, E, K, W, capacity,
-                           x_perm, perm_token, dest, demand, counts, offsets,
+                           x_perm, nullptr, perm_token, dest, demand, counts, offsets,
                            rank_offsets, ws, as_stream(stream)),
       "moe_dispatch");
+}
+
+int moe_dispatch_fp8(const void* x, int32_t N, int32_t d, const int32_t* topk_idx, int32_t E,
+                     int32_t K, int32_t W, int64_t capacity, uint8_t* x8, float* x_scale,
+                     int32_t* perm_token, int32_t* dest, int32_t* demand, int32_t* counts,
+                     int32_t* offsets, int32_t* rank_offsets, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  int st = dispatch_checks("moe_dispatch_fp8", x, 2, N, d, topk_idx, E, K, W, capacity, x8,
+                           perm_token, dest, demand, counts, offsets, rank_offsets, workspace,
+                           workspace_bytes);
+  if (st != MOE_OK) return st;
+  if (!x_scale) return fail(MOE_ERR_INVALID_ARG, "moe_dispatch_fp8: null pointer");
+  st = fp8_row_checks("moe_dispatch_fp8", d);
+  if (st != MOE_OK) return st;
+  const moe::DispatchWorkspace ws = moe::dispatch_workspace(workspace, N, E, K);
+  return hip_status(
+      moe::launch_dispatch(x, (size_t)d * 2, N, topk_idx, E, K, W, capacity, x8, x_scale,
+                           perm_token, dest, demand, counts, offsets, rank_offsets, ws,
+                           as_stream(stream)),
+      "moe_dispatch_fp8");
+}
+
+int moe_combine_fp8(const uint8_t* y8, const float* y_scale, int32_t N, int32_t d, int32_t K,
+                    const int32_t* dest, const float* topk_w, void* out, void* stream) {
+  if (!y8 || !y_scale || !dest || !topk_w || !out)
+    return fail(MOE_ERR_INVALID_ARG, "moe_combine_fp8: null pointer");
+  if (N < 1 || K < 1) return fail(MOE_ERR_INVALID_ARG, "moe_combine_fp8: need N, K >= 1");
+  const int st = fp8_row_checks("moe_combine_fp8", d);
+  if (st != MOE_OK) return st;
+  if (K > MOE_MAX_TOPK)
+    return fail(MOE_ERR_UNSUPPORTED, "moe_combine_fp8: K <= %d supported", MOE_MAX_TOPK);
+  return hip_status(moe::launch_combine_fp8(y8, y_scale, N, d, K, dest, topk_w, out,
+                                            as_stream(stream)),
+                    "moe_combine_fp8");
+}
+
+int moe_fp8_quantize_rows(const void* src, const int32_t* n_rows, int64_t max_rows, int32_t d,
+                          uint8_t* q, float* scale, void* stream) {
+  if (!src || !n_rows || !q || !scale)
+    return fail(MOE_ERR_INVALID_ARG, "moe_fp8_quantize_rows: null pointer");
+  if (max_rows < 0 || max_rows >= ((int64_t)1 << 31))
+    return fail(MOE_ERR_INVALID_ARG, "moe_fp8_quantize_rows: need 0 <= max_rows < 2^31");
+  const int st = fp8_row_checks("moe_fp8_quantize_rows", d);
+  if (st != MOE_OK) return st;
+  return hip_status(moe::launch_fp8_quantize_rows(src, n_rows, (int)max_rows, d, q, scale,
+                                                  as_stream(stream)),
+                    "moe_fp8_quantize_rows");
+}
+
+int moe_fp8_dequantize_rows(const uint8_t* q, const float* scale, const int32_t* n_rows,
+                            int64_t max_rows, int32_t d, void* dst, void* stream) {
+  if (!q || !scale || !n_rows || !dst)
+    return fail(MOE_ERR_INVALID_ARG, "moe_fp8_dequantize_rows: null pointer");
+  if (max_rows < 0 || max_rows >= ((int64_t)1 << 31))
+    return fail(MOE_ERR_INVALID_ARG, "moe_fp8_dequantize_rows: need 0 <= max_rows < 2^31");
+  const int st = fp8_row_checks("moe_fp8_dequantize_rows", d);
+  if (st != MOE_OK) return st;
+  return hip_status(moe::launch_fp8_dequantize_rows(q, scale, n_rows, (int)max_rows, d, dst,
+                                                    as_stream(stream)),
+                    "moe_fp8_dequantize_rows");
 }
 
 size_t moe_grouped_ffn_workspace_bytes(int64_t max_rows, int32_t E,

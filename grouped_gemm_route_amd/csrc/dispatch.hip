@@ -32,6 +32,7 @@
 #include "moe_route.h"
 #include "moe_internal.h"
 #include "block_scan.h"
+#include "fp8_codec.h"
 
 namespace moe {
 namespace {
@@ -147,15 +148,20 @@ constexpr int kFusedScanMaxCounts = 1024;
 //   the expert offsets (and block 0 writes demand / counts / offsets /
 //   rank_offsets) and its own per-expert bases from block_counts directly;
 //   otherwise block_excl and offsets come from the scan kernel.
-template <bool kFusedScan>
+//   kFp8: the payload is the fp8 form of the bf16 row (fp8_codec.h): a
+//   piece's 16 lanes of one 128-column group agree on its scale, and each
+//   lane stores its 8 codes (8 bytes) and, once per group, the scale to
+//   every kept row.
+template <bool kFusedScan, bool kFp8>
 __global__ __launch_bounds__(kScatterThreads) void dispatch_scatter_kernel(
     const uint4* __restrict__ x, int row_chunks, int N,
     const int32_t* __restrict__ topk_idx, int E, int K, int W, int64_t capacity,
     const int32_t* __restrict__ block_counts, const int32_t* __restrict__ block_excl,
     const int32_t* __restrict__ local_rank, int32_t* __restrict__ offsets,
     int32_t* __restrict__ demand, int32_t* __restrict__ counts,
-    int32_t* __restrict__ rank_offsets, uint4* __restrict__ x_perm,
-    int32_t* __restrict__ perm_token, int32_t* __restrict__ dest) {
+    int32_t* __restrict__ rank_offsets, void* __restrict__ x_perm,
+    float* __restrict__ x_scale, int32_t* __restrict__ perm_token,
+    int32_t* __restrict__ dest) {
   __shared__ int rows[MOE_MAX_TOPK];
   __shared__ int offs[kFusedScan ? kScatterThreads + 1 : 1];
   __shared__ int wave_sums[kScatterThreads / kWave];
@@ -210,11 +216,30 @@ __global__ __launch_bounds__(kScatterThreads) void dispatch_scatter_kernel(
   __syncthreads();
 
   const uint4* src = x + (size_t)t * row_chunks;
-  for (int c = tid; c < row_chunks; c += kScatterThreads) {
-    const uint4 v = src[c];
-    for (int k = 0; k < K; ++k) {
-      const int rk = rows[k];
-      if (rk >= 0) x_perm[(size_t)rk * row_chunks + c] = v;
+  if constexpr (kFp8) {
+    // row_chunks is a multiple of 16, so the lanes of a group are active
+    // together
+    constexpr int kPieces = kFp8Group / 8;
+    const int groups = row_chunks / kPieces;
+    uint2* q = static_cast<uint2*>(x_perm);
+    for (int c = tid; c < row_chunks; c += kScatterThreads) {
+      float scale;
+      const uint2 codes = quantize_piece(src[c], &scale);
+      for (int k = 0; k < K; ++k) {
+        const int rk = rows[k];
+        if (rk < 0) continue;
+        q[(size_t)rk * row_chunks + c] = codes;
+        if (c % kPieces == 0) x_scale[(size_t)rk * groups + c / kPieces] = scale;
+      }
+    }
+  } else {
+    uint4* dst = static_cast<uint4*>(x_perm);
+    for (int c = tid; c < row_chunks; c += kScatterThreads) {
+      const uint4 v = src[c];
+      for (int k = 0; k < K; ++k) {
+        const int rk = rows[k];
+        if (rk >= 0) dst[(size_t)rk * row_chunks + c] = v;
+      }
     }
   }
 }
@@ -241,7 +266,7 @@ DispatchWorkspace dispatch_workspace(void* base, int N, int E, int K) {
 
 hipError_t launch_dispatch(const void* x, size_t row_bytes, int N,
                            const int32_t* topk_idx, int E, int K, int W,
-                           int64_t capacity, void* x_perm,
+                           int64_t capacity, void* x_perm, float* x_scale,
                            int32_t* perm_token, int32_t* dest,
                            int32_t* demand, int32_t* counts,
                            int32_t* offsets, int32_t* rank_offsets,
@@ -252,12 +277,21 @@ hipError_t launch_dispatch(const void* x, size_t row_bytes, int N,
       topk_idx, N, E, K, ws.block_counts, ws.local_rank);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
+  // x_scale != nullptr: fp8 payload of a bf16 row (row_bytes = 2 d)
+  const bool fp8 = x_scale != nullptr;
   const int row_chunks = (int)(row_bytes / 16);
+  const uint4* xs = static_cast<const uint4*>(x);
   if ((int64_t)B * E <= kFusedScanMaxCounts && E <= kScatterThreads) {
-    dispatch_scatter_kernel<true><<<N, kScatterThreads, 0, stream>>>(
-        static_cast<const uint4*>(x), row_chunks, N, topk_idx, E, K, W, capacity,
-        ws.block_counts, nullptr, ws.local_rank, offsets, demand, counts, rank_offsets,
-        static_cast<uint4*>(x_perm), perm_token, dest);
+    if (fp8)
+      dispatch_scatter_kernel<true, true><<<N, kScatterThreads, 0, stream>>>(
+          xs, row_chunks, N, topk_idx, E, K, W, capacity, ws.block_counts, nullptr,
+          ws.local_rank, offsets, demand, counts, rank_offsets, x_perm, x_scale, perm_token,
+          dest);
+    else
+      dispatch_scatter_kernel<true, false><<<N, kScatterThreads, 0, stream>>>(
+          xs, row_chunks, N, topk_idx, E, K, W, capacity, ws.block_counts, nullptr,
+          ws.local_rank, offsets, demand, counts, rank_offsets, x_perm, nullptr, perm_token,
+          dest);
     return hipGetLastError();
   }
   dispatch_scan_kernel<<<1, kScanThreads, 0, stream>>>(
@@ -265,10 +299,16 @@ hipError_t launch_dispatch(const void* x, size_t row_bytes, int N,
       offsets, rank_offsets);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
-  dispatch_scatter_kernel<false><<<N, kScatterThreads, 0, stream>>>(
-      static_cast<const uint4*>(x), row_chunks, N, topk_idx, E, K, W, capacity,
-      ws.block_counts, ws.block_excl, ws.local_rank, offsets, demand, counts, rank_offsets,
-      static_cast<uint4*>(x_perm), perm_token, dest);
+  if (fp8)
+    dispatch_scatter_kernel<false, true><<<N, kScatterThreads, 0, stream>>>(
+        xs, row_chunks, N, topk_idx, E, K, W, capacity, ws.block_counts, ws.block_excl,
+        ws.local_rank, offsets, demand, counts, rank_offsets, x_perm, x_scale, perm_token,
+        dest);
+  else
+    dispatch_scatter_kernel<false, false><<<N, kScatterThreads, 0, stream>>>(
+        xs, row_chunks, N, topk_idx, E, K, W, capacity, ws.block_counts, ws.block_excl,
+        ws.local_rank, offsets, demand, counts, rank_offsets, x_perm, nullptr, perm_token,
+        dest);
   return hipGetLastError();
 }
 

@@ -41,9 +41,11 @@ struct DispatchWorkspace {
 size_t dispatch_workspace_bytes(int N, int E, int K);
 DispatchWorkspace dispatch_workspace(void* base, int N, int E, int K);
 
+// x_scale == nullptr: x_perm rows are bit copies of x's rows; otherwise x is
+// bf16 and x_perm / x_scale receive the fp8 payload (fp8_codec.h).
 hipError_t launch_dispatch(const void* x, size_t row_bytes, int N,
                            const int32_t* topk_idx, int E, int K, int W,
-                           int64_t capacity, void* x_perm,
+                           int64_t capacity, void* x_perm, float* x_scale,
                            int32_t* perm_token, int32_t* dest,
                            int32_t* demand, int32_t* counts,
                            int32_t* offsets, int32_t* rank_offsets,
@@ -68,6 +70,17 @@ hipError_t launch_reroute(const float* logits, int N, int E, int K, bool sigmoid
 hipError_t launch_combine(const void* y_perm, bool bf16_data, int N, int d,
                           int K, const int32_t* dest, const float* topk_w,
                           void* out, hipStream_t stream);
+
+// fp8 payload (fp8_codec.h).  Row kernels act on rows [0, min(*n_rows,
+// max_rows)) of d columns; d is a multiple of 128.
+hipError_t launch_combine_fp8(const uint8_t* y8, const float* y_scale, int N, int d, int K,
+                              const int32_t* dest, const float* topk_w, void* out,
+                              hipStream_t stream);
+hipError_t launch_fp8_quantize_rows(const void* src, const int32_t* n_rows, int max_rows,
+                                    int d, uint8_t* q, float* scale, hipStream_t stream);
+hipError_t launch_fp8_dequantize_rows(const uint8_t* q, const float* scale,
+                                      const int32_t* n_rows, int max_rows, int d, void* dst,
+                                      hipStream_t stream);
 
 size_t grouped_ffn_workspace_bytes(int64_t max_rows, int E, bool bf16_data);
 

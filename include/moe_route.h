@@ -263,6 +263,60 @@ int moe_combine(const void* y_perm, int32_t dtype, int32_t N, int32_t d,
                 int32_t K, const int32_t* dest, const float* topk_w, void* out,
                 void* stream);
 
+/*
+ * FP8 exchange payload.  "MoE 推理服务工程真相 2026", section 6.3: the
+ * all-to-all token data goes as FP8 instead of BF16, halving its bytes.
+ * Format: rows of d columns (d a multiple of 128) are cut into groups of
+ * 128; a group is stored as OCP FP8 E4M3 codes (uint8: sign, 4-bit exponent
+ * with bias 7, 3-bit mantissa, largest finite 448) of x * (448 / amax),
+ * amax the group's largest |x| (zero codes when amax < 2^-100), and its
+ * fp32 scale amax / 448 in a [rows, d / 128] array; it is read back as
+ * code value * scale.  Each step is one fp32 operation with
+ * round-to-nearest-even, so codes are an exact function of the inputs.
+ * Activations are bf16.
+ */
+
+/*
+ * moe_dispatch with an fp8 payload: identical routing outputs (perm_token,
+ * dest, demand, counts, offsets, rank_offsets), and row p of the packed
+ * buffer is the fp8 form of x[perm_token[p]]:
+ *   x       [N, d] bf16;  x8 [N*K, d] uint8 out;  x_scale [N*K, d/128] fp32 out.
+ * Checks: as moe_dispatch, plus d a positive multiple of 128 (INVALID_ARG).
+ */
+int moe_dispatch_fp8(const void* x, int32_t N, int32_t d, const int32_t* topk_idx, int32_t E,
+                     int32_t K, int32_t W, int64_t capacity, uint8_t* x8, float* x_scale,
+                     int32_t* perm_token, int32_t* dest, int32_t* demand, int32_t* counts,
+                     int32_t* offsets, int32_t* rank_offsets, void* workspace,
+                     size_t workspace_bytes, void* stream);
+
+/*
+ * moe_combine reading fp8 expert outputs: out[t] = sum over kept k of
+ * topk_w[t,k] * (code value * scale) of row dest[t,k], in fp32, ascending k,
+ * rounded to bf16.
+ *   y8 [rows, d] uint8; y_scale [rows, d/128] fp32; dest, topk_w as in
+ *   moe_combine; out [N, d] bf16.
+ * Checks: pointers non-null; N, K >= 1; d a positive multiple of 128
+ *         (INVALID_ARG); K limit (UNSUPPORTED).
+ */
+int moe_combine_fp8(const uint8_t* y8, const float* y_scale, int32_t N, int32_t d, int32_t K,
+                    const int32_t* dest, const float* topk_w, void* out, void* stream);
+
+/*
+ * Row passes at either end of an fp8 exchange, over rows [0, min(*n_rows,
+ * max_rows)) where n_rows is a DEVICE int32 (e.g. offsets + E, so the row
+ * count never visits the host); other rows are not touched.
+ *   quantize:   src [max_rows, d] bf16 -> q [max_rows, d] uint8, scale
+ *               [max_rows, d/128] fp32.
+ *   dequantize: q, scale -> dst [max_rows, d] bf16 (code value * scale,
+ *               rounded to nearest even).
+ * Checks: pointers non-null; 0 <= max_rows < 2^31; d a positive multiple of
+ *         128 (INVALID_ARG).  max_rows == 0 enqueues nothing.
+ */
+int moe_fp8_quantize_rows(const void* src, const int32_t* n_rows, int64_t max_rows, int32_t d,
+                          uint8_t* q, float* scale, void* stream);
+int moe_fp8_dequantize_rows(const uint8_t* q, const float* scale, const int32_t* n_rows,
+                            int64_t max_rows, int32_t d, void* dst, void* stream);
+
 /* Bytes of device workspace moe_exchange_plan needs for these sizes. */
 size_t moe_exchange_workspace_bytes(int32_t E, int32_t W);
 

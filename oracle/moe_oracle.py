@@ -549,9 +549,11 @@ def quantize_fp8(x, group=FP8_GROUP):
     scales float32 [R, d / group]).
 
     Per group of `group` columns, in fp32 as a GPU computes it: amax = max
-    |x|; r = 448 / amax (0 when amax = 0); code = e4m3_encode(clamp(x * r,
-    -448, 448)); scale = amax / 448.  Each quotient and product is one fp32
-    operation, so the codes are exact functions of the inputs."""
+    |x|; r = 448 / amax, or 0 when amax < 2**-100 (a zero group, or one so
+    small that the quotient would overflow fp32: its codes are zeros);
+    code = e4m3_encode(clamp(x * r, -448, 448)); scale = amax / 448.  Each
+    quotient and product is one fp32 operation, so the codes are exact
+    functions of the inputs."""
     x32 = np.asarray(x, dtype=np.float32)
     R, d = x32.shape
     if d % group:
@@ -559,8 +561,8 @@ def quantize_fp8(x, group=FP8_GROUP):
     g = x32.reshape(R, d // group, group)
     amax = np.abs(g).max(axis=2)
     f448 = np.float32(E4M3_MAX)
-    with np.errstate(divide="ignore"):
-        r = np.where(amax > 0, f448 / np.where(amax > 0, amax, np.float32(1)), np.float32(0))
+    big = amax >= np.float32(2.0 ** -100)
+    r = np.where(big, f448 / np.where(big, amax, np.float32(1)), np.float32(0))
     r = r.astype(np.float32)
     v = (g * r[:, :, None]).astype(np.float32)
     v = np.clip(v, -f448, f448)

@@ -148,6 +148,38 @@ def test_dispatch_rejects_bad_arguments(lib):
     assert "workspace" in lib.moe_last_error().decode()
 
 
+def test_fp8_entry_points_reject_bad_arguments(lib):
+    def disp(**kw):
+        a = dict(x=FAKE, N=16, d=256, idx=FAKE, E=8, K=2, W=4, cap=-1, x8=FAKE, xs=FAKE,
+                 perm=FAKE, dest=FAKE, demand=FAKE, counts=FAKE, offsets=FAKE, roff=FAKE,
+                 ws=FAKE, ws_bytes=1 << 30)
+        a.update(kw)
+        return lib.moe_dispatch_fp8(a["x"], a["N"], a["d"], a["idx"], a["E"], a["K"], a["W"],
+                                    a["cap"], a["x8"], a["xs"], a["perm"], a["dest"],
+                                    a["demand"], a["counts"], a["offsets"], a["roff"], a["ws"],
+                                    a["ws_bytes"], NUL)
+    assert disp(xs=NUL) == 1
+    assert disp(x8=NUL) == 1
+    assert disp(d=64) == 1                       # not a multiple of 128
+    assert disp(d=200) == 1
+    assert disp(K=9) == 1
+    assert disp(ws_bytes=1) == 3
+    c = lib.moe_combine_fp8
+    assert c(FAKE, NUL, 4, 256, 2, FAKE, FAKE, FAKE, NUL) == 1
+    assert c(FAKE, FAKE, 4, 96, 2, FAKE, FAKE, FAKE, NUL) == 1
+    assert c(FAKE, FAKE, 0, 256, 2, FAKE, FAKE, FAKE, NUL) == 1
+    assert c(FAKE, FAKE, 4, 256, 17, FAKE, FAKE, FAKE, NUL) == 2
+    q = lib.moe_fp8_quantize_rows
+    assert q(FAKE, NUL, 8, 256, FAKE, FAKE, NUL) == 1
+    assert q(FAKE, FAKE, -1, 256, FAKE, FAKE, NUL) == 1
+    assert q(FAKE, FAKE, 8, 100, FAKE, FAKE, NUL) == 1
+    dq = lib.moe_fp8_dequantize_rows
+    assert dq(FAKE, FAKE, FAKE, 8, 100, FAKE, NUL) == 1
+    assert dq(FAKE, FAKE, FAKE, 1 << 31, 128, FAKE, NUL) == 1
+    assert dq(NUL, FAKE, FAKE, 8, 128, FAKE, NUL) == 1
+    assert "128" in lib.moe_last_error().decode() or "null" in lib.moe_last_error().decode()
+
+
 def _ffn(lib, **kw):
     a = dict(x=FAKE, dtype=1, d=128, ffn=128, E=8, off=FAKE, max_rows=64, wg=FAKE, wu=FAKE,
              wd=FAKE, h=FAKE, y=FAKE, ws=FAKE, ws_bytes=1 << 30)

@@ -43,6 +43,7 @@ def test_quantize_group_properties():
     x = (rng.standard_normal((37, 512)) * rng.uniform(0.01, 100, (37, 1))).astype(np.float32)
     x[3, 128:256] = 0.0                           # an all-zero group
     x[5, :128] = -x[5, :128]
+    x[7, 256:384] *= np.float32(1e-32)           # amax below 2^-100: zero codes
     codes, scales = O.quantize_fp8(x)
     assert codes.dtype == np.uint8 and codes.shape == x.shape
     assert scales.dtype == np.float32 and scales.shape == (37, 4)
@@ -51,15 +52,18 @@ def test_quantize_group_properties():
     assert np.array_equal(scales, (amax / np.float32(448)).astype(np.float32))
     c = codes.reshape(37, 4, 128)
     assert scales[3, 1] == 0 and (c[3, 1] & 0x7F == 0).all()
+    assert scales[7, 2] > 0 and (c[7, 2] & 0x7F == 0).all()
     for r in range(37):
         for j in range(4):
-            if amax[r, j] > 0:                    # the group's largest value maps to +-448
+            if amax[r, j] >= 2.0 ** -100:         # the group's largest value maps to +-448
                 assert (c[r, j] & 0x7F).max() == 0x7E
     # round trip: within half a code step of the scaled value
     back = O.dequantize_fp8(codes, scales).astype(np.float64)
     s = np.repeat(scales.astype(np.float64), 128, axis=1)
     bound = np.maximum(np.abs(x) * 2.0 ** -4, s * 2.0 ** -10) * (1 + 1e-6) + s * 1e-6
-    assert (np.abs(back - x) <= bound).all()
+    big = np.repeat(amax >= 2.0 ** -100, 128, axis=1)
+    assert (np.abs(back - x) <= bound)[big].all()
+    assert (back[~big] == 0).all()
     assert np.array_equal(np.sign(back[back != 0]), np.sign(x[back != 0]))
 
 
