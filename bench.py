@@ -256,6 +256,10 @@ def main():
     if not args.no_exchange:
         result["exchange"] = exchange_block(B, layer, inp["x"], cfg, M, b, stream)
         result["router_projection"] = router_block(B, synth, inp["x"], cfg, b, stream)
+        result["routing_variants"] = routing_variants_block(B, inp["logits"], cfg, cap, stream)
+        if cfg["act"] == "bf16" and d % 128 == 0:
+            result["fp8_payload"] = fp8_block(B, layer, inp["x"], cfg, M, stream,
+                                              args.cold_reps)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_sample_tokens)
     print(json.dumps(result))
@@ -340,6 +344,128 @@ def exchange_block(B, layer, src_x, cfg, M, b, stream):
         "tau_min_rows": tau_rows,
         "tau_min_bytes": tau_rows * row_bytes,
         "tau_min_us_at_xgmi_egress": tau_rows * row_bytes / (XGMI_EGRESS_GBPS * 1e9) * 1e6,
+    }
+
+
+def _timed(stream, fn, reps=5):
+    import torch
+
+    fn()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        fn()
+    e1.record(stream)
+    e1.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def routing_variants_block(B, logits, cfg, cap, stream):
+    """Sigmoid gate and one-round re-route of capacity overflow ("MoE
+    推理服务工程真相 2026", sections 2.3 and 4.3), timed alone on warm buffers.
+    A dropless workload is re-routed at the capacity of C = 1.0."""
+    import torch
+
+    N, E, K = cfg["N"], cfg["E"], cfg["K"]
+    c = cap if cap >= 0 else B.moe_capacity(1.0, N, K, E)
+    idx = torch.empty(N, K, dtype=torch.int32, device=logits.device)
+    w = torch.empty(N, K, dtype=torch.float32, device=logits.device)
+    t_soft = _timed(stream, lambda: B.moe_route_topk(logits, K, False, idx, w))
+    t_sig = _timed(stream, lambda: B.moe_route_topk(logits, K, False, idx, w, "sigmoid"))
+    ws = torch.empty(max(1, B.moe_reroute_workspace_bytes(N, E, K)), dtype=torch.uint8,
+                     device=logits.device)
+    rr = torch.empty(E, dtype=torch.int32, device=logits.device)
+    idx2, w2 = idx.clone(), w.clone()
+
+    def reroute():
+        idx2.copy_(idx)
+        w2.copy_(w)
+        B.moe_reroute_overflow(logits, idx2, w2, c, "softmax", False, rr, ws)
+
+    B.moe_route_topk(logits, K, False, idx, w)
+    t_copy = _timed(stream, lambda: (idx2.copy_(idx), w2.copy_(w)))
+    t_rr = _timed(stream, reroute)
+    demand = torch.bincount(idx.flatten().long(), minlength=E)
+    kept = int(torch.clamp(demand, max=c).sum())
+    admitted = int(rr.sum())
+    return {
+        "route_softmax_us": t_soft * 1e3,
+        "route_sigmoid_us": t_sig * 1e3,
+        "reroute_capacity": int(c),
+        "reroute_us": max(t_rr - t_copy, 0.0) * 1e3,
+        "dropped_without_reroute": N * K - kept,
+        "reroute_admitted": admitted,
+        "dropped_with_reroute": N * K - kept - admitted,
+    }
+
+
+def fp8_block(B, layer, x, cfg, M, stream, cold_reps):
+    """FP8 (e4m3, one fp32 scale per 128 columns) exchange payload ("MoE
+    推理服务工程真相 2026", section 6.3): the fp8 dispatch and combine timed
+    with a cold cache like the bf16 ones, the quantize / dequantize passes at
+    either end of an exchange timed warm, and the payload bytes per
+    exchange direction in bf16 and fp8."""
+    import numpy as np
+    import torch
+
+    N, d, E, K, W = cfg["N"], cfg["d"], cfg["E"], cfg["K"], cfg["W"]
+    cap = layer.capacity
+    dev = x.device
+    out8 = B.alloc_dispatch_fp8_outputs(N, d, E, K, W, dev)
+    n_rows = layer.disp["offsets"][E:E + 1]
+    y8 = torch.empty(N * K, d, dtype=torch.uint8, device=dev)
+    ys = torch.empty(N * K, d // 128, dtype=torch.float32, device=dev)
+    out = torch.empty(N, d, dtype=torch.bfloat16, device=dev)
+    xp = torch.empty(N * K, d, dtype=torch.bfloat16, device=dev)
+    B.moe_dispatch_fp8(x, layer.topk_idx, E, W, cap, out8)
+    B.moe_fp8_quantize_rows(layer.y_perm, n_rows, N * K, y8, ys)
+    torch.cuda.synchronize()
+
+    scrub = torch.empty(SCRUB_MIB << 18, dtype=torch.float32, device=dev)
+    cold = {}
+    fns = {
+        "dispatch": lambda: B.moe_dispatch_fp8(x, layer.topk_idx, E, W, cap, out8),
+        "combine": lambda: B.moe_combine_fp8(y8, ys, out8["dest"], layer.topk_w, out),
+    }
+    for name, fn in fns.items():
+        times = []
+        for i in range(max(cold_reps, 1)):
+            scrub.fill_(float(i))
+            scrub.sum()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            e1.synchronize()
+            times.append(e0.elapsed_time(e1))
+        cold[name] = float(np.median(times))
+    del scrub
+    t_q = _timed(stream, lambda: B.moe_fp8_quantize_rows(layer.y_perm, n_rows, N * K, y8, ys))
+    t_dq = _timed(stream, lambda: B.moe_fp8_dequantize_rows(out8["x8"], out8["x_scale"], n_rows,
+                                                            N * K, xp))
+    sb = M * (d // 128) * 4                        # scale bytes of M rows
+    disp_b = N * d * 2 + M * d + sb + 12 * N * K
+    comb_b = M * d + sb + N * d * 2 + 8 * N * K
+    q_b = M * d * 2 + M * d + sb
+    return {
+        "format": "OCP e4m3 codes, one fp32 scale per 128 columns",
+        "wire_bytes_per_direction_bf16": M * d * 2,
+        "wire_bytes_per_direction_fp8": M * d + sb,
+        "cold_dispatch_us": cold["dispatch"] * 1e3,
+        "cold_combine_us": cold["combine"] * 1e3,
+        "dispatch_bytes": disp_b,
+        "combine_bytes": comb_b,
+        "cold_dispatch_GBps": disp_b / (cold["dispatch"] * 1e-3) / 1e9,
+        "cold_combine_GBps": comb_b / (cold["combine"] * 1e-3) / 1e9,
+        "cold_dispatch_combine_GBps": (disp_b + comb_b) /
+                                      ((cold["dispatch"] + cold["combine"]) * 1e-3) / 1e9,
+        "quantize_rows_us": t_q * 1e3,
+        "quantize_rows_GBps": q_b / (t_q * 1e-3) / 1e9,
+        "dequantize_rows_us": t_dq * 1e3,
+        "dequantize_rows_GBps": q_b / (t_dq * 1e-3) / 1e9,
     }
 
 
