@@ -8,12 +8,15 @@
 //
 // Scheduling.  A one-block kernel turns offsets[] (which stays on the device)
 // into row tiles (expert, first row, end row) of at most BM rows of one
-// expert, plus each expert's first tile.  The GEMM grid is sized on the host
+// expert, and into per-XCD work lists: block b runs on XCD b % 8, each
+// expert's output-column tiles are dealt round-robin over the XCDs, and an
+// XCD runs, expert by expert, each of its column tiles with all of that
+// expert's row tiles, so the blocks resident on an XCD share one weight
+// tile and a few activation tiles through its L2 and every XCD gets the
+// same mix of full and ragged tiles.  The GEMM grid is sized on the host
 // from the upper bound max_rows; blocks beyond the real work exit at once.
-// Work is ordered expert-major, then output-column tile, then the expert's
-// row tiles, and renumbered so that each XCD (block b runs on XCD b % 8)
-// takes one contiguous run of that order: the blocks resident on an XCD
-// share one weight tile and a few token tiles through its L2.
+// The tiles of an XCD's partial last round are split along the reduction
+// (see map_unit).
 //
 // bf16 GEMM (gfx950 MFMA v_mfma_f32_32x32x16_bf16, fp32 accumulate).  Both
 // operands are contiguous along the reduction dimension (x_perm and h rows;
@@ -28,12 +31,14 @@
 //     pass loads 256 rows of Wd.
 //   4 waves; at BM = 256 each wave owns 128 tokens x 128 weight rows
 //     (16 accumulators of 32 x 32, 256 AGPRs).
-//   LDS: two stages of (256 + BM) rows x 128 bytes (128 KB at BM = 256);
-//     16-byte chunks XOR-swizzled by (row & 7) so the 8 lanes of an LDS read
-//     phase hit 8 different bank groups.
-//   pipeline: buffer loads of the next reduction tile are issued before the
-//     current tile's MFMAs (a scheduling barrier keeps them there), then
-//     written to the other LDS stage; one barrier per reduction tile.
+//   LDS: two activation stages and a ring of three 32 KB weight slots (160
+//     KB at BM = 256), filled by direct-to-LDS buffer loads; 16-byte chunks
+//     XOR-swizzled by (row / 2) & 7, which keeps the 16 lanes of an LDS read
+//     phase on 16 different bank groups.  Tiles of at most 32 rows use
+//     four-deep rings for both operands instead.
+//   pipeline: the next tiles' loads and the next step's operand reads are
+//     interleaved one by one with the MFMAs (scheduling fences keep the
+//     order); one fence-free barrier per reduction tile.
 // fp32 path: a plain LDS-tiled FMA kernel (64 x 64 tiles), used for fp32
 // layers, which are small.
 #include "moe_internal.h"
