@@ -39,8 +39,11 @@ FFN_SOURCE = os.path.join(ROOT, "grouped_gemm_route_amd", "csrc", "grouped_ffn.h
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=5)
+    # the GEMM's clock settles over the first ~10 layer steps; 20 untimed
+    # steps put the timed ones in steady state (the timed region stays well
+    # under a second)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", default=DEFAULT_WORKLOAD)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample-tokens", type=int, default=4096)

@@ -20,7 +20,14 @@ constexpr int kPiecesPerGroup = kFp8Group / kPiece;
 __device__ __forceinline__ void decode16(const uint4 raw, float scale, float* f) {
   const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
-  for (int i = 0; i < 16; ++i) f[i] = e4m3_decode((w[i / 4] >> (8 * (i % 4))) & 0xFFu) * scale;
+  for (int i = 0; i < 4; ++i) {
+    const f32x2 a = e4m3_decode2<false>(w[i]);
+    const f32x2 b = e4m3_decode2<true>(w[i]);
+    f[4 * i + 0] = a.x * scale;
+    f[4 * i + 1] = a.y * scale;
+    f[4 * i + 2] = b.x * scale;
+    f[4 * i + 3] = b.y * scale;
+  }
 }
 
 __device__ __forceinline__ void store_bf16x16(uint4* dst, const float* f) {

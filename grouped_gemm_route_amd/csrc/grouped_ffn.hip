@@ -34,8 +34,8 @@
 //   LDS: two activation stages and a ring of three 32 KB weight slots (160
 //     KB at BM = 256), filled by direct-to-LDS buffer loads; 16-byte chunks
 //     XOR-swizzled by (row / 2) & 7, which keeps the 16 lanes of an LDS read
-//     phase on 16 different bank groups.  Tiles of at most 32 rows use
-//     four-deep rings for both operands instead.
+//     phase on 16 different bank groups.  Tiles of at most 64 rows (32 at
+//     BM = 32) use four-deep rings for both operands instead.
 //   pipeline: the next tiles' loads and the next step's operand reads are
 //     interleaved one by one with the MFMAs (scheduling fences keep the
 //     order); one fence-free barrier per reduction tile.
@@ -309,13 +309,16 @@ struct TileGeo {
   static constexpr int kWLoads = kBW / (8 * NW);
   static constexpr int kALoads = BM / (8 * NW);
   static constexpr size_t kMainLds = (size_t)kWRegion + 3 * (size_t)kWSlotBytes;
-  // Thin tiles (at most 32 token rows: an expert's ragged last tile, or every
-  // tile of a decode-sized layer) do a few MFMAs per reduction tile and would
-  // wait on load latency, so they use rings four deep for both operands,
-  // loaded three reduction tiles ahead: 32-row activation slots, then
-  // four weight slots.  A thin activation slot is one load per wave.
-  static constexpr bool kThin = NW * 8 == 32;
-  static constexpr int kThinABytes = 32 * kRowBytes;
+  // Thin tiles (at most kThinRows token rows: an expert's ragged last tile,
+  // or every tile of a decode-sized layer) do few MFMAs per reduction tile
+  // and would wait on load latency, so they use rings four deep for both
+  // operands, loaded three reduction tiles ahead: kThinRows-row activation
+  // slots, then four weight slots (160 KB with 64-row slots, 144 KB with
+  // 32).  A thin activation slot is kThinALoads loads per wave.
+  static constexpr int kThinRows = BM >= 128 ? 64 : 32;
+  static constexpr bool kThin = NW == 4 && kThinRows <= BM / WM;
+  static constexpr int kThinALoads = kThinRows / (8 * NW);
+  static constexpr int kThinABytes = kThinRows * kRowBytes;
   static constexpr int kThinWRegion = 4 * kThinABytes;
   static constexpr size_t kThinLds = (size_t)kThinWRegion + 4 * (size_t)kWSlotBytes;
   static constexpr size_t kLds = kThin && kThinLds > kMainLds ? kThinLds : kMainLds;
@@ -604,16 +607,24 @@ __global__ __launch_bounds__(NW * kWave, 1) void ffn_gemm_bf16_kernel(
   // the last step the wave waits until only the loads of tiles kt + 2 and
   // kt + 3 may be outstanding, then meets the others at the barrier, as
   // above.
+  using TA = std::integral_constant<int, G::kThinALoads>;
+  auto thin_wait = []() __attribute__((always_inline)) {
+    // the loads of two tiles, 2 x (kThinALoads + 8) per wave, may be in flight
+    if constexpr (G::kThinALoads == 2)
+      asm volatile("s_waitcnt vmcnt(20)" ::: "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
+  };
   auto thin_step = [&](auto jn_c, int kt, int u) __attribute__((always_inline)) {
     const int k3 = min(kt + 3, nk - 1) * kBK;
     const int ao = u * G::kThinABytes, wo = G::kThinWRegion + u * G::kWSlotBytes;
     const int u1 = (u + 1) & 3, u3 = (u + 3) & 3;
     const int ao3 = u3 * G::kThinABytes, wo3 = G::kThinWRegion + u3 * G::kWSlotBytes;
-    mfma_step(jn_c, IC0{}, ICW{}, YES{}, IC0{}, IC1{}, IC0{}, IC0{}, 0, ao, wo, 1, 1, ao3, k3, 0, 0);
+    mfma_step(jn_c, IC0{}, ICW{}, YES{}, IC0{}, TA{}, IC0{}, IC0{}, 0, ao, wo, 1, 1, ao3, k3, 0, 0);
     mfma_step(jn_c, IC0{}, ICW{}, YES{}, IC0{}, IC0{}, IC0{}, WA{}, 1, ao, wo, 2, 0, 0, 0, wo3, k3);
     mfma_step(jn_c, IC0{}, ICW{}, YES{}, IC0{}, IC0{}, IC0{}, IC0{}, 0, ao, wo, 3, 1, 0, 0, 0, 0);
     mfma_step(jn_c, IC0{}, ICH{}, NO{}, IC0{}, IC0{}, IC0{}, IC0{}, 1, 0, 0, 0, 0, 0, 0, 0, 0);
-    asm volatile("s_waitcnt vmcnt(18)" ::: "memory");  // 2 tiles x (1 + 8) loads
+    thin_wait();
     fence_free_barrier();
     mfma_step(jn_c, ICH{}, ICW{}, YES{}, IC0{}, IC0{}, IC0{}, IC0{}, 1, u1 * G::kThinABytes,
               G::kThinWRegion + u1 * G::kWSlotBytes, 0, 0, 0, 0, 0, 0);
@@ -624,12 +635,13 @@ __global__ __launch_bounds__(NW * kWave, 1) void ffn_gemm_bf16_kernel(
 #pragma unroll
     for (int t = 0; t < 3; ++t) {
       const int k0 = min(t, nk - 1) * kBK;
-      issue_aload(t * G::kThinABytes, k0, 0);
+#pragma unroll
+      for (int l = 0; l < G::kThinALoads; ++l) issue_aload(t * G::kThinABytes, k0, l);
 #pragma unroll
       for (int l = 0; l < G::kWLoads; ++l)
         issue_wload(G::kThinWRegion + t * G::kWSlotBytes, k0, l);
     }
-    asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
+    thin_wait();
     fence_free_barrier();
     constexpr int JN = decltype(jn_c)::value;
 #pragma unroll
@@ -640,9 +652,11 @@ __global__ __launch_bounds__(NW * kWave, 1) void ffn_gemm_bf16_kernel(
 
   constexpr int kTM = G::kTM;
   if constexpr (G::kThin) {
-    if (rows <= 32) {
-      // only the first 32-token subtile of wave row 0 holds rows
-      if (jlim >= 1)
+    if (rows <= G::kThinRows) {
+      // only the first kThinRows / 32 token subtiles of wave row 0 hold rows
+      if (G::kThinRows > 32 && jlim >= 2)
+        thin_loop(std::integral_constant<int, (G::kThinRows > 32 ? 2 : 1)>{});
+      else if (jlim >= 1)
         thin_loop(IC1{});
       else
         thin_loop(IC0{});

@@ -26,6 +26,7 @@ def _rows(R, d, seed):
     """bf16 rows whose 128-column groups span many magnitudes, with zero
     groups, negative zeros and values that land in the subnormal codes."""
     g = torch.Generator().manual_seed(seed)
+    g_sign = torch.Generator().manual_seed(seed + 1)
     x = torch.randn(R, d, generator=g)
     mag = 10.0 ** torch.randint(-6, 5, (R, d // 128), generator=g).float()
     x = x * mag.repeat_interleave(128, dim=1)
@@ -34,6 +35,14 @@ def _rows(R, d, seed):
     x[3, :] = x[3, :] * 1e-3
     x[3, 0] = 50.0                               # most of the group in subnormal codes
     x[4, 256:384] *= 1e-32                       # below 2^-100: zero codes
+    if R > 5:
+        # a group whose maximum is 448 (scale 1): every value is an exact
+        # e4m3 value or the midpoint of two, so rounding ties decide the codes
+        t = torch.tensor(O.e4m3_value(np.arange(0x7F)))
+        mids = (t[1:] + t[:-1]) / 2
+        g = torch.cat([t, mids])[torch.randperm(2 * 0x7F - 1, generator=g)[:127]]
+        g = g * torch.where(torch.rand(127, generator=g_sign) < 0.5, -1.0, 1.0)
+        x[5, :128] = torch.cat([torch.tensor([448.0]), g])
     return x.to(torch.bfloat16)
 
 
