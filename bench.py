@@ -297,6 +297,7 @@ def routing_metrics(layer, cfg, cap, M):
         "expert_overflow_rate": float((demand > cap).mean()) if cap >= 0 else 0.0,
         "nonempty_experts": int((counts > 0).sum()),
         "max_rows_per_expert": int(counts.max()),
+        "expert_rows": counts.tolist() if E <= 16 else None,
         "rank_load_std_over_mean": float(per_rank.std() / max(per_rank.mean(), 1e-9)),
         "rank_load_max_over_min": float(per_rank.max() / max(per_rank.min(), 1)),
     }

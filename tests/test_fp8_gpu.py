@@ -74,6 +74,39 @@ def test_quantize_and_dequantize_rows_match_oracle(R, d, n):
     assert (_np(back)[n:] == 7.0).all()
 
 
+def test_every_code_and_every_tie():
+    # groups whose maximum is 448 (scale 1) holding every finite e4m3 value
+    # and every midpoint of neighbours, both signs: each code decision is a
+    # table hit or an exact tie; then every code is decoded with scale 1
+    t = O.e4m3_value(np.arange(0x7F))
+    vals = np.concatenate([t, (t[1:] + t[:-1]) / 2])
+    vals = np.concatenate([vals, -vals])
+    per = 127
+    n_groups = -(-len(vals) // per)
+    rows = np.zeros((n_groups, 128), np.float32)
+    rows[:, 0] = 448.0
+    flat = np.zeros(n_groups * per, np.float32)
+    flat[:len(vals)] = vals
+    rows[:, 1:] = flat.reshape(n_groups, per)
+    x = torch.from_numpy(rows).to(torch.bfloat16)
+    assert np.array_equal(x.float().numpy(), rows)              # exact in bf16
+    xd = x.to(DEV)
+    n = torch.tensor([n_groups], dtype=torch.int32, device=DEV)
+    q, s = B.moe_fp8_quantize_rows(xd, n)
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8).reshape(2, 128).to(DEV)
+    ones = torch.ones(2, 1, dtype=torch.float32, device=DEV)
+    back = B.moe_fp8_dequantize_rows(codes, ones, torch.tensor([2], dtype=torch.int32,
+                                                               device=DEV))
+    torch.cuda.synchronize()
+    rq, rs = O.quantize_fp8(rows)
+    assert np.array_equal(_np(q), rq) and np.array_equal(_np(s), rs)
+    ref = O.e4m3_value(np.arange(256)).reshape(2, 128)
+    got = _np(back).astype(np.float64)
+    finite = ~np.isnan(ref)
+    assert np.array_equal(got[finite], ref[finite])             # each value exact in bf16
+    assert np.isnan(got[~finite]).all()
+
+
 def _fp8_dispatch(cfg, cap):
     inp = synth.make_inputs(cfg, DEV, weights=False)
     idx, w = B.moe_route_topk(inp["logits"], cfg["K"])
