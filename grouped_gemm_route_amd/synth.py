@@ -44,6 +44,12 @@ CONFIGS = {
                            act="bf16", bias="hot", hot_bias=4.0, C=None),
     "prefill256_hot_c1.0": dict(N=32768, d=7168, ffn=2048, E=256, K=8, W=8,
                                 act="bf16", bias="hot", hot_bias=4.0, C=1.0),
+    # the same hot set with the bias that puts ~70% of assignments on it
+    # (70.1% with these seeds), the share the skewed-prefill workload names
+    "prefill256_cal": dict(N=32768, d=7168, ffn=2048, E=256, K=8, W=8,
+                           act="bf16", bias="hot", hot_bias=1.2, C=None),
+    "prefill256_cal_c1.0": dict(N=32768, d=7168, ffn=2048, E=256, K=8, W=8,
+                                act="bf16", bias="hot", hot_bias=1.2, C=1.0),
 }
 
 TORCH_DTYPE = {"bf16": torch.bfloat16, "f32": torch.float32}

@@ -230,9 +230,10 @@ def test_identity_ffn_round_trip_is_bitwise():
 # full-size layers: full route/dispatch, sampled FFN and combine
 # ---------------------------------------------------------------------------
 
-FULL = ["dense8", "fine128_zipf_c1.25", "decode256", "prefill256_hot", "prefill256_hot_c1.0"]
+FULL = ["dense8", "fine128_zipf_c1.25", "decode256", "prefill256_hot", "prefill256_hot_c1.0",
+        "prefill256_cal", "prefill256_cal_c1.0"]
 SAMPLES = {"dense8": 6, "fine128_zipf_c1.25": 8, "decode256": 4, "prefill256_hot": 4,
-           "prefill256_hot_c1.0": 4}
+           "prefill256_hot_c1.0": 4, "prefill256_cal": 4, "prefill256_cal_c1.0": 4}
 
 
 @pytest.mark.parametrize("name", FULL)
