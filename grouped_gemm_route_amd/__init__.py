@@ -6,6 +6,7 @@ include/moe_route.h); ``binding`` marshals torch tensors into its calls.
 from .binding import (  # noqa: F401
     MoeError,
     MoeLayer,
+    PackedFfnWeights,
     load_library,
     moe_abi_version,
     moe_capacity,
@@ -19,7 +20,10 @@ from .binding import (  # noqa: F401
     moe_fp8_dequantize_rows,
     moe_fp8_quantize_rows,
     moe_grouped_ffn,
+    moe_grouped_ffn_packed,
     moe_grouped_ffn_workspace_bytes,
+    moe_pack_ffn_weights,
+    moe_packed_ffn_weight_bytes,
     moe_reroute_overflow,
     moe_reroute_workspace_bytes,
     moe_route_topk,

@@ -40,6 +40,10 @@ SIGNATURES = [
     ("moe_grouped_ffn_workspace_bytes", _SZ, [_I64, _I32, _I32]),
     ("moe_grouped_ffn", ctypes.c_int,
      [_P, _I32, _I32, _I32, _I32, _P, _I64, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    ("moe_packed_ffn_weight_bytes", _SZ, [_I32, _I32, _I32, _I32]),
+    ("moe_pack_ffn_weights", ctypes.c_int, [_P, _P, _P, _I32, _I32, _I32, _P, _P, _P]),
+    ("moe_grouped_ffn_packed", ctypes.c_int,
+     [_P, _I32, _I32, _I32, _P, _I64, _P, _P, _P, _P, _P, _SZ, _P]),
     ("moe_combine", ctypes.c_int, [_P, _I32, _I32, _I32, _I32, _P, _P, _P, _P]),
     ("moe_router_logits", ctypes.c_int, [_P, _I32, _I32, _I32, _P, _I32, _P, _P]),
     ("moe_exchange_workspace_bytes", _SZ, [_I32, _I32]),
@@ -420,6 +424,79 @@ def moe_grouped_ffn(x_perm, offsets, w_gate, w_up, w_down, max_rows=None, h=None
     return h, y_perm
 
 
+MOE_FFN_GATE_UP, MOE_FFN_DOWN = 0, 1
+
+
+def moe_packed_ffn_weight_bytes(E, d, ffn, part):
+    return int(load_library().moe_packed_ffn_weight_bytes(E, d, ffn, part))
+
+
+class PackedFfnWeights:
+    """bf16 expert weights packed by moe_pack_ffn_weights (byte tensors up
+    and down, for E experts of d x ffn)."""
+
+    def __init__(self, up, down, E, d, ffn):
+        self.up, self.down, self.E, self.d, self.ffn = up, down, E, d, ffn
+
+
+def moe_pack_ffn_weights(w_gate, w_up, w_down):
+    """Pack bf16 w_gate/w_up [E, ffn, d] and w_down [E, d, ffn] for
+    moe_grouped_ffn_packed (once, at weight-load time)."""
+    E, ffn, d = w_gate.shape
+    if tuple(w_up.shape) != (E, ffn, d) or tuple(w_down.shape) != (E, d, ffn):
+        raise ValueError("weights must be w_gate/w_up [E, ffn, d] and w_down [E, d, ffn]")
+    dev = w_gate.device
+    for name, t in (("w_gate", w_gate), ("w_up", w_up), ("w_down", w_down)):
+        _need(t, name, torch.bfloat16, dev)
+    nu = moe_packed_ffn_weight_bytes(E, d, ffn, MOE_FFN_GATE_UP)
+    nd = moe_packed_ffn_weight_bytes(E, d, ffn, MOE_FFN_DOWN)
+    if nu == 0 or nd == 0:
+        raise ValueError(f"cannot pack d={d} ffn={ffn}: both must be multiples of 64")
+    up = torch.empty(nu, dtype=torch.uint8, device=dev)
+    down = torch.empty(nd, dtype=torch.uint8, device=dev)
+    _check("moe_pack_ffn_weights", load_library().moe_pack_ffn_weights(
+        _ptr(w_gate), _ptr(w_up), _ptr(w_down), E, d, ffn, _ptr(up), _ptr(down),
+        _stream(w_gate)))
+    return PackedFfnWeights(up, down, E, d, ffn)
+
+
+def moe_grouped_ffn_packed(x_perm, offsets, packed, max_rows=None, h=None, y_perm=None,
+                           workspace=None):
+    """moe_grouped_ffn on weights packed by moe_pack_ffn_weights; returns
+    (h, y_perm)."""
+    _need(x_perm, "x_perm", torch.bfloat16)
+    dev = x_perm.device
+    E, d, ffn = packed.E, packed.d, packed.ffn
+    if x_perm.shape[1] != d:
+        raise ValueError("x_perm rows must have d columns")
+    _need(packed.up, "packed.up", torch.uint8, dev)
+    _need(packed.down, "packed.down", torch.uint8, dev)
+    _need(offsets, "offsets", torch.int32, dev)
+    if offsets.numel() != E + 1:
+        raise ValueError("offsets must have E+1 entries")
+    if max_rows is None:
+        max_rows = x_perm.shape[0]
+    if x_perm.shape[0] < max_rows:
+        raise ValueError("x_perm must have at least max_rows rows")
+    if h is None:
+        h = torch.empty(max_rows, ffn, dtype=x_perm.dtype, device=dev)
+    if y_perm is None:
+        y_perm = torch.empty(max_rows, d, dtype=x_perm.dtype, device=dev)
+    _need(h, "h", x_perm.dtype, dev)
+    _need(y_perm, "y_perm", x_perm.dtype, dev)
+    if h.numel() < max_rows * ffn or y_perm.numel() < max_rows * d:
+        raise ValueError("h / y_perm too small for max_rows")
+    if workspace is None:
+        workspace = torch.empty(max(1, moe_grouped_ffn_workspace_bytes(max_rows, E, x_perm.dtype)),
+                                dtype=torch.uint8, device=dev)
+    _need(workspace, "workspace", None, dev)
+    _check("moe_grouped_ffn_packed", load_library().moe_grouped_ffn_packed(
+        _ptr(x_perm), d, ffn, E, _ptr(offsets), int(max_rows), _ptr(packed.up),
+        _ptr(packed.down), _ptr(h), _ptr(y_perm), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(x_perm)))
+    return h, y_perm
+
+
 def moe_combine(y_perm, dest, topk_w, out=None):
     """Weighted merge back to token order; returns out [N, d]."""
     _need(y_perm, "y_perm")
@@ -565,7 +642,12 @@ class MoeLayer:
                                 self.disp["x_perm"])
         return self.disp
 
-    def ffn(self, w_gate, w_up, w_down):
+    def ffn(self, w_gate, w_up=None, w_down=None):
+        """w_gate, w_up, w_down: the weights, or w_gate alone: PackedFfnWeights
+        from moe_pack_ffn_weights (bf16 layers)."""
+        if isinstance(w_gate, PackedFfnWeights):
+            return moe_grouped_ffn_packed(self.disp["x_perm"], self.disp["offsets"], w_gate,
+                                          self.max_rows, self.h, self.y_perm, self.ffn_ws)
         return moe_grouped_ffn(self.disp["x_perm"], self.disp["offsets"], w_gate, w_up, w_down,
                                self.max_rows, self.h, self.y_perm, self.ffn_ws)
 
@@ -576,7 +658,7 @@ class MoeLayer:
         moe_fp8_quantize_rows(self.y_perm, n_rows, self.max_rows, self.y8, self.y_scale)
         return moe_combine_fp8(self.y8, self.y_scale, self.disp["dest"], self.topk_w, self.out)
 
-    def forward(self, logits, x, w_gate, w_up, w_down):
+    def forward(self, logits, x, w_gate, w_up=None, w_down=None):
         self.route(logits)
         self.dispatch(x)
         self.ffn(w_gate, w_up, w_down)

@@ -314,6 +314,65 @@ int moe_grouped_ffn(const void* x_perm, int32_t dtype, int32_t d, int32_t ffn,
       "moe_grouped_ffn");
 }
 
+// Size checks shared by the packed-weight entry points: the packed matrices
+// of one expert (plus the 3 panels a block's last waves may point past them)
+// must stay below 2 GiB, the kernel's 32-bit per-lane offsets.
+static int packed_shape_checks(const char* fn, int32_t E, int32_t d, int32_t ffn) {
+  if (E < 1 || d < 1 || ffn < 1)
+    return fail(MOE_ERR_INVALID_ARG, "%s: need E, d, ffn >= 1", fn);
+  if (E > MOE_MAX_EXPERTS)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: E <= %d supported", fn, MOE_MAX_EXPERTS);
+  if (d % 64 != 0 || ffn % 64 != 0)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: d and ffn must be multiples of 64 (d=%d ffn=%d)", fn,
+                d, ffn);
+  const int64_t up = (int64_t)(moe::packed_panels(d, ffn, true) + 3) * (d / 16) * 4096;
+  const int64_t dn = (int64_t)(moe::packed_panels(d, ffn, false) + 3) * (ffn / 16) * 4096;
+  if (up >= ((int64_t)1 << 31) || dn >= ((int64_t)1 << 31))
+    return fail(MOE_ERR_UNSUPPORTED, "%s: one expert's packed weights must stay below 2 GiB (d=%d ffn=%d)",
+                fn, d, ffn);
+  return MOE_OK;
+}
+
+size_t moe_packed_ffn_weight_bytes(int32_t E, int32_t d, int32_t ffn, int32_t part) {
+  if (E < 1 || d < 1 || ffn < 1 || d % 64 != 0 || ffn % 64 != 0) return 0;
+  if (part != MOE_FFN_GATE_UP && part != MOE_FFN_DOWN) return 0;
+  return moe::packed_ffn_weight_bytes(E, d, ffn, part == MOE_FFN_GATE_UP);
+}
+
+int moe_pack_ffn_weights(const void* w_gate, const void* w_up, const void* w_down,
+                         int32_t E, int32_t d, int32_t ffn, void* packed_up,
+                         void* packed_down, void* stream) {
+  if (!w_gate || !w_up || !w_down || !packed_up || !packed_down)
+    return fail(MOE_ERR_INVALID_ARG, "moe_pack_ffn_weights: null pointer");
+  const int rc = packed_shape_checks("moe_pack_ffn_weights", E, d, ffn);
+  if (rc != MOE_OK) return rc;
+  return hip_status(moe::launch_pack_ffn_weights(w_gate, w_up, w_down, E, d, ffn, packed_up,
+                                                 packed_down, as_stream(stream)),
+                    "moe_pack_ffn_weights");
+}
+
+int moe_grouped_ffn_packed(const void* x_perm, int32_t d, int32_t ffn, int32_t E,
+                           const int32_t* offsets, int64_t max_rows, const void* packed_up,
+                           const void* packed_down, void* h, void* y_perm, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  if (!x_perm || !offsets || !packed_up || !packed_down || !h || !y_perm)
+    return fail(MOE_ERR_INVALID_ARG, "moe_grouped_ffn_packed: null pointer");
+  if (max_rows < 0)
+    return fail(MOE_ERR_INVALID_ARG, "moe_grouped_ffn_packed: need max_rows >= 0");
+  const int rc = packed_shape_checks("moe_grouped_ffn_packed", E, d, ffn);
+  if (rc != MOE_OK) return rc;
+  if (max_rows >= ((int64_t)1 << 31))
+    return fail(MOE_ERR_UNSUPPORTED, "moe_grouped_ffn_packed: max_rows must be below 2^31");
+  if (max_rows == 0) return MOE_OK;
+  const size_t need = moe::grouped_ffn_workspace_bytes(max_rows, E, true);
+  if (!workspace || workspace_bytes < need)
+    return fail(MOE_ERR_WORKSPACE, "moe_grouped_ffn_packed: workspace needs %zu bytes", need);
+  return hip_status(moe::launch_grouped_ffn_packed(x_perm, d, ffn, E, offsets, max_rows,
+                                                   packed_up, packed_down, h, y_perm,
+                                                   workspace, as_stream(stream)),
+                    "moe_grouped_ffn_packed");
+}
+
 int moe_combine(const void* y_perm, int32_t dtype, int32_t N, int32_t d,
                 int32_t K, const int32_t* dest, const float* topk_w, void* out,
                 void* stream) {

@@ -6,17 +6,9 @@
 // padding of the token count.  Per expert e on rows R = x_perm[offsets[e] :
 // offsets[e+1]]:  h = silu(R Wg[e]^T) * (R Wu[e]^T);  y = h Wd[e]^T.
 //
-// Scheduling.  A one-block kernel turns offsets[] (which stays on the device)
-// into row tiles (expert, first row, end row) of at most BM rows of one
-// expert, and into per-XCD work lists: block b runs on XCD b % 8, each
-// expert's output-column tiles are dealt round-robin over the XCDs, and an
-// XCD runs, expert by expert, each of its column tiles with all of that
-// expert's row tiles, so the blocks resident on an XCD share one weight
-// tile and a few activation tiles through its L2 and every XCD gets the
-// same mix of full and ragged tiles.  The GEMM grid is sized on the host
-// from the upper bound max_rows; blocks beyond the real work exit at once.
-// The tiles of an XCD's partial last round are split along the reduction
-// (see map_unit).
+// Weights in their row-major layout ([E, ffn, d] gate and up, [E, d, ffn]
+// down).  Tiles are scheduled as in ffn_tiles.h; grouped_ffn_packed.hip
+// holds the variant for weights packed in MFMA operand order.
 //
 // bf16 GEMM (gfx950 MFMA v_mfma_f32_32x32x16_bf16, fp32 accumulate).  Both
 // operands are contiguous along the reduction dimension (x_perm and h rows;
@@ -41,8 +33,7 @@
 //     order); one fence-free barrier per reduction tile.
 // fp32 path: a plain LDS-tiled FMA kernel (64 x 64 tiles), used for fp32
 // layers, which are small.
-#include "moe_internal.h"
-#include "block_scan.h"
+#include "ffn_tiles.h"
 
 #include <mutex>
 #include <type_traits>
@@ -53,244 +44,10 @@ namespace {
 constexpr int kThreads = 256;
 
 // ---------------------------------------------------------------------------
-// tile schedule
-// ---------------------------------------------------------------------------
-
-// Split reduction.  A block-tile grid rarely divides evenly among the
-// resident block slots (one block per CU): the 576 blocks of an 8-expert
-// down projection over 8192 rows with d = 4096 fill 256 CUs twice and then a
-// quarter of them.  The tiles of such a last, partial round are split along
-// the reduction into up to kMaxSplit pieces, so that the round fills the
-// chip; each piece writes its fp32 accumulators to a workspace slot and the
-// last piece to finish adds the pieces up in piece order (a fixed order, so
-// results do not depend on which piece finishes last) and stores the tile.
-constexpr int kMaxSplitUnits = 256;  // split pieces per launch (block slots)
-constexpr int kMaxSplit = 8;         // pieces per tile
-constexpr int kMinSplitTiles = 8;    // reduction tiles per piece, at least
-
-// Workspace layout: [num_tiles | pad to 256 B][split counters: 2 x
-// kMaxSplitUnits ints][XCD block tables: 2 passes x 8 XCDs x (E+1) ints |
-// pad][tile_start[E+1] | pad][tiles | pad][split partials].
-struct FfnWorkspace {
-  int* num_tiles;
-  int* split_cnt;   // arrival counters of split tiles: gate/up pass, then down
-  int* xcd_start;   // [pass][xcd][E+1]: the XCD's blocks for experts < e
-  int* tile_start;  // tiles of expert e are slots [tile_start[e], tile_start[e+1])
-  int4* tiles;      // (expert, first row, end row, 0)
-  float* partial;   // kMaxSplitUnits fp32 accumulator tiles of BM x 256
-};
-
-constexpr int kXcds = 8;  // block b runs on XCD b % 8
-constexpr size_t kSplitCntBytes = 2 * kMaxSplitUnits * sizeof(int);
-
-inline size_t ffn_xcd_table_bytes(int E) {
-  return align_up((size_t)2 * kXcds * (E + 1) * sizeof(int), 256);
-}
-
-inline size_t ffn_tiles_offset(int E) {
-  return 256 + kSplitCntBytes + ffn_xcd_table_bytes(E) +
-         align_up((size_t)(E + 1) * sizeof(int), 256);
-}
-
-inline FfnWorkspace ffn_workspace(void* base, int E, int max_tiles) {
-  char* p = static_cast<char*>(base);
-  FfnWorkspace ws;
-  ws.num_tiles = reinterpret_cast<int*>(p);
-  ws.split_cnt = reinterpret_cast<int*>(p + 256);
-  ws.xcd_start = reinterpret_cast<int*>(p + 256 + kSplitCntBytes);
-  ws.tile_start = reinterpret_cast<int*>(p + 256 + kSplitCntBytes + ffn_xcd_table_bytes(E));
-  ws.tiles = reinterpret_cast<int4*>(p + ffn_tiles_offset(E));
-  ws.partial = reinterpret_cast<float*>(
-      p + ffn_tiles_offset(E) + align_up((size_t)max_tiles * sizeof(int4), 256));
-  return ws;
-}
-
-// Column tiles n of expert e that XCD x runs: n = xcd_first_n(e, x, n) + 8 k.
-// Expert e's column tiles are dealt round-robin over the XCDs, continuing
-// where expert e - 1 stopped, so every XCD gets about the same share of
-// every expert (of its thin and full row tiles alike).
-__device__ __forceinline__ int xcd_first_n(int e, int x, int n_tiles) {
-  const int start = ((e % kXcds) * (n_tiles % kXcds)) % kXcds;  // (e * n_tiles) % 8
-  return (x - start + kXcds) % kXcds;
-}
-__device__ __forceinline__ int xcd_groups(int e, int x, int n_tiles) {
-  const int f = xcd_first_n(e, x, n_tiles);
-  return f < n_tiles ? (n_tiles - f + kXcds - 1) / kXcds : 0;
-}
-
-__global__ __launch_bounds__(1024) void ffn_schedule_kernel(
-    const int32_t* __restrict__ offsets, int E, int tile_rows, int max_rows,
-    int max_tiles, int n_up, int n_dn, int4* __restrict__ tiles,
-    int* __restrict__ tile_start, int* __restrict__ num_tiles,
-    int* __restrict__ split_cnt, int* __restrict__ xcd_start) {
-  __shared__ int wave_sums[1024 / kWave];
-  const int e = threadIdx.x;
-  if (e < 2 * kMaxSplitUnits) split_cnt[e] = 0;
-  int a = 0, b = 0, nt = 0;
-  if (e < E) {
-    a = min(max(offsets[e], 0), max_rows);
-    b = min(max(offsets[e + 1], a), max_rows);
-    nt = (b - a + tile_rows - 1) / tile_rows;
-  }
-  int total = 0;
-  const int base = block_exclusive_scan(nt, wave_sums, &total);
-  if (e < E) tile_start[e] = min(base, max_tiles);
-  if (e == 0) tile_start[E] = min(total, max_tiles);
-  for (int i = 0; i < nt; ++i) {
-    const int slot = base + i;
-    if (slot < max_tiles) {
-      const int r0 = a + i * tile_rows;
-      tiles[slot] = make_int4(e, r0, min(b, r0 + tile_rows), 0);
-    }
-  }
-  if (e == 0) *num_tiles = min(total, max_tiles);
-  // Per pass and XCD, the exclusive scan over experts of the XCD's blocks:
-  // wave w < 16 scans the table of pass w / 8 and XCD w % 8, 64 experts at
-  // a time.
-  __shared__ int cnt_s[1024];
-  cnt_s[e] = e < E ? min(base + nt, max_tiles) - min(base, max_tiles) : 0;
-  __syncthreads();
-  const int wave = e / kWave, lane = e % kWave;
-  if (wave < 2 * kXcds) {
-    const int x = wave % kXcds;
-    const int n_tiles = wave < kXcds ? n_up : n_dn;
-    int* P = xcd_start + wave * (E + 1);
-    int run = 0;
-    for (int c = 0; c < E; c += kWave) {
-      const int ee = c + lane;
-      const int v = ee < E ? xcd_groups(ee, x, n_tiles) * cnt_s[ee] : 0;
-      int incl = v;
-#pragma unroll
-      for (int off = 1; off < kWave; off <<= 1) {
-        const int o = __shfl_up(incl, off);
-        if (lane >= off) incl += o;
-      }
-      if (ee < E) P[ee] = run + incl - v;
-      run += __shfl(incl, kWave - 1);
-    }
-    if (lane == 0) P[E] = run;
-  }
-}
-
-inline int max_tiles_for(int64_t max_rows, int E, int tile_rows) {
-  return (int)((max_rows + tile_rows - 1) / tile_rows +
-               (max_rows < E ? max_rows : E));
-}
-
-// Block -> (tile slot, output column tile).  The first round_up(total, 8)
-// blocks carry work; block b runs on XCD b % 8, so blocks are renumbered to
-// give every XCD one contiguous run of the work order.  The work order is
-// expert-major, then column tile, then the expert's row tiles, so the blocks
-// that an XCD runs together read the same weight tile and the same few row
-// tiles from its L2.  Returns false for blocks without work.
-__device__ __forceinline__ bool map_block(const int* __restrict__ tile_start,
-                                          const int* __restrict__ num_tiles_p,
-                                          int E, int n_tiles, int* slot,
-                                          int* n_tile) {
-  const int total = n_tiles * *num_tiles_p;
-  const int per_xcd = (total + 7) / 8;
-  const int b = blockIdx.x;
-  if (b >= per_xcd * 8) return false;
-  const int L = (b % 8) * per_xcd + b / 8;
-  if (L >= total) return false;
-  int lo = 0, hi = E;  // largest e with n_tiles * tile_start[e] <= L
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (n_tiles * tile_start[mid] <= L) lo = mid; else hi = mid;
-  }
-  const int first = tile_start[lo];
-  const int cnt = tile_start[lo + 1] - first;
-  const int r = L - n_tiles * first;
-  *n_tile = r / cnt;
-  *slot = first + r % cnt;
-  return true;
-}
-
-// Work unit of a bf16 GEMM block: a tile slot and column tile, and the range
-// [kb, ke) of reduction tiles.  For a piece of a split tile, split >= 0
-// numbers the tile's arrival counter, the tile is piece `piece` of `parts`
-// and its pieces' partials go to workspace slots pslot0 + 0 .. parts - 1.
-struct Unit {
-  int slot, n_tile, kb, ke, split, piece, parts, pslot0;
-};
-
-// Block -> work unit.  Block b runs on XCD x = b % 8 as that XCD's block
-// i = b / 8.  XCD x works through its own list: expert by expert, its share
-// of the expert's column tiles (dealt round-robin, see xcd_first_n), and
-// for each column tile all of the expert's row tiles, so that the blocks an
-// XCD runs together share one weight tile and a few activation tiles
-// through its L2.  xcd_start (the XCD's row of the schedule's table) gives
-// the list position of each expert's first block.
-//
-// With cps blocks resident per XCD, the first B - R entries of a list of B
-// (R = B mod cps, the XCD's partial last round) are whole tiles; each of the
-// last R tiles becomes s = min(cps / R, kMaxSplit, nk / kMinSplitTiles)
-// pieces of consecutive reduction tiles, which take the XCD's block numbers
-// after the whole tiles and so fill its last round.  s < 2 leaves every
-// tile whole.
-__device__ __forceinline__ bool map_unit(const int* __restrict__ tile_start,
-                                         const int* __restrict__ xcd_start, int E,
-                                         int n_tiles, int nk, int cps, Unit* w) {
-  const int x = blockIdx.x % kXcds;
-  const int i = blockIdx.x / kXcds;
-  const int* __restrict__ P = xcd_start + x * (E + 1);
-  const int B = P[E];
-  const int R = B % cps;
-  int s = R > 0 ? min(min(cps / R, kMaxSplit), nk / kMinSplitTiles) : 1;
-  if (s < 2) s = 1;
-  const int whole = s > 1 ? B - R : B;
-  // (fields are set once, at the end: per-branch stores to a struct through
-  // a pointer can end up in scratch memory)
-  const bool is_piece = i >= whole;
-  const int p = i - whole;
-  if (is_piece && (s == 1 || p >= R * s)) return false;
-  const int t = is_piece ? p / s : 0;
-  const int piece = is_piece ? p % s : 0;
-  const int parts = is_piece ? s : 1;
-  const int entry = is_piece ? whole + t : i;
-  int lo = 0, hi = E;  // P[lo] <= entry < P[hi]: expert lo has blocks here
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (P[mid] <= entry) lo = mid; else hi = mid;
-  }
-  const int first = tile_start[lo];
-  const int cnt = tile_start[lo + 1] - first;
-  const int r = entry - P[lo];
-  *w = Unit{first + r % cnt,
-            xcd_first_n(lo, x, n_tiles) + kXcds * (r / cnt),
-            piece * nk / parts,
-            (piece + 1) * nk / parts,
-            is_piece ? x * cps + t : -1,
-            piece,
-            parts,
-            x * cps + t * s};
-  return true;
-}
-
-// ---------------------------------------------------------------------------
 // bf16 MFMA GEMM
 // ---------------------------------------------------------------------------
 
-// Buffer descriptor word 3 for raw (untyped) buffer loads on CDNA.
-constexpr int kBufferFlags = 0x00020000;
-
 constexpr int kBW = 256;            // weight rows per block tile
-constexpr int kBK = 64;             // reduction elements per stage
-constexpr int kRowBytes = kBK * (int)sizeof(bf16);  // 128: one LDS row
-
-typedef __attribute__((address_space(3))) void lds_void_t;
-
-// Element offset of 16-byte chunk `chunk` (0..7) of LDS row `row`.  An MFMA
-// operand read has 16 lanes in flight per LDS cycle (64 banks x 4 bytes),
-// reading 16 consecutive 128-byte rows at one chunk; rows r and r + 1 fall
-// in different halves of the 256-byte bank window, so XOR-ing the chunk
-// with (row / 2) & 7 puts the 16 lanes on 16 different 16-byte bank groups.
-__device__ __forceinline__ int swz_chunk(int row, int chunk) {
-  return chunk ^ ((row >> 1) & 7);
-}
-__device__ __forceinline__ int swz(int row, int chunk) {
-  return row * kBK + (swz_chunk(row, chunk) << 3);
-}
 
 // Geometry of a block tile of BM token rows x 256 weight rows, NW waves laid
 // out WM (along tokens) x NW/WM (along weight rows).
@@ -853,23 +610,6 @@ __global__ __launch_bounds__(kThreads) void ffn_gemm_f32_kernel(
   }
 }
 
-// Blocks of a bf16 GEMM resident at once on the current device: one per CU
-// (the kernels take all of a CU's LDS), capped at kMaxSplitUnits.  Cached per
-// device.
-int resident_blocks() {
-  constexpr int kMaxDevices = 64;
-  static int cache[kMaxDevices] = {};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return kMaxSplitUnits;
-  if (dev < kMaxDevices && cache[dev] > 0) return cache[dev];
-  int cus = 0;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-      cus <= 0)
-    cus = kMaxSplitUnits;
-  cus = cus < kMaxSplitUnits ? cus : kMaxSplitUnits;
-  if (dev < kMaxDevices) cache[dev] = cus;
-  return cus;
-}
 
 template <int BM, int WM, int NW, bool kDual>
 hipError_t launch_bf16_gemm(const bf16* act, int Kdim, const bf16* w0,
@@ -889,7 +629,7 @@ hipError_t launch_bf16_gemm(const bf16* act, int Kdim, const bf16* w0,
   const int n_tiles = (Nout + kNOut - 1) / kNOut;
   // an XCD's list holds at most max_tiles x ceil(n_tiles / 8) whole tiles,
   // and its split pieces take at most cps more blocks
-  const int cps = resident_blocks() / kXcds > 0 ? resident_blocks() / kXcds : 1;
+  const int cps = ffn_resident_blocks() / kXcds > 0 ? ffn_resident_blocks() / kXcds : 1;
   const long long per_xcd = (long long)max_tiles * ((n_tiles + kXcds - 1) / kXcds) + cps;
   const int grid = (int)(per_xcd * kXcds);
   const int* xcd_start = ws.xcd_start + (kDual ? 0 : kXcds * (E + 1));
@@ -928,14 +668,33 @@ int bf16_tile_rows(int64_t max_rows, int E) {
 
 }  // namespace
 
+int ffn_resident_blocks() {
+  constexpr int kMaxDevices = 64;
+  static int cache[kMaxDevices] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return kMaxSplitUnits;
+  if (dev < kMaxDevices && cache[dev] > 0) return cache[dev];
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0)
+    cus = kMaxSplitUnits;
+  cus = cus < kMaxSplitUnits ? cus : kMaxSplitUnits;
+  if (dev < kMaxDevices) cache[dev] = cus;
+  return cus;
+}
+
 size_t grouped_ffn_workspace_bytes(int64_t max_rows, int E, bool bf16_data) {
   // the tile table is sized for the smallest row tile, so it covers every
-  // tile choice; split partials hold kMaxSplitUnits fp32 tiles of BM x 256
+  // tile choice; split partials hold kMaxSplitUnits fp32 block tiles, of
+  // BM x 256 here and of BM x 512 in the packed-weight kernel (one
+  // workspace serves both)
   const int tr = bf16_data ? 32 : kF32TileRows;
   const size_t table = ffn_tiles_offset(E) +
                        align_up((size_t)max_tiles_for(max_rows, E, tr) * sizeof(int4), 256);
   if (!bf16_data) return table;
-  return table + (size_t)kMaxSplitUnits * bf16_tile_rows(max_rows, E) * kBW * sizeof(float);
+  const size_t mine = (size_t)kMaxSplitUnits * bf16_tile_rows(max_rows, E) * kBW * sizeof(float);
+  const size_t packed = packed_ffn_partial_bytes(max_rows, E);
+  return table + (mine > packed ? mine : packed);
 }
 
 hipError_t launch_grouped_ffn(const void* x_perm, bool bf16_data, int d,

@@ -67,6 +67,21 @@ hipError_t launch_reroute(const float* logits, int N, int E, int K, bool sigmoid
                           float* topk_w, int32_t* rerouted, void* workspace,
                           hipStream_t stream);
 
+// Grouped FFN on packed bf16 weights (grouped_ffn_packed.hip).  Panels of
+// the packed gate/up (gate_up) or down matrix, its bytes for E experts, the
+// row-tile height the launch picks and the split partials it needs.
+int packed_panels(int d, int ffn, bool gate_up);
+size_t packed_ffn_weight_bytes(int E, int d, int ffn, bool gate_up);
+int packed_ffn_tile_rows(int64_t max_rows, int E);
+size_t packed_ffn_partial_bytes(int64_t max_rows, int E);
+hipError_t launch_pack_ffn_weights(const void* w_gate, const void* w_up, const void* w_down,
+                                   int E, int d, int ffn, void* packed_up, void* packed_down,
+                                   hipStream_t stream);
+hipError_t launch_grouped_ffn_packed(const void* x_perm, int d, int ffn, int E,
+                                     const int32_t* offsets, int64_t max_rows,
+                                     const void* packed_up, const void* packed_down, void* h,
+                                     void* y_perm, void* workspace, hipStream_t stream);
+
 hipError_t launch_combine(const void* y_perm, bool bf16_data, int N, int d,
                           int K, const int32_t* dest, const float* topk_w,
                           void* out, hipStream_t stream);

@@ -246,6 +246,59 @@ int moe_grouped_ffn(const void* x_perm, int32_t dtype, int32_t d, int32_t ffn,
                     void* h, void* y_perm, void* workspace,
                     size_t workspace_bytes, void* stream);
 
+/* Which packed weight matrix moe_packed_ffn_weight_bytes sizes. */
+typedef enum {
+  MOE_FFN_GATE_UP = 0, /* w_gate and w_up together */
+  MOE_FFN_DOWN = 1     /* w_down */
+} moe_ffn_part_t;
+
+/*
+ * Bytes of one packed bf16 weight matrix for E experts (0 for invalid sizes).
+ * MOE_FFN_GATE_UP: E * 2 * ffn * d * 2; MOE_FFN_DOWN: E * ceil(d / 128) *
+ * 128 * ffn * 2.
+ */
+size_t moe_packed_ffn_weight_bytes(int32_t E, int32_t d, int32_t ffn, int32_t part);
+
+/*
+ * Pack bf16 expert weights for moe_grouped_ffn_packed: a one-time
+ * rearrangement (at weight-load time) into the order in which the gfx950
+ * matrix cores consume them; the values are bit copies.  Per expert, each
+ * matrix becomes panels of 128 rows; a panel holds, for each 16-wide
+ * reduction step s, four 1 KB fragments of 32 rows, fragment i holding for
+ * lane l = 0..63 the 8 values W[row(i, l % 32)][16 s + 8 (l / 32) .. + 8].
+ *   gate/up panel p: fragments gate rows 64p..64p+31, gate 64p+32..64p+63,
+ *     up 64p..64p+31, up 64p+32..64p+63 (P = ffn / 64 panels per expert);
+ *   down panel p: rows 128p .. 128p+127 of w_down, rows past d zero
+ *     (P = ceil(d / 128)).
+ *   byte offset of (expert e, panel p, step s, fragment i, lane l) =
+ *     (((e * P + p) * S + s) * 4 + i) * 1024 + 16 l, S = reduction / 16.
+ *   w_gate, w_up [E, ffn, d] bf16; w_down [E, d, ffn] bf16 (device).
+ *   packed_up   out, moe_packed_ffn_weight_bytes(E, d, ffn, MOE_FFN_GATE_UP).
+ *   packed_down out, moe_packed_ffn_weight_bytes(E, d, ffn, MOE_FFN_DOWN).
+ * Checks: pointers non-null; E, d, ffn >= 1 (INVALID_ARG); d and ffn
+ *         multiples of 64, E limit, packed matrices of one expert below 2 GiB
+ *         (UNSUPPORTED).
+ */
+int moe_pack_ffn_weights(const void* w_gate, const void* w_up, const void* w_down,
+                         int32_t E, int32_t d, int32_t ffn, void* packed_up,
+                         void* packed_down, void* stream);
+
+/*
+ * moe_grouped_ffn for bf16 layers whose weights were packed by
+ * moe_pack_ffn_weights: same operation, arguments and results (h and y_perm
+ * equal moe_grouped_ffn's up to the grouping of split reductions), with the
+ * weights streamed from the packed layout straight into the matrix cores'
+ * registers.  workspace: moe_grouped_ffn_workspace_bytes(max_rows, E,
+ * MOE_DTYPE_BF16) bytes.
+ * Checks: as moe_pack_ffn_weights for the sizes; pointers non-null;
+ *         max_rows >= 0 (INVALID_ARG); max_rows < 2^31 (UNSUPPORTED);
+ *         workspace (WORKSPACE).  max_rows == 0 enqueues nothing.
+ */
+int moe_grouped_ffn_packed(const void* x_perm, int32_t d, int32_t ffn, int32_t E,
+                           const int32_t* offsets, int64_t max_rows, const void* packed_up,
+                           const void* packed_down, void* h, void* y_perm, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
 /*
  * Combine: inverse permutation with the gate-weighted sum.
  * "MoE 专家并行的 All-to-All 通信瓶颈", flowchart step "加权合并回原 token

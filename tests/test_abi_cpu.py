@@ -204,6 +204,40 @@ def test_grouped_ffn_rejects_bad_arguments(lib):
     assert _ffn(lib, max_rows=0, ws=NUL) == 0       # nothing to do: no launch
 
 
+def test_packed_weight_bytes_closed_forms(lib):
+    for E, d, ffn in [(1, 64, 64), (8, 4096, 14336), (256, 7168, 2048), (3, 320, 192)]:
+        assert lib.moe_packed_ffn_weight_bytes(E, d, ffn, 0) == E * 2 * ffn * d * 2
+        assert lib.moe_packed_ffn_weight_bytes(E, d, ffn, 1) == E * (-(-d // 128) * 128) * ffn * 2
+    for E, d, ffn, part in [(0, 64, 64, 0), (1, 96, 64, 0), (1, 64, 32, 1), (1, 64, 64, 2)]:
+        assert lib.moe_packed_ffn_weight_bytes(E, d, ffn, part) == 0
+
+
+def test_packed_ffn_entry_points_reject_bad_arguments(lib):
+    pack = lib.moe_pack_ffn_weights
+    assert pack(FAKE, FAKE, NUL, 8, 128, 128, FAKE, FAKE, NUL) == 1
+    assert pack(FAKE, FAKE, FAKE, 0, 128, 128, FAKE, FAKE, NUL) == 1
+    assert pack(FAKE, FAKE, FAKE, 1025, 128, 128, FAKE, FAKE, NUL) == 2
+    assert pack(FAKE, FAKE, FAKE, 8, 96, 128, FAKE, FAKE, NUL) == 2
+    assert pack(FAKE, FAKE, FAKE, 8, 65536, 16384, FAKE, FAKE, NUL) == 2   # > 2 GiB / expert
+    assert "2 GiB" in lib.moe_last_error().decode()
+
+    def ffn(**kw):
+        a = dict(x=FAKE, d=128, ffn=128, E=8, off=FAKE, max_rows=64, up=FAKE, dn=FAKE, h=FAKE,
+                 y=FAKE, ws=FAKE, ws_bytes=1 << 30)
+        a.update(kw)
+        return lib.moe_grouped_ffn_packed(a["x"], a["d"], a["ffn"], a["E"], a["off"],
+                                          a["max_rows"], a["up"], a["dn"], a["h"], a["y"],
+                                          a["ws"], a["ws_bytes"], NUL)
+    assert ffn(dn=NUL) == 1
+    assert ffn(max_rows=-1) == 1
+    assert ffn(E=0) == 1
+    assert ffn(ffn=96) == 2
+    assert ffn(max_rows=1 << 31) == 2
+    need = lib.moe_grouped_ffn_workspace_bytes(64, 8, 1)
+    assert ffn(ws_bytes=need - 1) == 3
+    assert ffn(max_rows=0, ws=NUL) == 0
+
+
 def test_combine_rejects_bad_arguments(lib):
     f = lib.moe_combine
     assert f(NUL, 1, 4, 64, 2, FAKE, FAKE, FAKE, NUL) == 1

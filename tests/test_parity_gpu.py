@@ -48,12 +48,26 @@ def _cap(cfg):
     return O.capacity(cfg["C"], cfg["N"], cfg["K"], cfg["E"]) if cfg["C"] is not None else -1
 
 
-def _run_gpu(cfg, inp, cap):
+def _run_gpu(cfg, inp, cap, packed=False):
+    """One layer call; packed=True streams the weights from the layout of
+    moe_pack_ffn_weights (bf16 layers)."""
     layer = B.MoeLayer(cfg["N"], cfg["d"], cfg["ffn"], cfg["E"], cfg["K"], cfg["W"], cap,
                        synth.TORCH_DTYPE[cfg["act"]], DEV, cfg.get("renormalize", False))
-    layer.forward(inp["logits"], inp["x"], inp["w_gate"], inp["w_up"], inp["w_down"])
+    if packed:
+        pw = B.moe_pack_ffn_weights(inp["w_gate"], inp["w_up"], inp["w_down"])
+        layer.forward(inp["logits"], inp["x"], pw)
+    else:
+        layer.forward(inp["logits"], inp["x"], inp["w_gate"], inp["w_up"], inp["w_down"])
     torch.cuda.synchronize()
     return layer
+
+
+def _layers(cfg, inp, cap):
+    """The plain-weight layer and, for bf16 layers, the packed-weight one,
+    one after the other."""
+    yield "plain", _run_gpu(cfg, inp, cap)
+    if cfg["act"] == "bf16":
+        yield "packed", _run_gpu(cfg, inp, cap, packed=True)
 
 
 def _expert_weights_np(inp):
@@ -130,14 +144,15 @@ def _small_inputs(cfg, logits_override=None):
 
 def _check_small(cfg, inp):
     cap = _cap(cfg)
-    layer = _run_gpu(cfg, inp, cap)
     ref = O.layer(_np(inp["logits"]), _np(inp["x"]), _expert_weights_np(inp), cfg["K"],
                   cfg["W"], cap, cfg["act"], cfg.get("renormalize", False))
-    M = _check_route_dispatch(cfg, layer, ref, inp["x"])
-    if M > 0:
-        _close("h", _np(layer.h)[:M], ref["h"], cfg["act"])
-        _close("y_perm", _np(layer.y_perm)[:M], ref["y_perm"], cfg["act"])
-    _close("out", _np(layer.out), ref["out"], cfg["act"])
+    for kind, layer in _layers(cfg, inp, cap):
+        print(f"[parity]   {kind} weights", flush=True)
+        M = _check_route_dispatch(cfg, layer, ref, inp["x"])
+        if M > 0:
+            _close(f"{kind} h", _np(layer.h)[:M], ref["h"], cfg["act"])
+            _close(f"{kind} y_perm", _np(layer.y_perm)[:M], ref["y_perm"], cfg["act"])
+        _close(f"{kind} out", _np(layer.out), ref["out"], cfg["act"])
     return layer, ref
 
 
@@ -242,13 +257,10 @@ def test_full_size_layer_matches_oracle(name):
     print(f"[parity] {name} {cfg}", flush=True)
     inp = synth.make_inputs(cfg, DEV)
     cap = _cap(cfg)
-    layer = _run_gpu(cfg, inp, cap)
     logits = _np(inp["logits"])
     idx, w = O.route(logits, cfg["K"])
     ref = O.dispatch(idx, cfg["E"], cfg["W"], cap)
     ref.update(topk_idx=idx, topk_w=w)
-    M = _check_route_dispatch(cfg, layer, ref, inp["x"])
-    print(f"[parity] {name}: M={M} dropped={ref['dropped']}", flush=True)
 
     rng = np.random.default_rng(0)
     n = SAMPLES[name]
@@ -260,8 +272,13 @@ def test_full_size_layer_matches_oracle(name):
     xs = _np(inp["x"][torch.tensor(toks, device=DEV)])
     y_rows, out_ref = O.token_outputs(toks, xs, idx, w, ref["dest"],
                                       _expert_weights_np(inp), cfg["act"])
-    out_got = _np(layer.out[torch.tensor(toks, device=DEV)])
-    _close("out", out_got, out_ref, cfg["act"])
-    for (t, k), y in y_rows.items():
-        row = int(ref["dest"][t, k])
-        _close(f"y_perm[{row}]", _np(layer.y_perm[row]), y, cfg["act"])
+    for kind, layer in _layers(cfg, inp, cap):
+        M = _check_route_dispatch(cfg, layer, ref, inp["x"])
+        print(f"[parity] {name} {kind} weights: M={M} dropped={ref['dropped']}", flush=True)
+        out_got = _np(layer.out[torch.tensor(toks, device=DEV)])
+        _close(f"{kind} out", out_got, out_ref, cfg["act"])
+        for (t, k), y in y_rows.items():
+            row = int(ref["dest"][t, k])
+            _close(f"{kind} y_perm[{row}]", _np(layer.y_perm[row]), y, cfg["act"])
+        del layer
+        torch.cuda.empty_cache()
