@@ -7,7 +7,11 @@ already resident in HBM.  Prints one JSON line:
   value            whole-layer tokens/s (N tokens per step / time per step)
   roofline         the grouped FFN call (the dominant stage: its tile-schedule,
                    gate/up and down kernels) against bf16 MFMA peak:
-                   6*M*d*ffn flops per call / its event-timed duration
+                   6*M*d*ffn flops per call / its event-timed duration.
+                   bf16 layers stream expert weights packed in MFMA operand
+                   order (moe_pack_ffn_weights, run once at setup like a
+                   weight load, outside the timed steps); --plain-weights
+                   times the row-major-weight kernel instead
   stages           per-stage times of the timed steps; dispatch and combine
                    also timed alone with a cold cache (HBM GB/s vs peak)
   cpu_baseline     the CPU oracle on a bounded sample of the same workload
@@ -33,7 +37,12 @@ FP32_PEAK_TFLOPS = 157.3
 
 DEFAULT_WORKLOAD = "dense8"
 SCRUB_MIB = 512                  # > the 256 MB last-level (MALL) cache
-FFN_SOURCE = os.path.join(ROOT, "grouped_gemm_route_amd", "csrc", "grouped_ffn.hip")
+CSRC = os.path.join(ROOT, "grouped_gemm_route_amd", "csrc")
+# sources of the timed FFN kernels (their digest keys the traffic counters)
+FFN_SOURCES = {
+    "packed": [os.path.join(CSRC, "grouped_ffn_packed.hip"), os.path.join(CSRC, "ffn_tiles.h")],
+    "plain": [os.path.join(CSRC, "grouped_ffn.hip"), os.path.join(CSRC, "ffn_tiles.h")],
+}
 
 
 def parse():
@@ -52,6 +61,9 @@ def parse():
                    help="reps of the cold-cache dispatch/combine timing (0 skips it)")
     p.add_argument("--no-exchange", action="store_true",
                    help="skip the virtual multi-source exchange measurements")
+    p.add_argument("--plain-weights", action="store_true",
+                   help="time the FFN on row-major weights (moe_grouped_ffn) instead of "
+                        "packed ones")
     p.add_argument("--copy-ref-mib", type=int, default=0,
                    help="run one plain device-to-device copy of this many MiB first "
                         "(the reference kernel for scaling HBM byte counters)")
@@ -77,23 +89,26 @@ def ffn_flops(cfg, M):
     return 6.0 * M * cfg["d"] * cfg["ffn"]
 
 
-def source_digest(path):
-    """sha256[:16] of a C++ source with its comments and blank space removed,
-    so the digest names the code a counter run measured, not its prose."""
+def source_digest(paths):
+    """sha256[:16] of C++ sources with their comments and blank space
+    removed, so the digest names the code a counter run measured, not its
+    prose."""
     import re
 
-    with open(path, encoding="utf-8") as f:
-        text = f.read()
-    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
-    text = re.sub(r"//[^\n]*", " ", text)
-    text = " ".join(text.split())
-    return hashlib.sha256(text.encode()).hexdigest()[:16]
+    texts = []
+    for path in paths:
+        with open(path, encoding="utf-8") as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        texts.append(" ".join(text.split()))
+    return hashlib.sha256("\n".join(texts).encode()).hexdigest()[:16]
 
 
-def load_traffic(path, workload):
+def load_traffic(path, workload, weights):
     """HBM bytes per grouped-FFN call from the counter summary, or None when
-    the summary is missing, is for another workload, or predates the current
-    kernel source."""
+    the summary is missing, is for another workload or weight layout, or
+    predates the current kernel source."""
     if not os.path.exists(path):
         return None
     try:
@@ -101,7 +116,8 @@ def load_traffic(path, workload):
             tj = json.load(f)
     except (OSError, ValueError):
         return None
-    if tj.get("workload") != workload or tj.get("source_sha256_16") != source_digest(FFN_SOURCE):
+    if (tj.get("workload") != workload or tj.get("weights") != weights
+            or tj.get("source_sha256_16") != source_digest(FFN_SOURCES[weights])):
         return None
     return tj.get("bytes_per_call")
 
@@ -140,6 +156,16 @@ def main():
 
     inp = synth.make_inputs(cfg, dev)
     layer = B.MoeLayer(N, d, ffn, E, K, W, cap, dtype, dev)
+    weights = "packed" if cfg["act"] == "bf16" and not args.plain_weights else "plain"
+    pack_ms = None
+    if weights == "packed":   # once, as at weight-load time
+        torch.cuda.synchronize()
+        t_pack = time.perf_counter()
+        ffn_args = (B.moe_pack_ffn_weights(inp["w_gate"], inp["w_up"], inp["w_down"]),)
+        torch.cuda.synchronize()
+        pack_ms = (time.perf_counter() - t_pack) * 1e3
+    else:
+        ffn_args = (inp["w_gate"], inp["w_up"], inp["w_down"])
 
     def step(ev=None):
         if ev is not None:
@@ -150,7 +176,7 @@ def main():
         layer.dispatch(inp["x"])
         if ev is not None:
             ev[2].record(stream)
-        layer.ffn(inp["w_gate"], inp["w_up"], inp["w_down"])
+        layer.ffn(*ffn_args)
         if ev is not None:
             ev[3].record(stream)
         layer.combine()
@@ -208,6 +234,15 @@ def main():
         cold_dc = (disp_b + comb_b) / ((cold["dispatch"] + cold["combine"]) * 1e-3) / 1e9
     hot_dc = (disp_b + comb_b) / ((st["dispatch"] + st["combine"]) * 1e-3) / 1e9
 
+    # the other weight layout's FFN on the same rows, for comparison (outside
+    # the timed steps, after them, 10 calls)
+    other_ffn_ms = None
+    if cfg["act"] == "bf16":
+        other = ((inp["w_gate"], inp["w_up"], inp["w_down"]) if weights == "packed" else
+                 (B.moe_pack_ffn_weights(inp["w_gate"], inp["w_up"], inp["w_down"]),))
+        other_ffn_ms = _timed(stream, lambda: layer.ffn(*other), reps=10)
+        del other
+
     stages = {
         "route_ms": st["route"],
         "dispatch_ms": st["dispatch"],
@@ -218,6 +253,10 @@ def main():
         "dispatch_combine_GBps_in_step": hot_dc,
         "ffn_TFLOPs": achieved_tflops,
         "ffn_mfma_frac": achieved_tflops / peak,
+        "ffn_weights": weights,
+        "weight_pack_ms": pack_ms,
+        ("ffn_plain_weights_ms" if weights == "packed" else "ffn_packed_weights_ms"):
+            other_ffn_ms,
         "tokens_per_s": {n: N / (st[n] * 1e-3) for n in names},
     }
     if cold:
@@ -252,13 +291,14 @@ def main():
                            "virtual-rank slices",
         },
         "roofline": {
-            "kernel": "moe_grouped_ffn call (tile schedule + gate/up GEMM + down GEMM)",
+            "kernel": ("moe_grouped_ffn_packed" if weights == "packed" else "moe_grouped_ffn")
+                      + " call (tile schedule + gate/up GEMM + down GEMM)",
             "bound": "mfma",
             "achieved": achieved_tflops,
             "peak": peak,
             "unit": "TFLOP/s",
             "frac": achieved_tflops / peak,
-            "traffic": load_traffic(args.traffic_json, args.workload),
+            "traffic": load_traffic(args.traffic_json, args.workload, weights),
         },
         "stages": stages,
     }
