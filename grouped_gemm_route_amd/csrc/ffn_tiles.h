@@ -4,15 +4,18 @@
 //
 // A one-block kernel turns offsets[] (which stays on the device) into row
 // tiles (expert, first row, end row) of at most tile_rows rows of one
-// expert, and into per-XCD work lists: block b runs on XCD b % 8, each
-// expert's output-column tiles are dealt round-robin over the XCDs, and an
-// XCD runs, expert by expert, each of its column tiles with all of that
-// expert's row tiles, so the blocks resident on an XCD share one weight
-// tile and a few activation tiles through its L2 and every XCD gets the
-// same mix of full and ragged tiles.  A GEMM grid is sized on the host from
-// the upper bound max_rows; blocks beyond the real work exit at once.  The
-// tiles of an XCD's partial last round are split along the reduction (see
-// map_unit).
+// expert.  The blocks of a GEMM pass are (row tile, output-column tile)
+// pairs in one global order: expert by expert, column tile by column tile,
+// and for each column tile all of the expert's row tiles, so consecutive
+// blocks share one weight tile and a few activation tiles.  Block b runs
+// on XCD b % 8, and each XCD takes one contiguous eighth of that order
+// (cut at column-tile boundaries, see xcd_range), so the blocks resident on
+// an XCD share weight and activation tiles through its L2 and every XCD gets
+// the same number of blocks.  The tiles of an XCD's partial last round are
+// split along the reduction when that shortens the round enough (see
+// map_unit).  A GEMM either sizes its grid on the host from the upper bound
+// max_rows (blocks beyond the real work exit at once) or launches one block
+// per CU that walks its XCD's range (grouped_ffn_packed.hip).
 #pragma once
 
 #include "moe_internal.h"
@@ -36,29 +39,27 @@ namespace {
 constexpr int kMaxSplitUnits = 256;  // split pieces per launch (block slots)
 constexpr int kMaxSplit = 8;         // pieces per tile
 constexpr int kMinSplitTiles = 8;    // reduction tiles per piece, at least
+// A split costs each piece a pass of its fp32 partials through memory (about
+// as long as 40 reduction tiles of compute at BM = 128 on MI355X), so a tile
+// is split only when that takes at least this many reduction tiles off the
+// last round.
+constexpr int kSplitMinSaved = 48;
 
 // Workspace layout: [num_tiles | pad to 256 B][split counters: 2 x
-// kMaxSplitUnits ints][XCD block tables: 2 passes x 8 XCDs x (E+1) ints |
-// pad][tile_start[E+1] | pad][tiles | pad][split partials].
+// kMaxSplitUnits ints][tile_start[E+1] | pad][tiles | pad][split partials].
 struct FfnWorkspace {
   int* num_tiles;
   int* split_cnt;   // arrival counters of split tiles: gate/up pass, then down
-  int* xcd_start;   // [pass][xcd][E+1]: the XCD's blocks for experts < e
   int* tile_start;  // tiles of expert e are slots [tile_start[e], tile_start[e+1])
   int4* tiles;      // (expert, first row, end row, 0)
-  float* partial;   // kMaxSplitUnits fp32 accumulator tiles of BM x 256
+  float* partial;   // kMaxSplitUnits fp32 accumulator tiles (one per block slot)
 };
 
 constexpr int kXcds = 8;  // block b runs on XCD b % 8
 constexpr size_t kSplitCntBytes = 2 * kMaxSplitUnits * sizeof(int);
 
-inline size_t ffn_xcd_table_bytes(int E) {
-  return align_up((size_t)2 * kXcds * (E + 1) * sizeof(int), 256);
-}
-
 inline size_t ffn_tiles_offset(int E) {
-  return 256 + kSplitCntBytes + ffn_xcd_table_bytes(E) +
-         align_up((size_t)(E + 1) * sizeof(int), 256);
+  return 256 + kSplitCntBytes + align_up((size_t)(E + 1) * sizeof(int), 256);
 }
 
 inline FfnWorkspace ffn_workspace(void* base, int E, int max_tiles) {
@@ -66,32 +67,17 @@ inline FfnWorkspace ffn_workspace(void* base, int E, int max_tiles) {
   FfnWorkspace ws;
   ws.num_tiles = reinterpret_cast<int*>(p);
   ws.split_cnt = reinterpret_cast<int*>(p + 256);
-  ws.xcd_start = reinterpret_cast<int*>(p + 256 + kSplitCntBytes);
-  ws.tile_start = reinterpret_cast<int*>(p + 256 + kSplitCntBytes + ffn_xcd_table_bytes(E));
+  ws.tile_start = reinterpret_cast<int*>(p + 256 + kSplitCntBytes);
   ws.tiles = reinterpret_cast<int4*>(p + ffn_tiles_offset(E));
   ws.partial = reinterpret_cast<float*>(
       p + ffn_tiles_offset(E) + align_up((size_t)max_tiles * sizeof(int4), 256));
   return ws;
 }
 
-// Column tiles n of expert e that XCD x runs: n = xcd_first_n(e, x, n) + 8 k.
-// Expert e's column tiles are dealt round-robin over the XCDs, continuing
-// where expert e - 1 stopped, so every XCD gets about the same share of
-// every expert (of its thin and full row tiles alike).
-__device__ __forceinline__ int xcd_first_n(int e, int x, int n_tiles) {
-  const int start = ((e % kXcds) * (n_tiles % kXcds)) % kXcds;  // (e * n_tiles) % 8
-  return (x - start + kXcds) % kXcds;
-}
-__device__ __forceinline__ int xcd_groups(int e, int x, int n_tiles) {
-  const int f = xcd_first_n(e, x, n_tiles);
-  return f < n_tiles ? (n_tiles - f + kXcds - 1) / kXcds : 0;
-}
-
 __global__ __launch_bounds__(1024) void ffn_schedule_kernel(
     const int32_t* __restrict__ offsets, int E, int tile_rows, int max_rows,
-    int max_tiles, int n_up, int n_dn, int4* __restrict__ tiles,
-    int* __restrict__ tile_start, int* __restrict__ num_tiles,
-    int* __restrict__ split_cnt, int* __restrict__ xcd_start) {
+    int max_tiles, int4* __restrict__ tiles, int* __restrict__ tile_start,
+    int* __restrict__ num_tiles, int* __restrict__ split_cnt) {
   __shared__ int wave_sums[1024 / kWave];
   const int e = threadIdx.x;
   if (e < 2 * kMaxSplitUnits) split_cnt[e] = 0;
@@ -113,32 +99,6 @@ __global__ __launch_bounds__(1024) void ffn_schedule_kernel(
     }
   }
   if (e == 0) *num_tiles = min(total, max_tiles);
-  // Per pass and XCD, the exclusive scan over experts of the XCD's blocks:
-  // wave w < 16 scans the table of pass w / 8 and XCD w % 8, 64 experts at
-  // a time.
-  __shared__ int cnt_s[1024];
-  cnt_s[e] = e < E ? min(base + nt, max_tiles) - min(base, max_tiles) : 0;
-  __syncthreads();
-  const int wave = e / kWave, lane = e % kWave;
-  if (wave < 2 * kXcds) {
-    const int x = wave % kXcds;
-    const int n_tiles = wave < kXcds ? n_up : n_dn;
-    int* P = xcd_start + wave * (E + 1);
-    int run = 0;
-    for (int c = 0; c < E; c += kWave) {
-      const int ee = c + lane;
-      const int v = ee < E ? xcd_groups(ee, x, n_tiles) * cnt_s[ee] : 0;
-      int incl = v;
-#pragma unroll
-      for (int off = 1; off < kWave; off <<= 1) {
-        const int o = __shfl_up(incl, off);
-        if (lane >= off) incl += o;
-      }
-      if (ee < E) P[ee] = run + incl - v;
-      run += __shfl(incl, kWave - 1);
-    }
-    if (lane == 0) P[E] = run;
-  }
 }
 
 inline int max_tiles_for(int64_t max_rows, int E, int tile_rows) {
@@ -183,30 +143,57 @@ struct Unit {
   int slot, n_tile, kb, ke, split, piece, parts, pslot0;
 };
 
-// Block -> work unit.  Block b runs on XCD x = b % 8 as that XCD's block
-// i = b / 8.  XCD x works through its own list: expert by expert, its share
-// of the expert's column tiles (dealt round-robin, see xcd_first_n), and
-// for each column tile all of the expert's row tiles, so that the blocks an
-// XCD runs together share one weight tile and a few activation tiles
-// through its L2.  xcd_start (the XCD's row of the schedule's table) gives
-// the list position of each expert's first block.
+// Expert holding global block position L (0 <= L < n_tiles * tile_start[E]):
+// the largest e with n_tiles * tile_start[e] <= L (an expert without tiles
+// never matches, since the next expert starts at the same position).
+__device__ __forceinline__ int expert_at(const int* __restrict__ tile_start, int E, int n_tiles,
+                                         int L) {
+  int lo = 0, hi = E;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (n_tiles * tile_start[mid] <= L) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+// First global block position of XCD x's range: the first column-tile
+// boundary at or after x T / 8 (T = all blocks of the pass); x = 8 gives T.
+// Cutting at column-tile boundaries keeps a weight tile's blocks on one XCD.
+__device__ __forceinline__ int xcd_range(const int* __restrict__ tile_start, int E,
+                                         int n_tiles, int x) {
+  const int T = n_tiles * tile_start[E];
+  if (x >= kXcds) return T;
+  const int t = (int)((long long)x * T / kXcds);
+  if (t >= T) return T;
+  const int e = expert_at(tile_start, E, n_tiles, t);
+  const int g0 = n_tiles * tile_start[e];
+  const int cnt = tile_start[e + 1] - tile_start[e];
+  const int n = (t - g0 + cnt - 1) / cnt;  // column tiles of e that start before t
+  return g0 + n * cnt;
+}
+
+// Block slot b -> work unit.  Block slot b runs on XCD x = b % 8 as that
+// XCD's block i = b / 8 (b is the block index, or for a block that walks
+// its XCD's range, blockIdx.x + k gridDim.x with gridDim.x a multiple of 8);
+// i indexes the XCD's range [xcd_range(x), xcd_range(x + 1)) of the global
+// order.
 //
-// With cps blocks resident per XCD, the first B - R entries of a list of B
-// (R = B mod cps, the XCD's partial last round) are whole tiles; each of the
-// last R tiles becomes s = min(cps / R, kMaxSplit, nk / kMinSplitTiles)
+// With cps blocks resident per XCD, the first B - R entries of a range of
+// B (R = B mod cps, the XCD's partial last round) are whole tiles; each of
+// the last R tiles becomes s = min(cps / R, kMaxSplit, nk / kMinSplitTiles)
 // pieces of consecutive reduction tiles, which take the XCD's block numbers
-// after the whole tiles and so fill its last round.  s < 2 leaves every
-// tile whole.
-__device__ __forceinline__ bool map_unit(const int* __restrict__ tile_start,
-                                         const int* __restrict__ xcd_start, int E,
+// after the whole tiles and so fill its last round, if that saves at least
+// kSplitMinSaved reduction tiles of the round (nk - nk / s); otherwise
+// every tile stays whole.
+__device__ __forceinline__ bool map_unit(int b, const int* __restrict__ tile_start, int E,
                                          int n_tiles, int nk, int cps, Unit* w) {
-  const int x = blockIdx.x % kXcds;
-  const int i = blockIdx.x / kXcds;
-  const int* __restrict__ P = xcd_start + x * (E + 1);
-  const int B = P[E];
+  const int x = b % kXcds;
+  const int i = b / kXcds;
+  const int S0 = xcd_range(tile_start, E, n_tiles, x);
+  const int B = xcd_range(tile_start, E, n_tiles, x + 1) - S0;
   const int R = B % cps;
   int s = R > 0 ? min(min(cps / R, kMaxSplit), nk / kMinSplitTiles) : 1;
-  if (s < 2) s = 1;
+  if (s < 2 || nk - nk / s < kSplitMinSaved) s = 1;
   const int whole = s > 1 ? B - R : B;
   // (fields are set once, at the end: per-branch stores to a struct through
   // a pointer can end up in scratch memory)
@@ -216,17 +203,13 @@ __device__ __forceinline__ bool map_unit(const int* __restrict__ tile_start,
   const int t = is_piece ? p / s : 0;
   const int piece = is_piece ? p % s : 0;
   const int parts = is_piece ? s : 1;
-  const int entry = is_piece ? whole + t : i;
-  int lo = 0, hi = E;  // P[lo] <= entry < P[hi]: expert lo has blocks here
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (P[mid] <= entry) lo = mid; else hi = mid;
-  }
-  const int first = tile_start[lo];
-  const int cnt = tile_start[lo + 1] - first;
-  const int r = entry - P[lo];
+  const int L = S0 + (is_piece ? whole + t : i);
+  const int e = expert_at(tile_start, E, n_tiles, L);
+  const int first = tile_start[e];
+  const int cnt = tile_start[e + 1] - first;
+  const int r = L - n_tiles * first;
   *w = Unit{first + r % cnt,
-            xcd_first_n(lo, x, n_tiles) + kXcds * (r / cnt),
+            r / cnt,
             piece * nk / parts,
             (piece + 1) * nk / parts,
             is_piece ? x * cps + t : -1,
@@ -236,6 +219,25 @@ __device__ __forceinline__ bool map_unit(const int* __restrict__ tile_start,
   return true;
 }
 
+
+// Split-piece partials travel between blocks through memory with
+// system-scope cache policy (sc0 | sc1): a piece's stores go through the
+// caches to memory and complete (vmcnt) only once there, and the last piece's
+// loads bypass L1 and L2.  A piece then waits for its stores and counts
+// itself in with the arrival atomic; no device-wide fence is needed, which
+// on a multi-XCD GPU writes back (release) or invalidates (acquire) the
+// whole L2 of the XCD.
+constexpr int kCoherentPolicy = 1 | 16;
+
+__device__ __forceinline__ void store_partial(__amdgpu_buffer_rsrc_t r, int voff, int soff,
+                                              f32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, voff, soff,
+                                         kCoherentPolicy);
+}
+__device__ __forceinline__ f32x4 load_partial(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  return __builtin_bit_cast(f32x4,
+                            __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kCoherentPolicy));
+}
 
 // ---------------------------------------------------------------------------
 // operand staging helpers

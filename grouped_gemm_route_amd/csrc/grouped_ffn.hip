@@ -87,445 +87,461 @@ __global__ __launch_bounds__(NW * kWave, 1) void ffn_gemm_bf16_kernel(
     const bf16* __restrict__ act, int Kdim, const bf16* __restrict__ w0,
     const bf16* __restrict__ w1, int Nout, bf16* __restrict__ out,
     const int4* __restrict__ tiles, const int* __restrict__ tile_start,
-    const int* __restrict__ xcd_start, int E, int n_tiles, int cps,
-    float* __restrict__ partial, int* __restrict__ split_cnt) {
+    int E, int n_tiles,
+    int cps, float* __restrict__ partial, int* __restrict__ split_cnt) {
   using G = TileGeo<BM, WM, NW>;
   extern __shared__ __attribute__((aligned(16))) bf16 lds[];
-  Unit unit;
-  if (!map_unit(tile_start, xcd_start, E, n_tiles, Kdim / kBK, cps, &unit)) return;
-  const int slot = unit.slot;
-  const int n_tile = unit.n_tile;
-  const int kofs = unit.kb * kBK;  // first reduction element of this unit
-  const int4 tile = tiles[slot];
-  const int e = tile.x;
-  const int row0 = tile.y;
-  const int rows = tile.z - tile.y;
-  constexpr int kNOut = kDual ? kBW / 2 : kBW;  // output columns per block
-  const int n0 = n_tile * kNOut;
+  // One block per CU walks its XCD's range: block slot b = blockIdx.x + k
+  // gridDim.x (gridDim.x is 8 x the blocks resident per XCD).
+  for (int vb = blockIdx.x;; vb += gridDim.x) {
+    Unit unit;
+    if (!map_unit(vb, tile_start, E, n_tiles, Kdim / kBK, cps, &unit)) break;
+    // the previous unit's waves are done with LDS
+    __syncthreads();
+    const int slot = unit.slot;
+    const int n_tile = unit.n_tile;
+    const int kofs = unit.kb * kBK;  // first reduction element of this unit
+    const int4 tile = tiles[slot];
+    const int e = tile.x;
+    const int row0 = tile.y;
+    const int rows = tile.z - tile.y;
+    constexpr int kNOut = kDual ? kBW / 2 : kBW;  // output columns per block
+    const int n0 = n_tile * kNOut;
 
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
 
-  // Global -> LDS.  Loads go straight into LDS (buffer_load ... lds): a
-  // wave-wide load writes its 64 lanes' 16-byte pieces to 1 KB of
-  // consecutive LDS, i.e. 8 rows of 128 bytes.  Lane l fills slot l % 8 of
-  // row r = (its group's first row) + l / 8, and since slot s of row r must
-  // hold the chunk that swz_chunk maps to s (an involution), the lane
-  // fetches global chunk swz_chunk(r, l % 8).
-  // Sources are buffer descriptors (one per weight matrix of this expert,
-  // one for this tile's token rows); a load past a descriptor's size
-  // returns zeros, so edge rows (weight rows >= Nout, token rows >= rows)
-  // need no clamping and their results are never stored.  Per-lane byte
-  // offsets stay fixed; the reduction position rides in the scalar offset.
-  const size_t wexp = (size_t)e * Nout * Kdim;
-  const uint32_t wbytes = (uint32_t)((size_t)Nout * Kdim * sizeof(bf16));
-  const __amdgpu_buffer_rsrc_t wr0 =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(w0 + wexp), 0, wbytes, kBufferFlags);
-  const __amdgpu_buffer_rsrc_t wr1 = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)((kDual ? w1 : w0) + wexp), 0, wbytes, kBufferFlags);
-  const __amdgpu_buffer_rsrc_t ar = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(act + (size_t)row0 * Kdim), 0,
-      (uint32_t)((size_t)rows * Kdim * sizeof(bf16)), kBufferFlags);
-  const int grow = lane >> 3;                   // row within the wave's 8
-  int w_src[G::kWLoads];
+    // Global -> LDS.  Loads go straight into LDS (buffer_load ... lds): a
+    // wave-wide load writes its 64 lanes' 16-byte pieces to 1 KB of
+    // consecutive LDS, i.e. 8 rows of 128 bytes.  Lane l fills slot l % 8 of
+    // row r = (its group's first row) + l / 8, and since slot s of row r must
+    // hold the chunk that swz_chunk maps to s (an involution), the lane
+    // fetches global chunk swz_chunk(r, l % 8).
+    // Sources are buffer descriptors (one per weight matrix of this expert,
+    // one for this tile's token rows); a load past a descriptor's size
+    // returns zeros, so edge rows (weight rows >= Nout, token rows >= rows)
+    // need no clamping and their results are never stored.  Per-lane byte
+    // offsets stay fixed; the reduction position rides in the scalar offset.
+    const size_t wexp = (size_t)e * Nout * Kdim;
+    const uint32_t wbytes = (uint32_t)((size_t)Nout * Kdim * sizeof(bf16));
+    const __amdgpu_buffer_rsrc_t wr0 =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(w0 + wexp), 0, wbytes, kBufferFlags);
+    const __amdgpu_buffer_rsrc_t wr1 = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)((kDual ? w1 : w0) + wexp), 0, wbytes, kBufferFlags);
+    const __amdgpu_buffer_rsrc_t ar = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(act + (size_t)row0 * Kdim), 0,
+        (uint32_t)((size_t)rows * Kdim * sizeof(bf16)), kBufferFlags);
+    const int grow = lane >> 3;                   // row within the wave's 8
+    int w_src[G::kWLoads];
 #pragma unroll
-  for (int i = 0; i < G::kWLoads; ++i) {
-    const int lr = (i * NW + wave) * 8 + grow;
-    const int n = kDual ? n0 + (lr & (kBW / 2 - 1)) : n0 + lr;
-    w_src[i] = (n * Kdim + swz_chunk(lr, lane & 7) * 8) * (int)sizeof(bf16);
-  }
-  int a_src[G::kALoads];
-#pragma unroll
-  for (int i = 0; i < G::kALoads; ++i) {
-    const int lr = (i * NW + wave) * 8 + grow;
-    a_src[i] = (lr * Kdim + swz_chunk(lr, lane & 7) * 8) * (int)sizeof(bf16);
-  }
-  char* const lds_bytes = reinterpret_cast<char*>(lds);
-  // (offsets go through locals and each descriptor has its own call: an
-  // array element or a conditional expression of descriptor type as a
-  // builtin argument here drops the kernel's host-side stub)
-  // (LDS destinations and operand sources are byte offsets of a ring slot)
-  auto issue_wload = [&](int woff, int k0, int i) __attribute__((always_inline)) {
-    const int voff = w_src[i];
-    const int soff = (kofs + k0) * (int)sizeof(bf16);
-    lds_void_t* dst = (lds_void_t*)(lds_bytes + woff + (i * NW + wave) * 8 * kRowBytes);
-    if (kDual && i >= G::kWLoads / 2)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(wr1, dst, 16, voff, soff, 0, 0);
-    else
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(wr0, dst, 16, voff, soff, 0, 0);
-  };
-  auto issue_aload = [&](int aoff, int k0, int i) __attribute__((always_inline)) {
-    const int voff = a_src[i];
-    const int soff = (kofs + k0) * (int)sizeof(bf16);
-    lds_void_t* dst = (lds_void_t*)(lds_bytes + aoff + (i * NW + wave) * 8 * kRowBytes);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(ar, dst, 16, voff, soff, 0, 0);
-  };
-
-  // Wave tiling.  In the gate/up pass the first half of a wave's weight
-  // tiles are gate rows and the second half the up rows of the same output
-  // features, so SwiGLU pairs accumulator i with i + kTW / 2.
-  const int wm = wave % WM;
-  const int wn = wave / WM;
-  int wrow[G::kTW];
-#pragma unroll
-  for (int i = 0; i < G::kTW; ++i) {
-    if (kDual) {
-      constexpr int kHalf = G::kTW / 2;
-      wrow[i] = (i / kHalf) * (kBW / 2) + wn * (kBW / 2 / G::kWN) + (i % kHalf) * 32;
-    } else {
-      wrow[i] = wn * (kBW / G::kWN) + i * 32;
+    for (int i = 0; i < G::kWLoads; ++i) {
+      const int lr = (i * NW + wave) * 8 + grow;
+      const int n = kDual ? n0 + (lr & (kBW / 2 - 1)) : n0 + lr;
+      w_src[i] = (n * Kdim + swz_chunk(lr, lane & 7) * 8) * (int)sizeof(bf16);
     }
-  }
-  const int arow0 = wm * (BM / WM);
-  // this wave's 32-token subtiles that hold at least one of the tile's rows
-  const int jlim = min(G::kTM, max(0, (rows - arow0 + 31) / 32));
-  const int lrow = lane & 31;
-  const int lhalf = lane >> 5;
-
-  f32x16 acc[G::kTW][G::kTM];
+    int a_src[G::kALoads];
 #pragma unroll
-  for (int i = 0; i < G::kTW; ++i)
-#pragma unroll
-    for (int j = 0; j < G::kTM; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-
-  // LDS byte addresses of this lane's MFMA operands.  Operand tiles start
-  // at multiples of 32 rows, so the swizzle of row (tile + lane % 32) is
-  // that of lane % 32 and one per-lane base per reduction step ks covers
-  // every operand tile.
-  int wbase[kBK / 16], abase[kBK / 16];
-#pragma unroll
-  for (int ks = 0; ks < kBK / 16; ++ks) {
-    const int chunk = ks * 2 + lhalf;
-    wbase[ks] = swz(wrow[0] + lrow, chunk) * (int)sizeof(bf16);
-    abase[ks] = swz(arow0 + lrow, chunk) * (int)sizeof(bf16);
-  }
-
-  // MFMA operands of one 16-wide reduction step, double-buffered in
-  // registers: the LDS reads of step ks + 1 are spread between the MFMAs of
-  // step ks.
-  bf16x8 wf[2][G::kTW], af[2][G::kTM];
-  constexpr int kFrags = G::kTW + G::kTM;  // LDS reads per step
-  auto read_frag = [&](int aoff, int woff, int ks, int buf, int r) __attribute__((always_inline)) {
-    if (r < G::kTW)
-      wf[buf][r] = *reinterpret_cast<const bf16x8*>(
-          lds_bytes + woff + wbase[ks] + (wrow[r] - wrow[0]) * kRowBytes);
-    else
-      af[buf][r - G::kTW] = *reinterpret_cast<const bf16x8*>(
-          lds_bytes + aoff + abase[ks] + (r - G::kTW) * 32 * kRowBytes);
-  };
-  // MFMAs of weight tiles [I0, I1) on operand buffer `buf`, for the first
-  // JN token subtiles.  If kReads, the operand reads of reduction step ks
-  // from the ring slots at byte offsets (aoff, woff) into buffer rbuf are
-  // spread evenly between them (reads of subtiles that are skipped are left
-  // out), and so are the activation loads [A0, A1) into the slot at aoff_ld
-  // and the weight loads [W0, W1) into the slot at woff_ld of later tiles.
-  // A scheduling fence after every MFMA slot keeps this exact order: left
-  // alone, the compiler sinks each read next to its first use and bunches
-  // the loads, leaving the matrix cores idle meanwhile.
-  auto mfma_step = [&](auto jn_c, auto i0_c, auto i1_c, auto reads_c, auto a0_c, auto a1_c,
-                       auto w0_c, auto w1_c, int buf, int aoff, int woff, int ks, int rbuf,
-                       int aoff_ld, int ak0, int woff_ld, int wk0) __attribute__((always_inline)) {
-    constexpr int JN = decltype(jn_c)::value;
-    constexpr int I0 = decltype(i0_c)::value;
-    constexpr int I1 = decltype(i1_c)::value;
-    constexpr bool kReads = decltype(reads_c)::value && JN > 0;
-    constexpr int A0 = decltype(a0_c)::value, A1 = decltype(a1_c)::value;
-    constexpr int W0 = decltype(w0_c)::value, W1 = decltype(w1_c)::value;
-    constexpr int n = (I1 - I0) * G::kTM;
-#pragma unroll
-    for (int m = 0; m < n; ++m) {
-#pragma unroll
-      for (int l = A0 + (m * (A1 - A0) + n - 1) / n; l < A0 + ((m + 1) * (A1 - A0) + n - 1) / n;
-           ++l)
-        issue_aload(aoff_ld, ak0, l);
-#pragma unroll
-      for (int l = W0 + (m * (W1 - W0) + n - 1) / n; l < W0 + ((m + 1) * (W1 - W0) + n - 1) / n;
-           ++l)
-        issue_wload(woff_ld, wk0, l);
-      if (kReads) {
-#pragma unroll
-        for (int r = (m * kFrags + n - 1) / n; r < ((m + 1) * kFrags + n - 1) / n; ++r)
-          if (r < G::kTW + JN) read_frag(aoff, woff, ks, rbuf, r);
-      }
-      const int i = I0 + m / G::kTM;
-      const int j = m % G::kTM;
-      if (j < JN)  // 32-token subtiles past the tile's last row are skipped
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[buf][i], af[buf][j],
-                                                            acc[i][j], 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
+    for (int i = 0; i < G::kALoads; ++i) {
+      const int lr = (i * NW + wave) * 8 + grow;
+      a_src[i] = (lr * Kdim + swz_chunk(lr, lane & 7) * 8) * (int)sizeof(bf16);
     }
-  };
-  using IC0 = std::integral_constant<int, 0>;
-  using IC1 = std::integral_constant<int, 1>;
-  using ICH = std::integral_constant<int, G::kTW / 2>;
-  using ICW = std::integral_constant<int, G::kTW>;
-  using AA = std::integral_constant<int, G::kALoads>;
-  using WA = std::integral_constant<int, G::kWLoads>;
-  using YES = std::true_type;
-  using NO = std::false_type;
-  auto wslot_off = [](int u) __attribute__((always_inline)) {
-    return G::kWRegion + u * G::kWSlotBytes;
-  };
-  auto fence_free_barrier = []() __attribute__((always_inline)) {
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-  };
-
-  // One reduction tile kt: activations on LDS stage S = kt % 2, weights in
-  // slot u = kt % 3 of a three-slot ring.  Step 0 loads tile kt + 1's
-  // activations into the other stage and step 1 loads tile kt + 2's weights
-  // into slot (u + 2) % 3; both targets were last read by tile kt - 1, which
-  // every wave finished ahead of the barrier that closed it.  Halfway
-  // through the last step this wave waits until only the weight loads of
-  // tile kt + 2 may be outstanding (so tile kt + 1 has landed) and meets the
-  // others at a barrier, after which every wave's loads of tile kt + 1 are
-  // visible; tile kt + 1's first operands are then read between the last
-  // MFMAs.  Weights, which come from HBM more often, thus get two tiles'
-  // time to arrive.  The barrier has no memory fence: a fence would also
-  // wait for the weight loads still in flight.  The body has no branches:
-  // past the last tile the loads repeat the last tile (into buffers no one
-  // reads again) and the trailing reads go unused.
-  static_assert(kBK / 16 == 4, "four reduction steps per tile");
-  static_assert(G::kWLoads == 8 || G::kWLoads == 4, "vmcnt immediate");
-  const int nk = unit.ke - unit.kb;  // reduction tiles of this unit
-  auto tile_step = [&](auto jn_c, auto stage_c, int kt, int u) __attribute__((always_inline)) {
-    constexpr int S = decltype(stage_c)::value;
-    constexpr int ao = S * G::kAStageBytes, ao1 = (1 - S) * G::kAStageBytes;
-    const int ak0 = min(kt + 1, nk - 1) * kBK;
-    const int wk0 = min(kt + 2, nk - 1) * kBK;
-    const int wo = wslot_off(u);
-    const int wo1 = wslot_off(u == 2 ? 0 : u + 1);
-    const int wo2 = wslot_off(u == 0 ? 2 : u - 1);
-    mfma_step(jn_c, IC0{}, ICW{}, YES{}, IC0{}, AA{}, IC0{}, IC0{}, 0, ao, wo, 1, 1, ao1, ak0, 0, 0);
-    mfma_step(jn_c, IC0{}, ICW{}, YES{}, IC0{}, IC0{}, IC0{}, WA{}, 1, ao, wo, 2, 0, 0, 0, wo2, wk0);
-    mfma_step(jn_c, IC0{}, ICW{}, YES{}, IC0{}, IC0{}, IC0{}, IC0{}, 0, ao, wo, 3, 1, 0, 0, 0, 0);
-    mfma_step(jn_c, IC0{}, ICH{}, NO{}, IC0{}, IC0{}, IC0{}, IC0{}, 1, 0, 0, 0, 0, 0, 0, 0, 0);
-    if constexpr (G::kWLoads == 8)
-      asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-    else
-      asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-    fence_free_barrier();
-    mfma_step(jn_c, ICH{}, ICW{}, YES{}, IC0{}, IC0{}, IC0{}, IC0{}, 1, ao1, wo1, 0, 0, 0, 0, 0,
-              0);
-  };
-  using St0 = std::integral_constant<int, 0>;
-  using St1 = std::integral_constant<int, 1>;
-
-  // Tiles in pairs (stage 0, stage 1); an odd count starts with one tile
-  // on stage 0 and pairs (stage 1, stage 0) after it.  JN is the number of
-  // this wave's 32-token subtiles that are multiplied: a ragged last tile of
-  // an expert has all-zero subtiles past its last row, and the loop comes in
-  // variants that skip them (a run-time test per MFMA would force the
-  // accumulators out of registers).
-  auto main_loop = [&](auto jn_c) __attribute__((always_inline)) {
-    // prologue: weights of tile 0, activations of tile 0, weights of tile
-    // 1; wait for the first two
-#pragma unroll
-    for (int l = 0; l < G::kWLoads; ++l) issue_wload(wslot_off(0), 0, l);
-#pragma unroll
-    for (int l = 0; l < G::kALoads; ++l) issue_aload(0, 0, l);
-#pragma unroll
-    for (int l = 0; l < G::kWLoads; ++l) issue_wload(wslot_off(1), min(1, nk - 1) * kBK, l);
-    if constexpr (G::kWLoads == 8)
-      asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-    else
-      asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-    fence_free_barrier();
-    constexpr int JN = decltype(jn_c)::value;
-#pragma unroll
-    for (int r = 0; r < kFrags; ++r)
-      if (JN > 0 && r < G::kTW + JN) read_frag(0, wslot_off(0), 0, 0, r);
-    int u = 0;  // weight slot of the current tile, kt % 3
-    auto next = [](int v) { return v == 2 ? 0 : v + 1; };
-    if (nk & 1) {
-      tile_step(jn_c, St0{}, 0, u);
-      u = next(u);
-      for (int kt = 1; kt < nk; kt += 2) {
-        tile_step(jn_c, St1{}, kt, u);
-        u = next(u);
-        tile_step(jn_c, St0{}, kt + 1, u);
-        u = next(u);
-      }
-    } else {
-      for (int kt = 0; kt < nk; kt += 2) {
-        tile_step(jn_c, St0{}, kt, u);
-        u = next(u);
-        tile_step(jn_c, St1{}, kt + 1, u);
-        u = next(u);
-      }
-    }
-  };
-
-  // Thin tiles: reduction tile kt has both operands in slot u = kt % 4 of
-  // four-slot rings.  Steps 0 and 1 load tile kt + 3's activations and
-  // weights into slot (u + 3) % 4, last read by tile kt - 1; halfway through
-  // the last step the wave waits until only the loads of tiles kt + 2 and
-  // kt + 3 may be outstanding, then meets the others at the barrier, as
-  // above.
-  using TA = std::integral_constant<int, G::kThinALoads>;
-  auto thin_wait = []() __attribute__((always_inline)) {
-    // the loads of two tiles, 2 x (kThinALoads + 8) per wave, may be in flight
-    if constexpr (G::kThinALoads == 2)
-      asm volatile("s_waitcnt vmcnt(20)" ::: "memory");
-    else
-      asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
-  };
-  auto thin_step = [&](auto jn_c, int kt, int u) __attribute__((always_inline)) {
-    const int k3 = min(kt + 3, nk - 1) * kBK;
-    const int ao = u * G::kThinABytes, wo = G::kThinWRegion + u * G::kWSlotBytes;
-    const int u1 = (u + 1) & 3, u3 = (u + 3) & 3;
-    const int ao3 = u3 * G::kThinABytes, wo3 = G::kThinWRegion + u3 * G::kWSlotBytes;
-    mfma_step(jn_c, IC0{}, ICW{}, YES{}, IC0{}, TA{}, IC0{}, IC0{}, 0, ao, wo, 1, 1, ao3, k3, 0, 0);
-    mfma_step(jn_c, IC0{}, ICW{}, YES{}, IC0{}, IC0{}, IC0{}, WA{}, 1, ao, wo, 2, 0, 0, 0, wo3, k3);
-    mfma_step(jn_c, IC0{}, ICW{}, YES{}, IC0{}, IC0{}, IC0{}, IC0{}, 0, ao, wo, 3, 1, 0, 0, 0, 0);
-    mfma_step(jn_c, IC0{}, ICH{}, NO{}, IC0{}, IC0{}, IC0{}, IC0{}, 1, 0, 0, 0, 0, 0, 0, 0, 0);
-    thin_wait();
-    fence_free_barrier();
-    mfma_step(jn_c, ICH{}, ICW{}, YES{}, IC0{}, IC0{}, IC0{}, IC0{}, 1, u1 * G::kThinABytes,
-              G::kThinWRegion + u1 * G::kWSlotBytes, 0, 0, 0, 0, 0, 0);
-  };
-  auto thin_loop = [&](auto jn_c) __attribute__((always_inline)) {
-    static_assert(G::kWLoads == 8, "vmcnt immediate");
-    // prologue: tiles 0, 1 and 2 (activations, then weights); wait for tile 0
-#pragma unroll
-    for (int t = 0; t < 3; ++t) {
-      const int k0 = min(t, nk - 1) * kBK;
-#pragma unroll
-      for (int l = 0; l < G::kThinALoads; ++l) issue_aload(t * G::kThinABytes, k0, l);
-#pragma unroll
-      for (int l = 0; l < G::kWLoads; ++l)
-        issue_wload(G::kThinWRegion + t * G::kWSlotBytes, k0, l);
-    }
-    thin_wait();
-    fence_free_barrier();
-    constexpr int JN = decltype(jn_c)::value;
-#pragma unroll
-    for (int r = 0; r < kFrags; ++r)
-      if (JN > 0 && r < G::kTW + JN) read_frag(0, G::kThinWRegion, 0, 0, r);
-    for (int kt = 0; kt < nk; ++kt) thin_step(jn_c, kt, kt & 3);
-  };
-
-  constexpr int kTM = G::kTM;
-  if constexpr (G::kThin) {
-    if (rows <= G::kThinRows) {
-      // only the first kThinRows / 32 token subtiles of wave row 0 hold rows
-      if (G::kThinRows > 32 && jlim >= 2)
-        thin_loop(std::integral_constant<int, (G::kThinRows > 32 ? 2 : 1)>{});
-      else if (jlim >= 1)
-        thin_loop(IC1{});
+    char* const lds_bytes = reinterpret_cast<char*>(lds);
+    // (offsets go through locals and each descriptor has its own call: an
+    // array element or a conditional expression of descriptor type as a
+    // builtin argument here drops the kernel's host-side stub)
+    // (LDS destinations and operand sources are byte offsets of a ring slot)
+    auto issue_wload = [&](int woff, int k0, int i) __attribute__((always_inline)) {
+      const int voff = w_src[i];
+      const int soff = (kofs + k0) * (int)sizeof(bf16);
+      lds_void_t* dst = (lds_void_t*)(lds_bytes + woff + (i * NW + wave) * 8 * kRowBytes);
+      if (kDual && i >= G::kWLoads / 2)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(wr1, dst, 16, voff, soff, 0, 0);
       else
-        thin_loop(IC0{});
-    } else if constexpr (kTM > 1) {
-      if (jlim >= kTM || (kTM > 2 && jlim > 2))
-        main_loop(std::integral_constant<int, kTM>{});
-      else if (kTM > 2 && jlim == 2)
-        main_loop(std::integral_constant<int, (kTM > 2 ? 2 : kTM)>{});
-      else if (jlim == 1)
-        main_loop(IC1{});
-      else
-        main_loop(IC0{});
-    }
-  } else {
-    if (jlim >= kTM || (kTM > 2 && jlim > 2))
-      main_loop(std::integral_constant<int, kTM>{});
-    else if (kTM > 2 && jlim == 2)
-      main_loop(std::integral_constant<int, (kTM > 2 ? 2 : kTM)>{});
-    else if (kTM > 1 && jlim == 1)
-      main_loop(std::integral_constant<int, (kTM > 1 ? 1 : kTM)>{});
-    else
-      main_loop(IC0{});
-  }
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(wr0, dst, 16, voff, soff, 0, 0);
+    };
+    auto issue_aload = [&](int aoff, int k0, int i) __attribute__((always_inline)) {
+      const int voff = a_src[i];
+      const int soff = (kofs + k0) * (int)sizeof(bf16);
+      lds_void_t* dst = (lds_void_t*)(lds_bytes + aoff + (i * NW + wave) * 8 * kRowBytes);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ar, dst, 16, voff, soff, 0, 0);
+    };
 
-  // A piece of a split tile.  Its accumulators go to its workspace slot in
-  // register order (lane-contiguous 64-byte runs); every thread makes its
-  // stores visible device-wide (other XCDs' L2s included) before the block
-  // counts itself in, so the piece that arrives last sees every piece, adds
-  // them in piece order into its accumulators, re-arms the counter for the
-  // next launch and goes on to the ordinary epilogue.  No block waits on
-  // another.
-  if (unit.parts > 1) {
-    constexpr int kUnitFloats = NW * G::kTW * G::kTM * kWave * 16;
-    float* const base = partial + (size_t)unit.pslot0 * kUnitFloats +
-                        (size_t)wave * (G::kTW * G::kTM * kWave * 16) + lane * 16;
-    float* const mine = base + (size_t)unit.piece * kUnitFloats;
+    // Wave tiling.  In the gate/up pass the first half of a wave's weight
+    // tiles are gate rows and the second half the up rows of the same output
+    // features, so SwiGLU pairs accumulator i with i + kTW / 2.
+    const int wm = wave % WM;
+    const int wn = wave / WM;
+    int wrow[G::kTW];
+#pragma unroll
+    for (int i = 0; i < G::kTW; ++i) {
+      if (kDual) {
+        constexpr int kHalf = G::kTW / 2;
+        wrow[i] = (i / kHalf) * (kBW / 2) + wn * (kBW / 2 / G::kWN) + (i % kHalf) * 32;
+      } else {
+        wrow[i] = wn * (kBW / G::kWN) + i * 32;
+      }
+    }
+    const int arow0 = wm * (BM / WM);
+    // this wave's 32-token subtiles that hold at least one of the tile's rows
+    const int jlim = min(G::kTM, max(0, (rows - arow0 + 31) / 32));
+    const int lrow = lane & 31;
+    const int lhalf = lane >> 5;
+
+    f32x16 acc[G::kTW][G::kTM];
 #pragma unroll
     for (int i = 0; i < G::kTW; ++i)
 #pragma unroll
       for (int j = 0; j < G::kTM; ++j)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          f32x4 v;
-#pragma unroll
-          for (int c = 0; c < 4; ++c) v[c] = acc[i][j][q * 4 + c];
-          *reinterpret_cast<f32x4*>(mine + (i * G::kTM + j) * kWave * 16 + q * 4) = v;
-        }
-    __threadfence();
-    __syncthreads();  // also: every wave is done reading operand LDS
-    int* const flag = reinterpret_cast<int*>(lds);
-    if (threadIdx.x == 0) *flag = atomicAdd(&split_cnt[unit.split], 1);
-    __syncthreads();
-    if (*flag != unit.parts - 1) return;
-    __threadfence();
-#pragma unroll
-    for (int i = 0; i < G::kTW; ++i)
-#pragma unroll
-      for (int j = 0; j < G::kTM; ++j) {
-        f32x16 sum;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sum[r] = 0.0f;
-        for (int p = 0; p < unit.parts; ++p) {
-          const float* src = base + (size_t)p * kUnitFloats + (i * G::kTM + j) * kWave * 16;
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const f32x4 v = *reinterpret_cast<const f32x4*>(src + q * 4);
-#pragma unroll
-            for (int c = 0; c < 4; ++c) sum[q * 4 + c] += v[c];
-          }
-        }
-        acc[i][j] = sum;
-      }
-    if (threadIdx.x == 0) split_cnt[unit.split] = 0;
-  }
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  // Epilogue.  Accumulator register r of lane l holds weight row
-  // (r / 4) * 8 + (l / 32) * 4 + r % 4 of its 32-row weight tile and token
-  // l % 32 of its 32-row token tile: runs of 4 consecutive output features.
+    // LDS byte addresses of this lane's MFMA operands.  Operand tiles start
+    // at multiples of 32 rows, so the swizzle of row (tile + lane % 32) is
+    // that of lane % 32 and one per-lane base per reduction step ks covers
+    // every operand tile.
+    int wbase[kBK / 16], abase[kBK / 16];
 #pragma unroll
-  for (int j = 0; j < G::kTM; ++j) {
-    const int m_local = arow0 + j * 32 + lrow;
-    if (m_local >= rows) continue;
-    bf16* orow = out + (size_t)(row0 + m_local) * Nout;
-    if (kDual) {
-      constexpr int kHalf = G::kTW / 2;
+    for (int ks = 0; ks < kBK / 16; ++ks) {
+      const int chunk = ks * 2 + lhalf;
+      wbase[ks] = swz(wrow[0] + lrow, chunk) * (int)sizeof(bf16);
+      abase[ks] = swz(arow0 + lrow, chunk) * (int)sizeof(bf16);
+    }
+
+    // MFMA operands of one 16-wide reduction step, double-buffered in
+    // registers: the LDS reads of step ks + 1 are spread between the MFMAs of
+    // step ks.
+    bf16x8 wf[2][G::kTW], af[2][G::kTM];
+    constexpr int kFrags = G::kTW + G::kTM;  // LDS reads per step
+    auto read_frag = [&](int aoff, int woff, int ks, int buf, int r) __attribute__((always_inline)) {
+      if (r < G::kTW)
+        wf[buf][r] = *reinterpret_cast<const bf16x8*>(
+            lds_bytes + woff + wbase[ks] + (wrow[r] - wrow[0]) * kRowBytes);
+      else
+        af[buf][r - G::kTW] = *reinterpret_cast<const bf16x8*>(
+            lds_bytes + aoff + abase[ks] + (r - G::kTW) * 32 * kRowBytes);
+    };
+    // MFMAs of weight tiles [I0, I1) on operand buffer `buf`, for the first
+    // JN token subtiles.  If kReads, the operand reads of reduction step ks
+    // from the ring slots at byte offsets (aoff, woff) into buffer rbuf are
+    // spread evenly between them (reads of subtiles that are skipped are left
+    // out), and so are the activation loads [A0, A1) into the slot at aoff_ld
+    // and the weight loads [W0, W1) into the slot at woff_ld of later tiles.
+    // A scheduling fence after every MFMA slot keeps this exact order: left
+    // alone, the compiler sinks each read next to its first use and bunches
+    // the loads, leaving the matrix cores idle meanwhile.
+    auto mfma_step = [&](auto jn_c, auto i0_c, auto i1_c, auto reads_c, auto a0_c, auto a1_c,
+                         auto w0_c, auto w1_c, int buf, int aoff, int woff, int ks, int rbuf,
+                         int aoff_ld, int ak0, int woff_ld, int wk0) __attribute__((always_inline)) {
+      constexpr int JN = decltype(jn_c)::value;
+      constexpr int I0 = decltype(i0_c)::value;
+      constexpr int I1 = decltype(i1_c)::value;
+      constexpr bool kReads = decltype(reads_c)::value && JN > 0;
+      constexpr int A0 = decltype(a0_c)::value, A1 = decltype(a1_c)::value;
+      constexpr int W0 = decltype(w0_c)::value, W1 = decltype(w1_c)::value;
+      constexpr int n = (I1 - I0) * G::kTM;
 #pragma unroll
-      for (int i = 0; i < kHalf; ++i) {
+      for (int m = 0; m < n; ++m) {
 #pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          const int f = n0 + wrow[i] + r4 * 8 + lhalf * 4;
-          if (f >= Nout) continue;
-          bf16x4 o;
+        for (int l = A0 + (m * (A1 - A0) + n - 1) / n; l < A0 + ((m + 1) * (A1 - A0) + n - 1) / n;
+             ++l)
+          issue_aload(aoff_ld, ak0, l);
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const float g = acc[i][j][r4 * 4 + q];
-            const float u = acc[i + kHalf][j][r4 * 4 + q];
-            o[q] = (bf16)(g / (1.0f + __expf(-g)) * u);
-          }
-          *reinterpret_cast<bf16x4*>(orow + f) = o;
+        for (int l = W0 + (m * (W1 - W0) + n - 1) / n; l < W0 + ((m + 1) * (W1 - W0) + n - 1) / n;
+             ++l)
+          issue_wload(woff_ld, wk0, l);
+        if (kReads) {
+#pragma unroll
+          for (int r = (m * kFrags + n - 1) / n; r < ((m + 1) * kFrags + n - 1) / n; ++r)
+            if (r < G::kTW + JN) read_frag(aoff, woff, ks, rbuf, r);
         }
+        const int i = I0 + m / G::kTM;
+        const int j = m % G::kTM;
+        if (j < JN)  // 32-token subtiles past the tile's last row are skipped
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[buf][i], af[buf][j],
+                                                              acc[i][j], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    using IC0 = std::integral_constant<int, 0>;
+    using IC1 = std::integral_constant<int, 1>;
+    using ICH = std::integral_constant<int, G::kTW / 2>;
+    using ICW = std::integral_constant<int, G::kTW>;
+    using AA = std::integral_constant<int, G::kALoads>;
+    using WA = std::integral_constant<int, G::kWLoads>;
+    using YES = std::true_type;
+    using NO = std::false_type;
+    auto wslot_off = [](int u) __attribute__((always_inline)) {
+      return G::kWRegion + u * G::kWSlotBytes;
+    };
+    auto fence_free_barrier = []() __attribute__((always_inline)) {
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+    };
+
+    // One reduction tile kt: activations on LDS stage S = kt % 2, weights in
+    // slot u = kt % 3 of a three-slot ring.  Step 0 loads tile kt + 1's
+    // activations into the other stage and step 1 loads tile kt + 2's weights
+    // into slot (u + 2) % 3; both targets were last read by tile kt - 1, which
+    // every wave finished ahead of the barrier that closed it.  Halfway
+    // through the last step this wave waits until only the weight loads of
+    // tile kt + 2 may be outstanding (so tile kt + 1 has landed) and meets the
+    // others at a barrier, after which every wave's loads of tile kt + 1 are
+    // visible; tile kt + 1's first operands are then read between the last
+    // MFMAs.  Weights, which come from HBM more often, thus get two tiles'
+    // time to arrive.  The barrier has no memory fence: a fence would also
+    // wait for the weight loads still in flight.  The body has no branches:
+    // past the last tile the loads repeat the last tile (into buffers no one
+    // reads again) and the trailing reads go unused.
+    static_assert(kBK / 16 == 4, "four reduction steps per tile");
+    static_assert(G::kWLoads == 8 || G::kWLoads == 4, "vmcnt immediate");
+    const int nk = unit.ke - unit.kb;  // reduction tiles of this unit
+    auto tile_step = [&](auto jn_c, auto stage_c, int kt, int u) __attribute__((always_inline)) {
+      constexpr int S = decltype(stage_c)::value;
+      constexpr int ao = S * G::kAStageBytes, ao1 = (1 - S) * G::kAStageBytes;
+      const int ak0 = min(kt + 1, nk - 1) * kBK;
+      const int wk0 = min(kt + 2, nk - 1) * kBK;
+      const int wo = wslot_off(u);
+      const int wo1 = wslot_off(u == 2 ? 0 : u + 1);
+      const int wo2 = wslot_off(u == 0 ? 2 : u - 1);
+      mfma_step(jn_c, IC0{}, ICW{}, YES{}, IC0{}, AA{}, IC0{}, IC0{}, 0, ao, wo, 1, 1, ao1, ak0, 0, 0);
+      mfma_step(jn_c, IC0{}, ICW{}, YES{}, IC0{}, IC0{}, IC0{}, WA{}, 1, ao, wo, 2, 0, 0, 0, wo2, wk0);
+      mfma_step(jn_c, IC0{}, ICW{}, YES{}, IC0{}, IC0{}, IC0{}, IC0{}, 0, ao, wo, 3, 1, 0, 0, 0, 0);
+      mfma_step(jn_c, IC0{}, ICH{}, NO{}, IC0{}, IC0{}, IC0{}, IC0{}, 1, 0, 0, 0, 0, 0, 0, 0, 0);
+      if constexpr (G::kWLoads == 8)
+        asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+      else
+        asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+      fence_free_barrier();
+      mfma_step(jn_c, ICH{}, ICW{}, YES{}, IC0{}, IC0{}, IC0{}, IC0{}, 1, ao1, wo1, 0, 0, 0, 0, 0,
+                0);
+    };
+    using St0 = std::integral_constant<int, 0>;
+    using St1 = std::integral_constant<int, 1>;
+
+    // Tiles in pairs (stage 0, stage 1); an odd count starts with one tile
+    // on stage 0 and pairs (stage 1, stage 0) after it.  JN is the number of
+    // this wave's 32-token subtiles that are multiplied: a ragged last tile of
+    // an expert has all-zero subtiles past its last row, and the loop comes in
+    // variants that skip them (a run-time test per MFMA would force the
+    // accumulators out of registers).
+    auto main_loop = [&](auto jn_c) __attribute__((always_inline)) {
+      // prologue: weights of tile 0, activations of tile 0, weights of tile
+      // 1; wait for the first two
+#pragma unroll
+      for (int l = 0; l < G::kWLoads; ++l) issue_wload(wslot_off(0), 0, l);
+#pragma unroll
+      for (int l = 0; l < G::kALoads; ++l) issue_aload(0, 0, l);
+#pragma unroll
+      for (int l = 0; l < G::kWLoads; ++l) issue_wload(wslot_off(1), min(1, nk - 1) * kBK, l);
+      if constexpr (G::kWLoads == 8)
+        asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+      else
+        asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+      fence_free_barrier();
+      constexpr int JN = decltype(jn_c)::value;
+#pragma unroll
+      for (int r = 0; r < kFrags; ++r)
+        if (JN > 0 && r < G::kTW + JN) read_frag(0, wslot_off(0), 0, 0, r);
+      int u = 0;  // weight slot of the current tile, kt % 3
+      auto next = [](int v) { return v == 2 ? 0 : v + 1; };
+      if (nk & 1) {
+        tile_step(jn_c, St0{}, 0, u);
+        u = next(u);
+        for (int kt = 1; kt < nk; kt += 2) {
+          tile_step(jn_c, St1{}, kt, u);
+          u = next(u);
+          tile_step(jn_c, St0{}, kt + 1, u);
+          u = next(u);
+        }
+      } else {
+        for (int kt = 0; kt < nk; kt += 2) {
+          tile_step(jn_c, St0{}, kt, u);
+          u = next(u);
+          tile_step(jn_c, St1{}, kt + 1, u);
+          u = next(u);
+        }
+      }
+    };
+
+    // Thin tiles: reduction tile kt has both operands in slot u = kt % 4 of
+    // four-slot rings.  Steps 0 and 1 load tile kt + 3's activations and
+    // weights into slot (u + 3) % 4, last read by tile kt - 1; halfway through
+    // the last step the wave waits until only the loads of tiles kt + 2 and
+    // kt + 3 may be outstanding, then meets the others at the barrier, as
+    // above.
+    using TA = std::integral_constant<int, G::kThinALoads>;
+    auto thin_wait = []() __attribute__((always_inline)) {
+      // the loads of two tiles, 2 x (kThinALoads + 8) per wave, may be in flight
+      if constexpr (G::kThinALoads == 2)
+        asm volatile("s_waitcnt vmcnt(20)" ::: "memory");
+      else
+        asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
+    };
+    auto thin_step = [&](auto jn_c, int kt, int u) __attribute__((always_inline)) {
+      const int k3 = min(kt + 3, nk - 1) * kBK;
+      const int ao = u * G::kThinABytes, wo = G::kThinWRegion + u * G::kWSlotBytes;
+      const int u1 = (u + 1) & 3, u3 = (u + 3) & 3;
+      const int ao3 = u3 * G::kThinABytes, wo3 = G::kThinWRegion + u3 * G::kWSlotBytes;
+      mfma_step(jn_c, IC0{}, ICW{}, YES{}, IC0{}, TA{}, IC0{}, IC0{}, 0, ao, wo, 1, 1, ao3, k3, 0, 0);
+      mfma_step(jn_c, IC0{}, ICW{}, YES{}, IC0{}, IC0{}, IC0{}, WA{}, 1, ao, wo, 2, 0, 0, 0, wo3, k3);
+      mfma_step(jn_c, IC0{}, ICW{}, YES{}, IC0{}, IC0{}, IC0{}, IC0{}, 0, ao, wo, 3, 1, 0, 0, 0, 0);
+      mfma_step(jn_c, IC0{}, ICH{}, NO{}, IC0{}, IC0{}, IC0{}, IC0{}, 1, 0, 0, 0, 0, 0, 0, 0, 0);
+      thin_wait();
+      fence_free_barrier();
+      mfma_step(jn_c, ICH{}, ICW{}, YES{}, IC0{}, IC0{}, IC0{}, IC0{}, 1, u1 * G::kThinABytes,
+                G::kThinWRegion + u1 * G::kWSlotBytes, 0, 0, 0, 0, 0, 0);
+    };
+    auto thin_loop = [&](auto jn_c) __attribute__((always_inline)) {
+      static_assert(G::kWLoads == 8, "vmcnt immediate");
+      // prologue: tiles 0, 1 and 2 (activations, then weights); wait for tile 0
+#pragma unroll
+      for (int t = 0; t < 3; ++t) {
+        const int k0 = min(t, nk - 1) * kBK;
+#pragma unroll
+        for (int l = 0; l < G::kThinALoads; ++l) issue_aload(t * G::kThinABytes, k0, l);
+#pragma unroll
+        for (int l = 0; l < G::kWLoads; ++l)
+          issue_wload(G::kThinWRegion + t * G::kWSlotBytes, k0, l);
+      }
+      thin_wait();
+      fence_free_barrier();
+      constexpr int JN = decltype(jn_c)::value;
+#pragma unroll
+      for (int r = 0; r < kFrags; ++r)
+        if (JN > 0 && r < G::kTW + JN) read_frag(0, G::kThinWRegion, 0, 0, r);
+      for (int kt = 0; kt < nk; ++kt) thin_step(jn_c, kt, kt & 3);
+    };
+
+    constexpr int kTM = G::kTM;
+    if constexpr (G::kThin) {
+      if (rows <= G::kThinRows) {
+        // only the first kThinRows / 32 token subtiles of wave row 0 hold rows
+        if (G::kThinRows > 32 && jlim >= 2)
+          thin_loop(std::integral_constant<int, (G::kThinRows > 32 ? 2 : 1)>{});
+        else if (jlim >= 1)
+          thin_loop(IC1{});
+        else
+          thin_loop(IC0{});
+      } else if constexpr (kTM > 1) {
+        if (jlim >= kTM || (kTM > 2 && jlim > 2))
+          main_loop(std::integral_constant<int, kTM>{});
+        else if (kTM > 2 && jlim == 2)
+          main_loop(std::integral_constant<int, (kTM > 2 ? 2 : kTM)>{});
+        else if (jlim == 1)
+          main_loop(IC1{});
+        else
+          main_loop(IC0{});
       }
     } else {
+      if (jlim >= kTM || (kTM > 2 && jlim > 2))
+        main_loop(std::integral_constant<int, kTM>{});
+      else if (kTM > 2 && jlim == 2)
+        main_loop(std::integral_constant<int, (kTM > 2 ? 2 : kTM)>{});
+      else if (kTM > 1 && jlim == 1)
+        main_loop(std::integral_constant<int, (kTM > 1 ? 1 : kTM)>{});
+      else
+        main_loop(IC0{});
+    }
+
+    // The trailing repeat loads of the reduction loop land before this unit
+    // ends: the next unit's loads reuse the same LDS.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+    // A piece of a split tile.  Its accumulators go to its workspace slot in
+    // register order (lane-contiguous 64-byte runs, with the coherent policy of
+    // store_partial); once they are in memory the block counts itself in, so
+    // the piece that arrives last sees every piece, adds them in piece order
+    // into its accumulators, re-arms the counter for the next launch and goes
+    // on to the ordinary epilogue.  No block waits on another.
+    if (unit.parts > 1) {
+      constexpr int kUnitFloats = NW * G::kTW * G::kTM * kWave * 16;
+      constexpr int kUnitBytes = kUnitFloats * (int)sizeof(float);
+      const __amdgpu_buffer_rsrc_t pr = __builtin_amdgcn_make_buffer_rsrc(
+          partial + (size_t)unit.pslot0 * kUnitFloats, 0, (uint32_t)(unit.parts * kUnitBytes),
+          kBufferFlags);
+      const int lane_off =
+          (wave * (G::kTW * G::kTM * kWave * 16) + lane * 16) * (int)sizeof(float);
+      const int mine = unit.piece * kUnitBytes;
 #pragma unroll
-      for (int i = 0; i < G::kTW; ++i) {
+      for (int i = 0; i < G::kTW; ++i)
 #pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          const int f = n0 + wrow[i] + r4 * 8 + lhalf * 4;
-          if (f >= Nout) continue;
-          bf16x4 o;
+        for (int j = 0; j < G::kTM; ++j)
 #pragma unroll
-          for (int q = 0; q < 4; ++q) o[q] = (bf16)acc[i][j][r4 * 4 + q];
-          *reinterpret_cast<bf16x4*>(orow + f) = o;
+          for (int q = 0; q < 4; ++q) {
+            f32x4 v;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) v[c] = acc[i][j][q * 4 + c];
+            const int voff =
+                lane_off + ((i * G::kTM + j) * kWave * 16 + q * 4) * (int)sizeof(float);
+            store_partial(pr, voff, mine, v);
+          }
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();  // also: every wave is done reading operand LDS
+      int* const flag = reinterpret_cast<int*>(lds);
+      if (threadIdx.x == 0) *flag = atomicAdd(&split_cnt[unit.split], 1);
+      __syncthreads();
+      if (*flag != unit.parts - 1) continue;
+#pragma unroll
+      for (int i = 0; i < G::kTW; ++i)
+#pragma unroll
+        for (int j = 0; j < G::kTM; ++j) {
+          f32x16 sum;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) sum[r] = 0.0f;
+          for (int p = 0; p < unit.parts; ++p) {
+            const int soff = p * kUnitBytes;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const int voff =
+                  lane_off + ((i * G::kTM + j) * kWave * 16 + q * 4) * (int)sizeof(float);
+              const f32x4 v = load_partial(pr, voff, soff);
+#pragma unroll
+              for (int c = 0; c < 4; ++c) sum[q * 4 + c] += v[c];
+            }
+          }
+          acc[i][j] = sum;
+        }
+      if (threadIdx.x == 0) split_cnt[unit.split] = 0;
+    }
+
+    // Epilogue.  Accumulator register r of lane l holds weight row
+    // (r / 4) * 8 + (l / 32) * 4 + r % 4 of its 32-row weight tile and token
+    // l % 32 of its 32-row token tile: runs of 4 consecutive output features.
+#pragma unroll
+    for (int j = 0; j < G::kTM; ++j) {
+      const int m_local = arow0 + j * 32 + lrow;
+      if (m_local >= rows) continue;
+      bf16* orow = out + (size_t)(row0 + m_local) * Nout;
+      if (kDual) {
+        constexpr int kHalf = G::kTW / 2;
+#pragma unroll
+        for (int i = 0; i < kHalf; ++i) {
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4) {
+            const int f = n0 + wrow[i] + r4 * 8 + lhalf * 4;
+            if (f >= Nout) continue;
+            bf16x4 o;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const float g = acc[i][j][r4 * 4 + q];
+              const float u = acc[i + kHalf][j][r4 * 4 + q];
+              o[q] = (bf16)(g / (1.0f + __expf(-g)) * u);
+            }
+            *reinterpret_cast<bf16x4*>(orow + f) = o;
+          }
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < G::kTW; ++i) {
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4) {
+            const int f = n0 + wrow[i] + r4 * 8 + lhalf * 4;
+            if (f >= Nout) continue;
+            bf16x4 o;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) o[q] = (bf16)acc[i][j][r4 * 4 + q];
+            *reinterpret_cast<bf16x4*>(orow + f) = o;
+          }
         }
       }
     }
@@ -627,15 +643,13 @@ hipError_t launch_bf16_gemm(const bf16* act, int Kdim, const bf16* w0,
   if (attr != hipSuccess) return attr;
   constexpr int kNOut = kDual ? kBW / 2 : kBW;
   const int n_tiles = (Nout + kNOut - 1) / kNOut;
-  // an XCD's list holds at most max_tiles x ceil(n_tiles / 8) whole tiles,
-  // and its split pieces take at most cps more blocks
+  // one block per CU (the kernel takes a CU's LDS), 8 per XCD row
   const int cps = ffn_resident_blocks() / kXcds > 0 ? ffn_resident_blocks() / kXcds : 1;
-  const long long per_xcd = (long long)max_tiles * ((n_tiles + kXcds - 1) / kXcds) + cps;
-  const int grid = (int)(per_xcd * kXcds);
-  const int* xcd_start = ws.xcd_start + (kDual ? 0 : kXcds * (E + 1));
+  const int grid = cps * kXcds;
+  (void)max_tiles;
   ffn_gemm_bf16_kernel<BM, WM, NW, kDual><<<grid, NW * kWave, G::kLds, stream>>>(
-      act, Kdim, w0, w1, Nout, out, ws.tiles, ws.tile_start, xcd_start, E, n_tiles,
-      cps, ws.partial, ws.split_cnt + (kDual ? 0 : kMaxSplitUnits));
+      act, Kdim, w0, w1, Nout, out, ws.tiles, ws.tile_start, E,
+      n_tiles, cps, ws.partial, ws.split_cnt + (kDual ? 0 : kMaxSplitUnits));
   return hipGetLastError();
 }
 
@@ -707,12 +721,9 @@ hipError_t launch_grouped_ffn(const void* x_perm, bool bf16_data, int d,
   const int tr = bf16_data ? bf16_tile_rows(max_rows, E) : kF32TileRows;
   const int max_tiles = max_tiles_for(max_rows, E, tr);
   const FfnWorkspace ws = ffn_workspace(workspace, E, max_tiles);
-  // column tiles of the bf16 passes (the XCD tables serve only those)
-  const int n_up = (ffn + kBW / 2 - 1) / (kBW / 2);
-  const int n_dn = (d + kBW - 1) / kBW;
   ffn_schedule_kernel<<<1, 1024, 0, stream>>>(offsets, E, tr, (int)max_rows, max_tiles,
-                                              n_up, n_dn, ws.tiles, ws.tile_start,
-                                              ws.num_tiles, ws.split_cnt, ws.xcd_start);
+                                              ws.tiles, ws.tile_start, ws.num_tiles,
+                                              ws.split_cnt);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
 

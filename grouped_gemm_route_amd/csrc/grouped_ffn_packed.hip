@@ -97,8 +97,8 @@ template <int BM, bool kDual>
 __global__ __launch_bounds__(kPkWaves * kWave, 1) void ffn_gemm_packed_kernel(
     const bf16* __restrict__ act, int Kdim, const bf16* __restrict__ wpk, int Nout, int P,
     bf16* __restrict__ out, const int4* __restrict__ tiles, const int* __restrict__ tile_start,
-    const int* __restrict__ xcd_start, int E, int n_tiles, int cps,
-    float* __restrict__ partial, int* __restrict__ split_cnt) {
+    int E, int n_tiles,
+    int cps, float* __restrict__ partial, int* __restrict__ split_cnt) {
   constexpr int NW = kPkWaves;
   constexpr int kTM = BM / 32;             // 32-token operands per wave (all BM rows)
   constexpr int kTW = 4;                   // 32-row weight operands per wave (one panel)
@@ -110,286 +110,301 @@ __global__ __launch_bounds__(kPkWaves * kWave, 1) void ffn_gemm_packed_kernel(
   static_assert(kAL == kTM && kTM >= 1 && kTM <= 4, "tile shape");
   static_assert(kDist >= 4 && kDist < kRing, "weight ring");
   extern __shared__ __attribute__((aligned(16))) bf16 lds[];
-  Unit unit;
-  if (!map_unit(tile_start, xcd_start, E, n_tiles, Kdim / kBK, cps, &unit)) return;
-  const int kofs = unit.kb * kBK;
-  const int4 tile = tiles[unit.slot];
-  const int e = tile.x;
-  const int row0 = tile.y;
-  const int rows = tile.z - tile.y;
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const int pn = unit.n_tile * NW + wave;  // this wave's panel
-  const int S = Kdim / 16;
-  const int nk = unit.ke - unit.kb;        // reduction tiles of this unit
-  const int nsteps = nk * 4;
+  // One block per CU walks its XCD's list: block slot b = blockIdx.x + k
+  // gridDim.x (gridDim.x is 8 x the blocks resident per XCD), so no block is
+  // launched only to find no work.
+  for (int vb = blockIdx.x;; vb += gridDim.x) {
+    Unit unit;
+    if (!map_unit(vb, tile_start, E, n_tiles, Kdim / kBK, cps, &unit))
+      break;
+    // the previous unit's waves are done with the LDS stages
+    __syncthreads();
+    const int kofs = unit.kb * kBK;
+    const int4 tile = tiles[unit.slot];
+    const int e = tile.x;
+    const int row0 = tile.y;
+    const int rows = tile.z - tile.y;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int pn = unit.n_tile * NW + wave;  // this wave's panel
+    const int S = Kdim / 16;
+    const int nk = unit.ke - unit.kb;        // reduction tiles of this unit
+    const int nsteps = nk * 4;
 
-  // Buffer descriptors: this expert's packed weights and this tile's token
-  // rows; loads past a descriptor's size return zeros.  The panel offset
-  // rides in the per-lane offset, which the range check covers (the scalar
-  // offset is not checked), so a wave whose panel lies past the expert's
-  // last reads zeros; its results are never stored.
-  const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(wpk + (size_t)e * P * S * (kStepBytes / sizeof(bf16))), 0,
-      (uint32_t)((size_t)P * S * kStepBytes), kBufferFlags);
-  const __amdgpu_buffer_rsrc_t ar = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(act + (size_t)row0 * Kdim), 0, (uint32_t)((size_t)rows * Kdim * sizeof(bf16)),
-      kBufferFlags);
-  const int w_lane = pn * S * kStepBytes + lane * 16;
-  const int w_step0 = unit.kb * 4 * kStepBytes;
-  // direct-to-LDS activation loads: as in grouped_ffn.hip, lane l fills
-  // slot l % 8 of LDS row (group row + l / 8) with global chunk
-  // swz_chunk(row, l % 8)
-  const int grow = lane >> 3;
-  int a_src[kAL];
+    // Buffer descriptors: this expert's packed weights and this tile's token
+    // rows; loads past a descriptor's size return zeros.  The panel offset
+    // rides in the per-lane offset, which the range check covers (the scalar
+    // offset is not checked), so a wave whose panel lies past the expert's
+    // last reads zeros; its results are never stored.
+    const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(wpk + (size_t)e * P * S * (kStepBytes / sizeof(bf16))), 0,
+        (uint32_t)((size_t)P * S * kStepBytes), kBufferFlags);
+    const __amdgpu_buffer_rsrc_t ar = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(act + (size_t)row0 * Kdim), 0, (uint32_t)((size_t)rows * Kdim * sizeof(bf16)),
+        kBufferFlags);
+    const int w_lane = pn * S * kStepBytes + lane * 16;
+    const int w_step0 = unit.kb * 4 * kStepBytes;
+    // direct-to-LDS activation loads: as in grouped_ffn.hip, lane l fills
+    // slot l % 8 of LDS row (group row + l / 8) with global chunk
+    // swz_chunk(row, l % 8)
+    const int grow = lane >> 3;
+    int a_src[kAL];
 #pragma unroll
-  for (int l = 0; l < kAL; ++l) {
-    const int lr = (l * NW + wave) * 8 + grow;
-    a_src[l] = (lr * Kdim + swz_chunk(lr, lane & 7) * 8) * (int)sizeof(bf16);
-  }
-  char* const lds_bytes = reinterpret_cast<char*>(lds);
-  const int lrow = lane & 31;
-  const int lhalf = lane >> 5;
-  // LDS byte offset of this lane's operand for step ks of 32-token operand
-  // 0 (operands start at multiples of 32 rows, which share a swizzle)
-  int abase[4];
-#pragma unroll
-  for (int ks = 0; ks < 4; ++ks) abase[ks] = swz(lrow, ks * 2 + lhalf) * (int)sizeof(bf16);
-  const int jlim = min(kTM, (rows + 31) / 32);  // operands holding at least one row
-
-  f32x16 acc[kTW][kTM];
-#pragma unroll
-  for (int i = 0; i < kTW; ++i)
-#pragma unroll
-    for (int j = 0; j < kTM; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-  bf16x8 wf[kRing][kTW];  // weight fragments, ring of steps
-  bf16x8 af[2][kTM];      // activation operands, double-buffered
-
-  // (offsets go through locals: an array element or a conditional
-  // expression as a buffer builtin's argument drops the kernel's host stub)
-  auto load_w = [&](int slot, int i, int q) __attribute__((always_inline)) {
-    const int voff = w_lane + i * kFragBytes;
-    const int soff = w_step0 + q * kStepBytes;
-    wf[slot][i] =
-        __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(wr, voff, soff, 0));
-  };
-  auto load_a = [&](int stage, int kt, int l) __attribute__((always_inline)) {
-    const int voff = a_src[l];
-    const int soff = (kofs + kt * kBK) * (int)sizeof(bf16);
-    lds_void_t* dst =
-        (lds_void_t*)(lds_bytes + stage * kAStage + (l * NW + wave) * 8 * kRowBytes);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(ar, dst, 16, voff, soff, 0, 0);
-  };
-  auto read_a = [&](int buf, int stage, int ks, int j) __attribute__((always_inline)) {
-    af[buf][j] = *reinterpret_cast<const bf16x8*>(lds_bytes + stage * kAStage + abase[ks] +
-                                                  j * 32 * kRowBytes);
-  };
-  auto fence_free_barrier = []() __attribute__((always_inline)) {
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-  };
-
-  // One 16-wide reduction step ks of reduction tile kt (weights in ring
-  // slot SL, activations on stage kt % 4), as kTW x kTM MFMA slots; a
-  // scheduling fence after every slot keeps the order below.
-  //   - the first slot of weight operand i loads fragment i of step
-  //     q + kDist into ring slot (SL + kDist) % 8;
-  //   - step 0 loads activation tile kt + 2 into stage (kt + 2) % 4 (last
-  //     read by tile kt - 2), load l in the middle slot of weight operand l;
-  //   - steps 0..2 read the next step's activation operands, one per 4
-  //     slots; step 3 waits halfway (see below), meets the other waves at
-  //     the barrier and then reads tile kt + 1's first operands.
-  // Halfway through step 3 the wave needs tile kt + 1's activations, loaded
-  // during step 0 of tile kt - 1.  Counting the loads issued after them
-  // (4 - kAL weight loads later in that step, 12 in its steps 1..3, 4 + kAL
-  // in step 0 of tile kt, 8 in its steps 1..2 and 2 before the wait) gives
-  // 30 in every tile; the prologue issues more (4 kDist weight loads after
-  // tile 1's activations), so vmcnt(30) is sufficient there too.  Weight
-  // operands need no explicit wait: the compiler waits for each register's
-  // own load.  Past the last tile the loads repeat the last step or tile
-  // into ring slots and stages nobody reads again, so the body has no
-  // branches.
-  auto step = [&](auto jn_c, auto sl_c, auto ks_c, int kt) __attribute__((always_inline)) {
-    constexpr int JN = decltype(jn_c)::value;
-    constexpr int SL = decltype(sl_c)::value;
-    constexpr int KS = decltype(ks_c)::value;
-    constexpr int n = kTW * kTM;                   // MFMA slots
-    constexpr int per_read = n / kTM;              // slots per operand read, steps 0..2
-    constexpr int half = n / 2;
-    constexpr int per_read3 = half / kTM > 0 ? half / kTM : 1;
-    const int q = kt * 4 + KS;
-    const int qw = min(q + kDist, nsteps - 1);
-    const int cur = (kt & (kStages - 1));
-    const int nxt = ((kt + 1) & (kStages - 1));
-    const int kt_a = min(kt + 2, nk - 1);
-#pragma unroll
-    for (int m = 0; m < n; ++m) {
-      const int i = m / kTM, j = m % kTM;
-      if (KS == 3 && m == half) {
-        wait_vmcnt<30>();
-        fence_free_barrier();
-      }
-      if (j == 0) load_w((SL + kDist) % kRing, i, qw);
-      if (KS == 0 && j == kTM / 2 && i < kAL) load_a((kt + 2) & (kStages - 1), kt_a, i);
-      if (KS < 3) {
-        if (m % per_read == 1 % per_read && m / per_read < JN)
-          read_a((KS + 1) & 1, cur, KS + 1, m / per_read);
-      } else if (m >= half) {
-        const int r = m - half;
-        if (r % per_read3 == (per_read3 > 1 ? 1 : 0) && r / per_read3 < JN)
-          read_a(0, nxt, 0, r / per_read3);
-      }
-      if (j < JN)  // 32-token operands past the tile's last row are skipped
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[SL][i], af[KS & 1][j],
-                                                            acc[i][j], 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
+    for (int l = 0; l < kAL; ++l) {
+      const int lr = (l * NW + wave) * 8 + grow;
+      a_src[l] = (lr * Kdim + swz_chunk(lr, lane & 7) * 8) * (int)sizeof(bf16);
     }
-  };
-  using C0 = std::integral_constant<int, 0>;
-  using C1 = std::integral_constant<int, 1>;
-  using C2 = std::integral_constant<int, 2>;
-  using C3 = std::integral_constant<int, 3>;
-  // tile kt uses ring slots (kt % 2) * 4 + ks
-  auto tile_fn = [&](auto jn_c, auto ph_c, int kt) __attribute__((always_inline)) {
-    constexpr int PH = decltype(ph_c)::value;
-    step(jn_c, std::integral_constant<int, PH + 0>{}, C0{}, kt);
-    step(jn_c, std::integral_constant<int, PH + 1>{}, C1{}, kt);
-    step(jn_c, std::integral_constant<int, PH + 2>{}, C2{}, kt);
-    step(jn_c, std::integral_constant<int, PH + 3>{}, C3{}, kt);
-  };
-  using P0 = std::integral_constant<int, 0>;
-  using P4 = std::integral_constant<int, 4>;
-  // JN: 32-token operands that hold rows (a ragged last tile of an expert
-  // multiplies fewer; a run-time test per MFMA would force the accumulators
-  // out of registers, so the loop comes in one variant per JN)
-  auto main_loop = [&](auto jn_c) __attribute__((always_inline)) {
-    constexpr int JN = decltype(jn_c)::value;
-    // prologue: activation tiles 0 and 1, weight steps 0 .. kDist - 1; wait
-    // for tile 0 (after it: kAL + 4 kDist loads)
+    char* const lds_bytes = reinterpret_cast<char*>(lds);
+    const int lrow = lane & 31;
+    const int lhalf = lane >> 5;
+    // LDS byte offset of this lane's operand for step ks of 32-token operand
+    // 0 (operands start at multiples of 32 rows, which share a swizzle)
+    int abase[4];
 #pragma unroll
-    for (int l = 0; l < kAL; ++l) load_a(0, 0, l);
-#pragma unroll
-    for (int l = 0; l < kAL; ++l) load_a(1, min(1, nk - 1), l);
-#pragma unroll
-    for (int s = 0; s < kDist; ++s)
-#pragma unroll
-      for (int i = 0; i < kTW; ++i) load_w(s, i, min(s, nsteps - 1));
-    wait_vmcnt<kAL + 4 * kDist>();
-    fence_free_barrier();
-#pragma unroll
-    for (int j = 0; j < kTM; ++j)
-      if (j < JN) read_a(0, 0, 0, j);
-    if (nk & 1) {
-      tile_fn(jn_c, P0{}, 0);
-      for (int kt = 1; kt < nk; kt += 2) {
-        tile_fn(jn_c, P4{}, kt);
-        tile_fn(jn_c, P0{}, kt + 1);
-      }
-    } else {
-      for (int kt = 0; kt < nk; kt += 2) {
-        tile_fn(jn_c, P0{}, kt);
-        tile_fn(jn_c, P4{}, kt + 1);
-      }
-    }
-    // the trailing repeat loads land before the block can end (and its LDS
-    // be handed to another block)
-    wait_vmcnt<0>();
-  };
-  if (jlim >= kTM)
-    main_loop(std::integral_constant<int, kTM>{});
-  else if (kTM > 2 && jlim == 3)
-    main_loop(std::integral_constant<int, (kTM > 2 ? 3 : kTM)>{});
-  else if (kTM > 1 && jlim == 2)
-    main_loop(std::integral_constant<int, (kTM > 1 ? 2 : kTM)>{});
-  else
-    main_loop(C1{});
+    for (int ks = 0; ks < 4; ++ks) abase[ks] = swz(lrow, ks * 2 + lhalf) * (int)sizeof(bf16);
+    const int jlim = min(kTM, (rows + 31) / 32);  // operands holding at least one row
 
-  // A piece of a split tile (map_unit): as in grouped_ffn.hip, its fp32
-  // accumulators go to its workspace slot in register order, the piece that
-  // arrives last adds the pieces in piece order, re-arms the counter and
-  // stores the tile.  The arrival flag sits past the activation stages.
-  if (unit.parts > 1) {
-    constexpr int kUnitFloats = NW * kTW * kTM * kWave * 16;
-    float* const base = partial + (size_t)unit.pslot0 * kUnitFloats +
-                        (size_t)wave * (kTW * kTM * kWave * 16) + lane * 16;
-    float* const mine = base + (size_t)unit.piece * kUnitFloats;
+    f32x16 acc[kTW][kTM];
 #pragma unroll
     for (int i = 0; i < kTW; ++i)
 #pragma unroll
       for (int j = 0; j < kTM; ++j)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          f32x4 v;
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+    bf16x8 wf[kRing][kTW];  // weight fragments, ring of steps
+    bf16x8 af[2][kTM];      // activation operands, double-buffered
+
+    // (offsets go through locals: an array element or a conditional
+    // expression as a buffer builtin's argument drops the kernel's host stub)
+    auto load_w = [&](int slot, int i, int q) __attribute__((always_inline)) {
+      const int voff = w_lane + i * kFragBytes;
+      const int soff = w_step0 + q * kStepBytes;
+      wf[slot][i] =
+          __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(wr, voff, soff, 0));
+    };
+    auto load_a = [&](int stage, int kt, int l) __attribute__((always_inline)) {
+      const int voff = a_src[l];
+      const int soff = (kofs + kt * kBK) * (int)sizeof(bf16);
+      lds_void_t* dst =
+          (lds_void_t*)(lds_bytes + stage * kAStage + (l * NW + wave) * 8 * kRowBytes);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ar, dst, 16, voff, soff, 0, 0);
+    };
+    auto read_a = [&](int buf, int stage, int ks, int j) __attribute__((always_inline)) {
+      af[buf][j] = *reinterpret_cast<const bf16x8*>(lds_bytes + stage * kAStage + abase[ks] +
+                                                    j * 32 * kRowBytes);
+    };
+    auto fence_free_barrier = []() __attribute__((always_inline)) {
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+    };
+
+    // One 16-wide reduction step ks of reduction tile kt (weights in ring
+    // slot SL, activations on stage kt % 4), as kTW x kTM MFMA slots; a
+    // scheduling fence after every slot keeps the order below.
+    //   - the first slot of weight operand i loads fragment i of step
+    //     q + kDist into ring slot (SL + kDist) % 8;
+    //   - step 0 loads activation tile kt + 2 into stage (kt + 2) % 4 (last
+    //     read by tile kt - 2), load l in the middle slot of weight operand l;
+    //   - steps 0..2 read the next step's activation operands, one per 4
+    //     slots; step 3 waits halfway (see below), meets the other waves at
+    //     the barrier and then reads tile kt + 1's first operands.
+    // Halfway through step 3 the wave needs tile kt + 1's activations, loaded
+    // during step 0 of tile kt - 1.  Counting the loads issued after them
+    // (4 - kAL weight loads later in that step, 12 in its steps 1..3, 4 + kAL
+    // in step 0 of tile kt, 8 in its steps 1..2 and 2 before the wait) gives
+    // 30 in every tile; the prologue issues more (4 kDist weight loads after
+    // tile 1's activations), so vmcnt(30) is sufficient there too.  Weight
+    // operands need no explicit wait: the compiler waits for each register's
+    // own load.  Past the last tile the loads repeat the last step or tile
+    // into ring slots and stages nobody reads again, so the body has no
+    // branches.
+    auto step = [&](auto jn_c, auto sl_c, auto ks_c, int kt) __attribute__((always_inline)) {
+      constexpr int JN = decltype(jn_c)::value;
+      constexpr int SL = decltype(sl_c)::value;
+      constexpr int KS = decltype(ks_c)::value;
+      constexpr int n = kTW * kTM;                   // MFMA slots
+      constexpr int per_read = n / kTM;              // slots per operand read, steps 0..2
+      constexpr int half = n / 2;
+      constexpr int per_read3 = half / kTM > 0 ? half / kTM : 1;
+      const int q = kt * 4 + KS;
+      const int qw = min(q + kDist, nsteps - 1);
+      const int cur = (kt & (kStages - 1));
+      const int nxt = ((kt + 1) & (kStages - 1));
+      const int kt_a = min(kt + 2, nk - 1);
 #pragma unroll
-          for (int c = 0; c < 4; ++c) v[c] = acc[i][j][q * 4 + c];
-          *reinterpret_cast<f32x4*>(mine + (i * kTM + j) * kWave * 16 + q * 4) = v;
+      for (int m = 0; m < n; ++m) {
+        const int i = m / kTM, j = m % kTM;
+        if (KS == 3 && m == half) {
+          wait_vmcnt<30>();
+          fence_free_barrier();
         }
-    __threadfence();
-    __syncthreads();
-    int* const flag = reinterpret_cast<int*>(lds_bytes + kStages * kAStage);
-    if (threadIdx.x == 0) *flag = atomicAdd(&split_cnt[unit.split], 1);
-    __syncthreads();
-    if (*flag != unit.parts - 1) return;
-    __threadfence();
+        if (j == 0) load_w((SL + kDist) % kRing, i, qw);
+        if (KS == 0 && j == kTM / 2 && i < kAL) load_a((kt + 2) & (kStages - 1), kt_a, i);
+        if (KS < 3) {
+          if (m % per_read == 1 % per_read && m / per_read < JN)
+            read_a((KS + 1) & 1, cur, KS + 1, m / per_read);
+        } else if (m >= half) {
+          const int r = m - half;
+          if (r % per_read3 == (per_read3 > 1 ? 1 : 0) && r / per_read3 < JN)
+            read_a(0, nxt, 0, r / per_read3);
+        }
+        if (j < JN)  // 32-token operands past the tile's last row are skipped
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[SL][i], af[KS & 1][j],
+                                                              acc[i][j], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    using C0 = std::integral_constant<int, 0>;
+    using C1 = std::integral_constant<int, 1>;
+    using C2 = std::integral_constant<int, 2>;
+    using C3 = std::integral_constant<int, 3>;
+    // tile kt uses ring slots (kt % 2) * 4 + ks
+    auto tile_fn = [&](auto jn_c, auto ph_c, int kt) __attribute__((always_inline)) {
+      constexpr int PH = decltype(ph_c)::value;
+      step(jn_c, std::integral_constant<int, PH + 0>{}, C0{}, kt);
+      step(jn_c, std::integral_constant<int, PH + 1>{}, C1{}, kt);
+      step(jn_c, std::integral_constant<int, PH + 2>{}, C2{}, kt);
+      step(jn_c, std::integral_constant<int, PH + 3>{}, C3{}, kt);
+    };
+    using P0 = std::integral_constant<int, 0>;
+    using P4 = std::integral_constant<int, 4>;
+    // JN: 32-token operands that hold rows (a ragged last tile of an expert
+    // multiplies fewer; a run-time test per MFMA would force the accumulators
+    // out of registers, so the loop comes in one variant per JN)
+    auto main_loop = [&](auto jn_c) __attribute__((always_inline)) {
+      constexpr int JN = decltype(jn_c)::value;
+      // prologue: activation tiles 0 and 1, weight steps 0 .. kDist - 1; wait
+      // for tile 0 (after it: kAL + 4 kDist loads)
 #pragma unroll
-    for (int i = 0; i < kTW; ++i)
+      for (int l = 0; l < kAL; ++l) load_a(0, 0, l);
 #pragma unroll
-      for (int j = 0; j < kTM; ++j) {
-        f32x16 sum;
+      for (int l = 0; l < kAL; ++l) load_a(1, min(1, nk - 1), l);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sum[r] = 0.0f;
-        for (int p = 0; p < unit.parts; ++p) {
-          const float* src = base + (size_t)p * kUnitFloats + (i * kTM + j) * kWave * 16;
+      for (int s = 0; s < kDist; ++s)
+#pragma unroll
+        for (int i = 0; i < kTW; ++i) load_w(s, i, min(s, nsteps - 1));
+      wait_vmcnt<kAL + 4 * kDist>();
+      fence_free_barrier();
+#pragma unroll
+      for (int j = 0; j < kTM; ++j)
+        if (j < JN) read_a(0, 0, 0, j);
+      if (nk & 1) {
+        tile_fn(jn_c, P0{}, 0);
+        for (int kt = 1; kt < nk; kt += 2) {
+          tile_fn(jn_c, P4{}, kt);
+          tile_fn(jn_c, P0{}, kt + 1);
+        }
+      } else {
+        for (int kt = 0; kt < nk; kt += 2) {
+          tile_fn(jn_c, P0{}, kt);
+          tile_fn(jn_c, P4{}, kt + 1);
+        }
+      }
+      // the trailing repeat loads land before the block can end (and its LDS
+      // be handed to another block)
+      wait_vmcnt<0>();
+    };
+    if (jlim >= kTM)
+      main_loop(std::integral_constant<int, kTM>{});
+    else if (kTM > 2 && jlim == 3)
+      main_loop(std::integral_constant<int, (kTM > 2 ? 3 : kTM)>{});
+    else if (kTM > 1 && jlim == 2)
+      main_loop(std::integral_constant<int, (kTM > 1 ? 2 : kTM)>{});
+    else
+      main_loop(C1{});
+
+    // A piece of a split tile (map_unit): its fp32 accumulators go to its
+    // workspace slot in register order (with the coherent policy of
+    // store_partial), and once they are in memory the piece counts itself in;
+    // the piece that arrives last adds the pieces in piece order, re-arms the
+    // counter and stores the tile.  The arrival flag sits past the activation
+    // stages.
+    if (unit.parts > 1) {
+      constexpr int kUnitFloats = NW * kTW * kTM * kWave * 16;
+      constexpr int kUnitBytes = kUnitFloats * (int)sizeof(float);
+      const __amdgpu_buffer_rsrc_t pr = __builtin_amdgcn_make_buffer_rsrc(
+          partial + (size_t)unit.pslot0 * kUnitFloats, 0, (uint32_t)(unit.parts * kUnitBytes),
+          kBufferFlags);
+      const int lane_off = (wave * (kTW * kTM * kWave * 16) + lane * 16) * (int)sizeof(float);
+      const int mine = unit.piece * kUnitBytes;
+#pragma unroll
+      for (int i = 0; i < kTW; ++i)
+#pragma unroll
+        for (int j = 0; j < kTM; ++j)
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            const f32x4 v = *reinterpret_cast<const f32x4*>(src + q * 4);
+            f32x4 v;
 #pragma unroll
-            for (int c = 0; c < 4; ++c) sum[q * 4 + c] += v[c];
+            for (int c = 0; c < 4; ++c) v[c] = acc[i][j][q * 4 + c];
+            const int voff = lane_off + ((i * kTM + j) * kWave * 16 + q * 4) * (int)sizeof(float);
+            store_partial(pr, voff, mine, v);
           }
+      wait_vmcnt<0>();
+      __syncthreads();
+      int* const flag = reinterpret_cast<int*>(lds_bytes + kStages * kAStage);
+      if (threadIdx.x == 0) *flag = atomicAdd(&split_cnt[unit.split], 1);
+      __syncthreads();
+      if (*flag != unit.parts - 1) continue;
+#pragma unroll
+      for (int i = 0; i < kTW; ++i)
+#pragma unroll
+        for (int j = 0; j < kTM; ++j) {
+          f32x16 sum;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) sum[r] = 0.0f;
+          for (int p = 0; p < unit.parts; ++p) {
+            const int soff = p * kUnitBytes;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const int voff =
+                  lane_off + ((i * kTM + j) * kWave * 16 + q * 4) * (int)sizeof(float);
+              const f32x4 v = load_partial(pr, voff, soff);
+#pragma unroll
+              for (int c = 0; c < 4; ++c) sum[q * 4 + c] += v[c];
+            }
+          }
+          acc[i][j] = sum;
         }
-        acc[i][j] = sum;
-      }
-    if (threadIdx.x == 0) split_cnt[unit.split] = 0;
-  }
+      if (threadIdx.x == 0) split_cnt[unit.split] = 0;
+    }
 
-  // Epilogue.  Accumulator register r of lane l holds weight row
-  // (r / 4) * 8 + (l / 32) * 4 + r % 4 of its 32-row fragment and token
-  // l % 32 of its 32-token operand: runs of 4 consecutive output features.
+    // Epilogue.  Accumulator register r of lane l holds weight row
+    // (r / 4) * 8 + (l / 32) * 4 + r % 4 of its 32-row fragment and token
+    // l % 32 of its 32-token operand: runs of 4 consecutive output features.
 #pragma unroll
-  for (int j = 0; j < kTM; ++j) {
-    const int m_local = j * 32 + lrow;
-    if (m_local >= rows) continue;
-    bf16* orow = out + (size_t)(row0 + m_local) * Nout;
-    if (kDual) {
+    for (int j = 0; j < kTM; ++j) {
+      const int m_local = j * 32 + lrow;
+      if (m_local >= rows) continue;
+      bf16* orow = out + (size_t)(row0 + m_local) * Nout;
+      if (kDual) {
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
+        for (int i = 0; i < 2; ++i) {
 #pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          const int f = pn * 64 + i * 32 + r4 * 8 + lhalf * 4;
-          if (f >= Nout) continue;
-          bf16x4 o;
+          for (int r4 = 0; r4 < 4; ++r4) {
+            const int f = pn * 64 + i * 32 + r4 * 8 + lhalf * 4;
+            if (f >= Nout) continue;
+            bf16x4 o;
 #pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            const float g = acc[i][j][r4 * 4 + c];
-            const float u = acc[i + 2][j][r4 * 4 + c];
-            o[c] = (bf16)(g / (1.0f + __expf(-g)) * u);
+            for (int c = 0; c < 4; ++c) {
+              const float g = acc[i][j][r4 * 4 + c];
+              const float u = acc[i + 2][j][r4 * 4 + c];
+              o[c] = (bf16)(g / (1.0f + __expf(-g)) * u);
+            }
+            *reinterpret_cast<bf16x4*>(orow + f) = o;
           }
-          *reinterpret_cast<bf16x4*>(orow + f) = o;
         }
-      }
-    } else {
+      } else {
 #pragma unroll
-      for (int i = 0; i < kTW; ++i) {
+        for (int i = 0; i < kTW; ++i) {
 #pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          const int f = pn * kPanelRows + i * 32 + r4 * 8 + lhalf * 4;
-          if (f >= Nout) continue;
-          bf16x4 o;
+          for (int r4 = 0; r4 < 4; ++r4) {
+            const int f = pn * kPanelRows + i * 32 + r4 * 8 + lhalf * 4;
+            if (f >= Nout) continue;
+            bf16x4 o;
 #pragma unroll
-          for (int c = 0; c < 4; ++c) o[c] = (bf16)acc[i][j][r4 * 4 + c];
-          *reinterpret_cast<bf16x4*>(orow + f) = o;
+            for (int c = 0; c < 4; ++c) o[c] = (bf16)acc[i][j][r4 * 4 + c];
+            *reinterpret_cast<bf16x4*>(orow + f) = o;
+          }
         }
       }
     }
@@ -414,13 +429,13 @@ hipError_t launch_packed_gemm(const bf16* act, int Kdim, const bf16* wpk, int No
   });
   if (attr != hipSuccess) return attr;
   const int n_tiles = (P + kPkWaves - 1) / kPkWaves;
+  // one block per CU (the kernel takes a CU's registers), 8 per XCD row
   const int cps = ffn_resident_blocks() / kXcds > 0 ? ffn_resident_blocks() / kXcds : 1;
-  const long long per_xcd = (long long)max_tiles * ((n_tiles + kXcds - 1) / kXcds) + cps;
-  const int grid = (int)(per_xcd * kXcds);
-  const int* xcd_start = ws.xcd_start + (kDual ? 0 : kXcds * (E + 1));
+  const int grid = cps * kXcds;
+  (void)max_tiles;
   ffn_gemm_packed_kernel<BM, kDual><<<grid, kPkWaves * kWave, packed_lds_bytes<BM>(), stream>>>(
-      act, Kdim, wpk, Nout, P, out, ws.tiles, ws.tile_start, xcd_start, E, n_tiles, cps,
-      ws.partial, ws.split_cnt + (kDual ? 0 : kMaxSplitUnits));
+      act, Kdim, wpk, Nout, P, out, ws.tiles, ws.tile_start, E,
+      n_tiles, cps, ws.partial, ws.split_cnt + (kDual ? 0 : kMaxSplitUnits));
   return hipGetLastError();
 }
 
@@ -484,11 +499,9 @@ hipError_t launch_grouped_ffn_packed(const void* x_perm, int d, int ffn, int E,
   const int tr = packed_ffn_tile_rows(max_rows, E);
   const int max_tiles = max_tiles_for(max_rows, E, tr);
   const FfnWorkspace ws = ffn_workspace(workspace, E, max_tiles);
-  const int n_up = (packed_panels(d, ffn, true) + kPkWaves - 1) / kPkWaves;
-  const int n_dn = (packed_panels(d, ffn, false) + kPkWaves - 1) / kPkWaves;
-  ffn_schedule_kernel<<<1, 1024, 0, stream>>>(offsets, E, tr, (int)max_rows, max_tiles, n_up,
-                                              n_dn, ws.tiles, ws.tile_start, ws.num_tiles,
-                                              ws.split_cnt, ws.xcd_start);
+  ffn_schedule_kernel<<<1, 1024, 0, stream>>>(offsets, E, tr, (int)max_rows, max_tiles,
+                                              ws.tiles, ws.tile_start, ws.num_tiles,
+                                              ws.split_cnt);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   if (tr == 128)
