@@ -5,17 +5,23 @@
 // A one-block kernel turns offsets[] (which stays on the device) into row
 // tiles (expert, first row, end row) of at most tile_rows rows of one
 // expert.  The blocks of a GEMM pass are (row tile, output-column tile)
-// pairs in one global order: expert by expert, column tile by column tile,
-// and for each column tile all of the expert's row tiles, so consecutive
-// blocks share one weight tile and a few activation tiles.  Block b runs
-// on XCD b % 8, and each XCD takes one contiguous eighth of that order
-// (cut at column-tile boundaries, see xcd_range), so the blocks resident on
-// an XCD share weight and activation tiles through its L2 and every XCD gets
-// the same number of blocks.  The tiles of an XCD's partial last round are
-// split along the reduction when that shortens the round enough (see
-// map_unit).  A GEMM either sizes its grid on the host from the upper bound
-// max_rows (blocks beyond the real work exit at once) or launches one block
-// per CU that walks its XCD's range (grouped_ffn_packed.hip).
+// pairs; block b runs on XCD b % 8, and every XCD works through a list in
+// which each column tile comes with all of its expert's row tiles, so the
+// blocks resident on an XCD share one weight tile and a few activation
+// tiles through its L2.  How the column tiles are dealt to the XCDs depends
+// on how many a pass has (see map_unit):
+//   - 8 or more: each expert's column tiles are dealt round-robin over the
+//     XCDs, so all XCDs work on an expert at once, walk its row tiles in the
+//     same order and share its activation tiles through the MALL (experts of
+//     hundreds of row tiles, whose activations do not fit in one XCD's
+//     caches, need this), and every XCD gets the same share of every expert;
+//   - fewer: an expert's column tiles would land on a few XCDs only, which
+//     with skewed routing leaves others idle, so each XCD instead takes one
+//     contiguous eighth of the global order (expert by expert, column tile
+//     by column tile) and gets the same number of blocks.
+// The tiles of an XCD's partial last round are split along the reduction
+// when that shortens the round enough.  Both GEMMs launch one block per CU
+// that walks its XCD's list.
 #pragma once
 
 #include "moe_internal.h"
@@ -46,11 +52,15 @@ constexpr int kMinSplitTiles = 8;    // reduction tiles per piece, at least
 constexpr int kSplitMinSaved = 48;
 
 // Workspace layout: [num_tiles | pad to 256 B][split counters: 2 x
-// kMaxSplitUnits ints][tile_start[E+1] | pad][tiles | pad][split partials].
+// kMaxSplitUnits ints][XCD block tables: 2 passes x 8 XCDs x (E+1) ints |
+// pad][tile_start[E+1] | pad][deal_rank[E+1] | pad][tiles | pad][split
+// partials].
 struct FfnWorkspace {
   int* num_tiles;
   int* split_cnt;   // arrival counters of split tiles: gate/up pass, then down
+  int* xcd_start;   // [pass][xcd][E+1]: round-robin lists, the XCD's blocks for experts < e
   int* tile_start;  // tiles of expert e are slots [tile_start[e], tile_start[e+1])
+  int* deal_rank;   // experts with tiles before expert e
   int4* tiles;      // (expert, first row, end row, 0)
   float* partial;   // kMaxSplitUnits fp32 accumulator tiles (one per block slot)
 };
@@ -58,8 +68,13 @@ struct FfnWorkspace {
 constexpr int kXcds = 8;  // block b runs on XCD b % 8
 constexpr size_t kSplitCntBytes = 2 * kMaxSplitUnits * sizeof(int);
 
+inline size_t ffn_xcd_table_bytes(int E) {
+  return align_up((size_t)2 * kXcds * (E + 1) * sizeof(int), 256);
+}
+
 inline size_t ffn_tiles_offset(int E) {
-  return 256 + kSplitCntBytes + align_up((size_t)(E + 1) * sizeof(int), 256);
+  return 256 + kSplitCntBytes + ffn_xcd_table_bytes(E) +
+         2 * align_up((size_t)(E + 1) * sizeof(int), 256);
 }
 
 inline FfnWorkspace ffn_workspace(void* base, int E, int max_tiles) {
@@ -67,18 +82,39 @@ inline FfnWorkspace ffn_workspace(void* base, int E, int max_tiles) {
   FfnWorkspace ws;
   ws.num_tiles = reinterpret_cast<int*>(p);
   ws.split_cnt = reinterpret_cast<int*>(p + 256);
-  ws.tile_start = reinterpret_cast<int*>(p + 256 + kSplitCntBytes);
+  ws.xcd_start = reinterpret_cast<int*>(p + 256 + kSplitCntBytes);
+  ws.tile_start = reinterpret_cast<int*>(p + 256 + kSplitCntBytes + ffn_xcd_table_bytes(E));
+  ws.deal_rank = ws.tile_start + align_up((size_t)(E + 1) * sizeof(int), 256) / sizeof(int);
   ws.tiles = reinterpret_cast<int4*>(p + ffn_tiles_offset(E));
   ws.partial = reinterpret_cast<float*>(
       p + ffn_tiles_offset(E) + align_up((size_t)max_tiles * sizeof(int4), 256));
   return ws;
 }
 
+// Round-robin dealing: column tiles n of an expert that XCD x runs are
+// n = xcd_first_n(rank, x, n_tiles) + 8 k, rank = the expert's deal_rank
+// (experts with tiles before it).  The column tiles of the experts that
+// have rows are dealt round-robin over the XCDs, each expert continuing
+// where the previous one with rows stopped (counting empty experts too
+// would tie an expert's XCDs to its id).
+__device__ __forceinline__ int xcd_first_n(int rank, int x, int n_tiles) {
+  const int start = ((rank % kXcds) * (n_tiles % kXcds)) % kXcds;  // (rank * n_tiles) % 8
+  return (x - start + kXcds) % kXcds;
+}
+__device__ __forceinline__ int xcd_groups(int rank, int x, int n_tiles) {
+  const int f = xcd_first_n(rank, x, n_tiles);
+  return f < n_tiles ? (n_tiles - f + kXcds - 1) / kXcds : 0;
+}
+
+// n_up, n_dn: column tiles of the two passes (a pass with at least 8 gets
+// round-robin tables).
 __global__ __launch_bounds__(1024) void ffn_schedule_kernel(
     const int32_t* __restrict__ offsets, int E, int tile_rows, int max_rows,
-    int max_tiles, int4* __restrict__ tiles, int* __restrict__ tile_start,
-    int* __restrict__ num_tiles, int* __restrict__ split_cnt) {
+    int max_tiles, int n_up, int n_dn, int4* __restrict__ tiles,
+    int* __restrict__ tile_start, int* __restrict__ num_tiles,
+    int* __restrict__ split_cnt, int* __restrict__ xcd_start, int* __restrict__ deal_rank) {
   __shared__ int wave_sums[1024 / kWave];
+  __shared__ int wave_sums2[1024 / kWave];
   const int e = threadIdx.x;
   if (e < 2 * kMaxSplitUnits) split_cnt[e] = 0;
   int a = 0, b = 0, nt = 0;
@@ -99,6 +135,38 @@ __global__ __launch_bounds__(1024) void ffn_schedule_kernel(
     }
   }
   if (e == 0) *num_tiles = min(total, max_tiles);
+  // Per round-robin pass and XCD, the exclusive scan over experts of the
+  // XCD's blocks: wave w < 16 scans the table of pass w / 8 and XCD w % 8,
+  // 64 experts at a time.
+  __shared__ int cnt_s[1024];
+  __shared__ int rank_s[1024];
+  const int cnt = e < E ? min(base + nt, max_tiles) - min(base, max_tiles) : 0;
+  cnt_s[e] = cnt;
+  int with_rows = 0;
+  rank_s[e] = block_exclusive_scan(cnt > 0 ? 1 : 0, wave_sums2, &with_rows);
+  if (e < E) deal_rank[e] = rank_s[e];
+  if (e == 0) deal_rank[E] = with_rows;
+  __syncthreads();
+  const int wave = e / kWave, lane = e % kWave;
+  const int n_tiles = wave < kXcds ? n_up : n_dn;
+  if (wave < 2 * kXcds && n_tiles >= kXcds) {
+    const int x = wave % kXcds;
+    int* P = xcd_start + wave * (E + 1);
+    int run = 0;
+    for (int c = 0; c < E; c += kWave) {
+      const int ee = c + lane;
+      const int v = ee < E ? xcd_groups(rank_s[ee], x, n_tiles) * cnt_s[ee] : 0;
+      int incl = v;
+#pragma unroll
+      for (int off = 1; off < kWave; off <<= 1) {
+        const int o = __shfl_up(incl, off);
+        if (lane >= off) incl += o;
+      }
+      if (ee < E) P[ee] = run + incl - v;
+      run += __shfl(incl, kWave - 1);
+    }
+    if (lane == 0) P[E] = run;
+  }
 }
 
 inline int max_tiles_for(int64_t max_rows, int E, int tile_rows) {
@@ -156,41 +224,40 @@ __device__ __forceinline__ int expert_at(const int* __restrict__ tile_start, int
   return lo;
 }
 
-// First global block position of XCD x's range: the first column-tile
-// boundary at or after x T / 8 (T = all blocks of the pass); x = 8 gives T.
-// Cutting at column-tile boundaries keeps a weight tile's blocks on one XCD.
+// First global block position of XCD x's range: x T / 8 (T = all blocks of
+// the pass); x = 8 gives T.  The XCDs' block counts differ by at most one;
+// a column tile whose row tiles straddle a cut is shared by two XCDs.
 __device__ __forceinline__ int xcd_range(const int* __restrict__ tile_start, int E,
                                          int n_tiles, int x) {
   const int T = n_tiles * tile_start[E];
-  if (x >= kXcds) return T;
-  const int t = (int)((long long)x * T / kXcds);
-  if (t >= T) return T;
-  const int e = expert_at(tile_start, E, n_tiles, t);
-  const int g0 = n_tiles * tile_start[e];
-  const int cnt = tile_start[e + 1] - tile_start[e];
-  const int n = (t - g0 + cnt - 1) / cnt;  // column tiles of e that start before t
-  return g0 + n * cnt;
+  return (int)((long long)x * T / kXcds);
 }
 
 // Block slot b -> work unit.  Block slot b runs on XCD x = b % 8 as that
-// XCD's block i = b / 8 (b is the block index, or for a block that walks
-// its XCD's range, blockIdx.x + k gridDim.x with gridDim.x a multiple of 8);
-// i indexes the XCD's range [xcd_range(x), xcd_range(x + 1)) of the global
-// order.
+// XCD's block i = b / 8 (b = blockIdx.x + k gridDim.x, gridDim.x a multiple
+// of 8).  With n_tiles >= 8, XCD x's list is, expert by expert, its
+// round-robin share of the expert's column tiles (xcd_first_n), each with
+// all of the expert's row tiles, and P (the XCD's row of xcd_start) gives
+// the list position of each expert's first block; with fewer, its list is
+// the range [xcd_range(x), xcd_range(x + 1)) of the global order.
 //
-// With cps blocks resident per XCD, the first B - R entries of a range of
-// B (R = B mod cps, the XCD's partial last round) are whole tiles; each of
-// the last R tiles becomes s = min(cps / R, kMaxSplit, nk / kMinSplitTiles)
+// With cps blocks resident per XCD, the first B - R entries of a list of B
+// (R = B mod cps, the XCD's partial last round) are whole tiles; each of the
+// last R tiles becomes s = min(cps / R, kMaxSplit, nk / kMinSplitTiles)
 // pieces of consecutive reduction tiles, which take the XCD's block numbers
 // after the whole tiles and so fill its last round, if that saves at least
 // kSplitMinSaved reduction tiles of the round (nk - nk / s); otherwise
 // every tile stays whole.
-__device__ __forceinline__ bool map_unit(int b, const int* __restrict__ tile_start, int E,
+__device__ __forceinline__ bool map_unit(int b, const int* __restrict__ tile_start,
+                                         const int* __restrict__ deal_rank,
+                                         const int* __restrict__ xcd_start, int E,
                                          int n_tiles, int nk, int cps, Unit* w) {
   const int x = b % kXcds;
   const int i = b / kXcds;
-  const int S0 = xcd_range(tile_start, E, n_tiles, x);
-  const int B = xcd_range(tile_start, E, n_tiles, x + 1) - S0;
+  const bool rr = n_tiles >= kXcds;
+  const int* __restrict__ P = xcd_start + x * (E + 1);
+  const int S0 = rr ? 0 : xcd_range(tile_start, E, n_tiles, x);
+  const int B = rr ? P[E] : xcd_range(tile_start, E, n_tiles, x + 1) - S0;
   const int R = B % cps;
   int s = R > 0 ? min(min(cps / R, kMaxSplit), nk / kMinSplitTiles) : 1;
   if (s < 2 || nk - nk / s < kSplitMinSaved) s = 1;
@@ -203,13 +270,26 @@ __device__ __forceinline__ bool map_unit(int b, const int* __restrict__ tile_sta
   const int t = is_piece ? p / s : 0;
   const int piece = is_piece ? p % s : 0;
   const int parts = is_piece ? s : 1;
-  const int L = S0 + (is_piece ? whole + t : i);
-  const int e = expert_at(tile_start, E, n_tiles, L);
+  const int entry = is_piece ? whole + t : i;
+  int e = 0, r = 0;
+  if (rr) {
+    int lo = 0, hi = E;  // P[lo] <= entry < P[hi]: expert lo has blocks here
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (P[mid] <= entry) lo = mid; else hi = mid;
+    }
+    e = lo;
+    r = entry - P[lo];
+  } else {
+    const int L = S0 + entry;
+    e = expert_at(tile_start, E, n_tiles, L);
+    r = L - n_tiles * tile_start[e];
+  }
   const int first = tile_start[e];
   const int cnt = tile_start[e + 1] - first;
-  const int r = L - n_tiles * first;
+  const int n_tile = rr ? xcd_first_n(deal_rank[e], x, n_tiles) + kXcds * (r / cnt) : r / cnt;
   *w = Unit{first + r % cnt,
-            r / cnt,
+            n_tile,
             piece * nk / parts,
             (piece + 1) * nk / parts,
             is_piece ? x * cps + t : -1,

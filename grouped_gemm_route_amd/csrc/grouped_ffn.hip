@@ -87,7 +87,7 @@ __global__ __launch_bounds__(NW * kWave, 1) void ffn_gemm_bf16_kernel(
     const bf16* __restrict__ act, int Kdim, const bf16* __restrict__ w0,
     const bf16* __restrict__ w1, int Nout, bf16* __restrict__ out,
     const int4* __restrict__ tiles, const int* __restrict__ tile_start,
-    int E, int n_tiles,
+    const int* __restrict__ deal_rank, const int* __restrict__ xcd_start, int E, int n_tiles,
     int cps, float* __restrict__ partial, int* __restrict__ split_cnt) {
   using G = TileGeo<BM, WM, NW>;
   extern __shared__ __attribute__((aligned(16))) bf16 lds[];
@@ -95,7 +95,8 @@ __global__ __launch_bounds__(NW * kWave, 1) void ffn_gemm_bf16_kernel(
   // gridDim.x (gridDim.x is 8 x the blocks resident per XCD).
   for (int vb = blockIdx.x;; vb += gridDim.x) {
     Unit unit;
-    if (!map_unit(vb, tile_start, E, n_tiles, Kdim / kBK, cps, &unit)) break;
+    if (!map_unit(vb, tile_start, deal_rank, xcd_start, E, n_tiles, Kdim / kBK, cps, &unit))
+      break;
     // the previous unit's waves are done with LDS
     __syncthreads();
     const int slot = unit.slot;
@@ -647,8 +648,9 @@ hipError_t launch_bf16_gemm(const bf16* act, int Kdim, const bf16* w0,
   const int cps = ffn_resident_blocks() / kXcds > 0 ? ffn_resident_blocks() / kXcds : 1;
   const int grid = cps * kXcds;
   (void)max_tiles;
+  const int* xcd_start = ws.xcd_start + (kDual ? 0 : kXcds * (E + 1));
   ffn_gemm_bf16_kernel<BM, WM, NW, kDual><<<grid, NW * kWave, G::kLds, stream>>>(
-      act, Kdim, w0, w1, Nout, out, ws.tiles, ws.tile_start, E,
+      act, Kdim, w0, w1, Nout, out, ws.tiles, ws.tile_start, ws.deal_rank, xcd_start, E,
       n_tiles, cps, ws.partial, ws.split_cnt + (kDual ? 0 : kMaxSplitUnits));
   return hipGetLastError();
 }
@@ -721,9 +723,13 @@ hipError_t launch_grouped_ffn(const void* x_perm, bool bf16_data, int d,
   const int tr = bf16_data ? bf16_tile_rows(max_rows, E) : kF32TileRows;
   const int max_tiles = max_tiles_for(max_rows, E, tr);
   const FfnWorkspace ws = ffn_workspace(workspace, E, max_tiles);
+  // column tiles of the bf16 passes (the round-robin tables serve only those)
+  const int n_up = (ffn + kBW / 2 - 1) / (kBW / 2);
+  const int n_dn = (d + kBW - 1) / kBW;
   ffn_schedule_kernel<<<1, 1024, 0, stream>>>(offsets, E, tr, (int)max_rows, max_tiles,
-                                              ws.tiles, ws.tile_start, ws.num_tiles,
-                                              ws.split_cnt);
+                                              n_up, n_dn, ws.tiles, ws.tile_start,
+                                              ws.num_tiles, ws.split_cnt, ws.xcd_start,
+                                              ws.deal_rank);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
 

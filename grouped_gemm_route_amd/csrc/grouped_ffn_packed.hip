@@ -97,7 +97,7 @@ template <int BM, bool kDual>
 __global__ __launch_bounds__(kPkWaves * kWave, 1) void ffn_gemm_packed_kernel(
     const bf16* __restrict__ act, int Kdim, const bf16* __restrict__ wpk, int Nout, int P,
     bf16* __restrict__ out, const int4* __restrict__ tiles, const int* __restrict__ tile_start,
-    int E, int n_tiles,
+    const int* __restrict__ deal_rank, const int* __restrict__ xcd_start, int E, int n_tiles,
     int cps, float* __restrict__ partial, int* __restrict__ split_cnt) {
   constexpr int NW = kPkWaves;
   constexpr int kTM = BM / 32;             // 32-token operands per wave (all BM rows)
@@ -115,7 +115,7 @@ __global__ __launch_bounds__(kPkWaves * kWave, 1) void ffn_gemm_packed_kernel(
   // launched only to find no work.
   for (int vb = blockIdx.x;; vb += gridDim.x) {
     Unit unit;
-    if (!map_unit(vb, tile_start, E, n_tiles, Kdim / kBK, cps, &unit))
+    if (!map_unit(vb, tile_start, deal_rank, xcd_start, E, n_tiles, Kdim / kBK, cps, &unit))
       break;
     // the previous unit's waves are done with the LDS stages
     __syncthreads();
@@ -433,8 +433,9 @@ hipError_t launch_packed_gemm(const bf16* act, int Kdim, const bf16* wpk, int No
   const int cps = ffn_resident_blocks() / kXcds > 0 ? ffn_resident_blocks() / kXcds : 1;
   const int grid = cps * kXcds;
   (void)max_tiles;
+  const int* xcd_start = ws.xcd_start + (kDual ? 0 : kXcds * (E + 1));
   ffn_gemm_packed_kernel<BM, kDual><<<grid, kPkWaves * kWave, packed_lds_bytes<BM>(), stream>>>(
-      act, Kdim, wpk, Nout, P, out, ws.tiles, ws.tile_start, E,
+      act, Kdim, wpk, Nout, P, out, ws.tiles, ws.tile_start, ws.deal_rank, xcd_start, E,
       n_tiles, cps, ws.partial, ws.split_cnt + (kDual ? 0 : kMaxSplitUnits));
   return hipGetLastError();
 }
@@ -499,9 +500,11 @@ hipError_t launch_grouped_ffn_packed(const void* x_perm, int d, int ffn, int E,
   const int tr = packed_ffn_tile_rows(max_rows, E);
   const int max_tiles = max_tiles_for(max_rows, E, tr);
   const FfnWorkspace ws = ffn_workspace(workspace, E, max_tiles);
-  ffn_schedule_kernel<<<1, 1024, 0, stream>>>(offsets, E, tr, (int)max_rows, max_tiles,
-                                              ws.tiles, ws.tile_start, ws.num_tiles,
-                                              ws.split_cnt);
+  const int n_up = (packed_panels(d, ffn, true) + kPkWaves - 1) / kPkWaves;
+  const int n_dn = (packed_panels(d, ffn, false) + kPkWaves - 1) / kPkWaves;
+  ffn_schedule_kernel<<<1, 1024, 0, stream>>>(offsets, E, tr, (int)max_rows, max_tiles, n_up,
+                                              n_dn, ws.tiles, ws.tile_start, ws.num_tiles,
+                                              ws.split_cnt, ws.xcd_start, ws.deal_rank);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   if (tr == 128)
