@@ -107,8 +107,9 @@ def _close(name, got, ref):
 
 
 @pytest.mark.parametrize("case", [
-    # a grid below one round of resident blocks: tiles split along the reduction
-    dict(N=96, d=1024, ffn=1536, E=4, K=2),
+    # grids below one round of resident blocks with long reductions: tiles
+    # split along the reduction (both passes here, the gate/up pass next)
+    dict(N=48, d=4096, ffn=4096, E=2, K=2),
     dict(N=29, d=4096, ffn=512, E=2, K=1),
     # 64-row tiles (mean 48 rows per expert) and 32-row tiles (decode-sized)
     dict(N=384, d=256, ffn=320, E=16, K=2),

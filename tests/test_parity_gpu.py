@@ -125,10 +125,12 @@ SMALL = {
                                  act="bf16", C=None, renormalize=True),
     "many_blocks_e8": synth.config("many_blocks_e8", N=1500, d=64, ffn=128, E=8, K=2, W=8,
                                    act="bf16", C=1.1),
-    # grids smaller than one round of resident blocks: the grouped GEMM splits
-    # tiles along the reduction (2 pieces in the gate/up pass and 3 in the
-    # down pass here; 8 in the gate/up pass of split8_bf16)
-    "split_reduce_bf16": synth.config("split_reduce_bf16", N=96, d=1024, ffn=1536, E=4, K=2,
+    # grids smaller than one round of resident blocks, with reductions long
+    # enough to be worth splitting: the grouped GEMMs split tiles along the
+    # reduction (here both passes of both kernels: 8 pieces per tile in the
+    # packed-weight kernel, 4 and 8 in the row-major one; split8_bf16: 8 in
+    # the gate/up pass)
+    "split_reduce_bf16": synth.config("split_reduce_bf16", N=48, d=4096, ffn=4096, E=2, K=2,
                                       W=2, act="bf16", C=None),
     "split8_bf16": synth.config("split8_bf16", N=29, d=4096, ffn=512, E=2, K=1, W=2,
                                 act="bf16", C=None),
@@ -210,14 +212,15 @@ def test_runs_are_bitwise_deterministic():
     assert torch.equal(a.disp["x_perm"][:M], b.disp["x_perm"][:M])
 
 
-def test_split_reduction_is_bitwise_deterministic():
+@pytest.mark.parametrize("packed", [False, True])
+def test_split_reduction_is_bitwise_deterministic(packed):
     # split tiles are summed in piece order whichever piece finishes last
     cfg = SMALL["split_reduce_bf16"]
     inp = _small_inputs(cfg)
-    a = _run_gpu(cfg, inp, _cap(cfg))
+    a = _run_gpu(cfg, inp, _cap(cfg), packed)
     M = int(a.disp["offsets"][-1])
     for _ in range(3):
-        b = _run_gpu(cfg, inp, _cap(cfg))
+        b = _run_gpu(cfg, inp, _cap(cfg), packed)
         assert torch.equal(a.h[:M], b.h[:M])
         assert torch.equal(a.y_perm[:M], b.y_perm[:M])
         assert torch.equal(a.out, b.out)
