@@ -449,8 +449,10 @@ __global__ __launch_bounds__(NW * kWave, 1) void ffn_gemm_bf16_kernel(
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
     // A piece of a split tile.  Its accumulators go to its workspace slot in
-    // register order (lane-contiguous 64-byte runs, with the coherent policy of
-    // store_partial); once they are in memory the block counts itself in, so
+    // register order (each store instruction writes one contiguous 1 KB run,
+    // lanes side by side, so only whole cache lines travel), with the
+    // coherent policy of store_partial; once they are in memory the block
+    // counts itself in, so
     // the piece that arrives last sees every piece, adds them in piece order
     // into its accumulators, re-arms the counter for the next launch and goes
     // on to the ordinary epilogue.  No block waits on another.
@@ -461,7 +463,7 @@ __global__ __launch_bounds__(NW * kWave, 1) void ffn_gemm_bf16_kernel(
           partial + (size_t)unit.pslot0 * kUnitFloats, 0, (uint32_t)(unit.parts * kUnitBytes),
           kBufferFlags);
       const int lane_off =
-          (wave * (G::kTW * G::kTM * kWave * 16) + lane * 16) * (int)sizeof(float);
+          (wave * (G::kTW * G::kTM * kWave * 16) + lane * 4) * (int)sizeof(float);
       const int mine = unit.piece * kUnitBytes;
 #pragma unroll
       for (int i = 0; i < G::kTW; ++i)
@@ -473,7 +475,7 @@ __global__ __launch_bounds__(NW * kWave, 1) void ffn_gemm_bf16_kernel(
 #pragma unroll
             for (int c = 0; c < 4; ++c) v[c] = acc[i][j][q * 4 + c];
             const int voff =
-                lane_off + ((i * G::kTM + j) * kWave * 16 + q * 4) * (int)sizeof(float);
+                lane_off + ((i * G::kTM + j) * 4 + q) * kWave * 4 * (int)sizeof(float);
             store_partial(pr, voff, mine, v);
           }
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -494,7 +496,7 @@ __global__ __launch_bounds__(NW * kWave, 1) void ffn_gemm_bf16_kernel(
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
               const int voff =
-                  lane_off + ((i * G::kTM + j) * kWave * 16 + q * 4) * (int)sizeof(float);
+                  lane_off + ((i * G::kTM + j) * 4 + q) * kWave * 4 * (int)sizeof(float);
               const f32x4 v = load_partial(pr, voff, soff);
 #pragma unroll
               for (int c = 0; c < 4; ++c) sum[q * 4 + c] += v[c];

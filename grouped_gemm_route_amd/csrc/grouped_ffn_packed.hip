@@ -314,7 +314,9 @@ __global__ __launch_bounds__(kPkWaves * kWave, 1) void ffn_gemm_packed_kernel(
       main_loop(C1{});
 
     // A piece of a split tile (map_unit): its fp32 accumulators go to its
-    // workspace slot in register order (with the coherent policy of
+    // workspace slot in register order (each store instruction writes one
+    // contiguous 1 KB run, lanes side by side, so only whole cache lines
+    // travel; with the coherent policy of
     // store_partial), and once they are in memory the piece counts itself in;
     // the piece that arrives last adds the pieces in piece order, re-arms the
     // counter and stores the tile.  The arrival flag sits past the activation
@@ -325,7 +327,8 @@ __global__ __launch_bounds__(kPkWaves * kWave, 1) void ffn_gemm_packed_kernel(
       const __amdgpu_buffer_rsrc_t pr = __builtin_amdgcn_make_buffer_rsrc(
           partial + (size_t)unit.pslot0 * kUnitFloats, 0, (uint32_t)(unit.parts * kUnitBytes),
           kBufferFlags);
-      const int lane_off = (wave * (kTW * kTM * kWave * 16) + lane * 16) * (int)sizeof(float);
+      const int lane_off =
+          (wave * (kTW * kTM * kWave * 16) + lane * 4) * (int)sizeof(float);
       const int mine = unit.piece * kUnitBytes;
 #pragma unroll
       for (int i = 0; i < kTW; ++i)
@@ -336,7 +339,7 @@ __global__ __launch_bounds__(kPkWaves * kWave, 1) void ffn_gemm_packed_kernel(
             f32x4 v;
 #pragma unroll
             for (int c = 0; c < 4; ++c) v[c] = acc[i][j][q * 4 + c];
-            const int voff = lane_off + ((i * kTM + j) * kWave * 16 + q * 4) * (int)sizeof(float);
+            const int voff = lane_off + ((i * kTM + j) * 4 + q) * kWave * 4 * (int)sizeof(float);
             store_partial(pr, voff, mine, v);
           }
       wait_vmcnt<0>();
@@ -357,7 +360,7 @@ __global__ __launch_bounds__(kPkWaves * kWave, 1) void ffn_gemm_packed_kernel(
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
               const int voff =
-                  lane_off + ((i * kTM + j) * kWave * 16 + q * 4) * (int)sizeof(float);
+                  lane_off + ((i * kTM + j) * 4 + q) * kWave * 4 * (int)sizeof(float);
               const f32x4 v = load_partial(pr, voff, soff);
 #pragma unroll
               for (int c = 0; c < 4; ++c) sum[q * 4 + c] += v[c];
