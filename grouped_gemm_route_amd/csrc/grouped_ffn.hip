@@ -484,26 +484,37 @@ __global__ __launch_bounds__(NW * kWave, 1) void ffn_gemm_bf16_kernel(
       if (threadIdx.x == 0) *flag = atomicAdd(&split_cnt[unit.split], 1);
       __syncthreads();
       if (*flag != unit.parts - 1) continue;
+      // the partials of one weight operand (all G::kTM token operands) of one
+      // piece are loaded together, so a piece costs one memory round trip per
+      // weight operand
 #pragma unroll
-      for (int i = 0; i < G::kTW; ++i)
+      for (int i = 0; i < G::kTW; ++i) {
+        f32x16 sum[G::kTM];
 #pragma unroll
-        for (int j = 0; j < G::kTM; ++j) {
-          f32x16 sum;
+        for (int j = 0; j < G::kTM; ++j)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) sum[r] = 0.0f;
-          for (int p = 0; p < unit.parts; ++p) {
-            const int soff = p * kUnitBytes;
+          for (int r = 0; r < 16; ++r) sum[j][r] = 0.0f;
+        for (int p = 0; p < unit.parts; ++p) {
+          const int soff = p * kUnitBytes;
+          f32x4 v[G::kTM][4];
+#pragma unroll
+          for (int j = 0; j < G::kTM; ++j)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
               const int voff =
                   lane_off + ((i * G::kTM + j) * 4 + q) * kWave * 4 * (int)sizeof(float);
-              const f32x4 v = load_partial(pr, voff, soff);
-#pragma unroll
-              for (int c = 0; c < 4; ++c) sum[q * 4 + c] += v[c];
+              v[j][q] = load_partial(pr, voff, soff);
             }
-          }
-          acc[i][j] = sum;
+#pragma unroll
+          for (int j = 0; j < G::kTM; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+#pragma unroll
+              for (int c = 0; c < 4; ++c) sum[j][q * 4 + c] += v[j][q][c];
         }
+#pragma unroll
+        for (int j = 0; j < G::kTM; ++j) acc[i][j] = sum[j];
+      }
       if (threadIdx.x == 0) split_cnt[unit.split] = 0;
     }
 
