@@ -45,10 +45,11 @@ namespace {
 constexpr int kMaxSplitUnits = 256;  // split pieces per launch (block slots)
 constexpr int kMaxSplit = 8;         // pieces per tile
 constexpr int kMinSplitTiles = 8;    // reduction tiles per piece, at least
-// A split costs each piece a pass of its fp32 partials through memory (about
-// as long as 40 reduction tiles of compute at BM = 128 on MI355X), so a tile
-// is split only when that takes at least this many reduction tiles off the
-// last round.
+// A split costs each piece a pass of its fp32 partials through memory, and
+// the last piece to finish the sum of all of them: on MI355X at BM = 128 about
+// 3 reduction tiles of compute for a piece and up to about 25 for the last of
+// 8, so a tile is split only when that takes at least this many reduction
+// tiles off the last round.
 constexpr int kSplitMinSaved = 48;
 
 // Workspace layout: [num_tiles | pad to 256 B][split counters: 2 x
