@@ -21,18 +21,21 @@
 //                  totals over blocks (block_excl) and their sum (demand);
 //                  counts = min(demand, capacity); offsets = exclusive scan
 //                  of counts over experts; rank_offsets[r] = offsets[r*E/W].
-//   scatter kernel (one block per token): r = block_excl + local rank; kept
-//                  iff capacity < 0 or r < capacity; writes dest and
-//                  perm_token, then copies the token's row once from HBM to
-//                  each kept destination row in 16-byte pieces.  When the
-//                  per-block count table is small, every scatter block
-//                  scans it itself and the scan kernel is not launched.
+//   scatter kernel (one block per token): loads the token's row once from
+//                  HBM in 16-byte pieces; meanwhile r = block_excl + local
+//                  rank, kept iff capacity < 0 or r < capacity, and dest and
+//                  perm_token are written; then every piece is stored to
+//                  each kept destination row.  When the per-block count
+//                  table is small, every scatter block scans it itself and
+//                  the scan kernel is not launched.
 // Because experts are numbered rank by rank, the (expert, token) order is
 // rank-major: rank r's send slice is rows [rank_offsets[r], rank_offsets[r+1]).
 #include "moe_route.h"
 #include "moe_internal.h"
 #include "block_scan.h"
 #include "fp8_codec.h"
+
+#include <type_traits>
 
 namespace moe {
 namespace {
@@ -140,19 +143,26 @@ constexpr int kScatterThreads = 256;
 // Largest per-block count table (blocks x experts) that every scatter block
 // scans for itself instead of waiting for the one-block scan kernel.
 constexpr int kFusedScanMaxCounts = 1024;
+// At most this many 16-byte pieces of the token's row per thread are loaded
+// before the index work (rows of up to 4 * kScatterThreads pieces are held
+// whole in registers); launches pick the fewest that hold the row.
+constexpr int kMaxHeld = 4;
+// buffer resource word 3 for raw 32-bit accesses (data format 32)
+constexpr int kRowBufferFlags = 0x00020000;
 
-// One block per token.  Threads 0..K-1 find the token's K rows; then the
-// block copies the row in 16-byte pieces, one piece per thread per round,
-// each piece loaded once and stored to every kept destination.
-//   kFusedScan: the per-block count table is small, so each block computes
-//   the expert offsets (and block 0 writes demand / counts / offsets /
-//   rank_offsets) and its own per-expert bases from block_counts directly;
-//   otherwise block_excl and offsets come from the scan kernel.
+// One block per token.  Every thread first loads its pieces of the token's
+// row into registers; meanwhile wave 0 finds the token's K destination rows,
+// and after one barrier the block stores each piece to every kept row.
+//   kFusedScan: the per-block count table is small, so wave 0 copies it into
+//   LDS (one coalesced round trip) and computes the expert offsets and the
+//   token's per-expert bases from it (block 0 also writes demand / counts /
+//   offsets / rank_offsets); otherwise block_excl and offsets come from the
+//   scan kernel.
 //   kFp8: the payload is the fp8 form of the bf16 row (fp8_codec.h): a
 //   piece's 16 lanes of one 128-column group agree on its scale, and each
 //   lane stores its 8 codes (8 bytes) and, once per group, the scale to
 //   every kept row.
-template <bool kFusedScan, bool kFp8>
+template <bool kFusedScan, bool kFp8, int kHeld>
 __global__ __launch_bounds__(kScatterThreads) void dispatch_scatter_kernel(
     const uint4* __restrict__ x, int row_chunks, int N,
     const int32_t* __restrict__ topk_idx, int E, int K, int W, int64_t capacity,
@@ -163,79 +173,169 @@ __global__ __launch_bounds__(kScatterThreads) void dispatch_scatter_kernel(
     float* __restrict__ x_scale, int32_t* __restrict__ perm_token,
     int32_t* __restrict__ dest) {
   __shared__ int rows[MOE_MAX_TOPK];
+  __shared__ int table[kFusedScan ? kFusedScanMaxCounts : 1];
   __shared__ int offs[kFusedScan ? kScatterThreads + 1 : 1];
-  __shared__ int wave_sums[kScatterThreads / kWave];
+  __shared__ int base[kFusedScan ? kScatterThreads : 1];
   const int t = blockIdx.x;
   const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
   const int b = t / kRankBlockTokens;
 
-  if constexpr (kFusedScan) {
-    // E <= 256 here: thread e sums its expert's counts over all blocks
-    const int B = (N + kRankBlockTokens - 1) / kRankBlockTokens;
-    int kept = 0;
-    if (tid < E) {
-      int tot = 0;
-      for (int bb = 0; bb < B; ++bb) tot += block_counts[(size_t)bb * E + tid];
-      kept = capacity < 0 ? tot : (int)min((int64_t)tot, capacity);
-      if (t == 0) {
-        demand[tid] = tot;
-        counts[tid] = kept;
-      }
-    }
-    int total = 0;
-    const int excl = block_exclusive_scan(tid < E ? kept : 0, wave_sums, &total);
-    if (tid < E) offs[tid] = excl;
-    if (tid == 0) offs[E] = total;
-    __syncthreads();
-    if (t == 0) {
-      for (int e = tid; e <= E; e += kScatterThreads) offsets[e] = offs[e];
-      const int per_rank = E / W;
-      for (int r = tid; r <= W; r += kScatterThreads) rank_offsets[r] = offs[r * per_rank];
-    }
-  }
-
-  if (tid < K) {
-    int row = -1;
-    const int e = topk_idx[(size_t)t * K + tid];
-    if ((unsigned)e < (unsigned)E) {
-      int r = local_rank[(size_t)t * K + tid];
-      int off;
-      if constexpr (kFusedScan) {
-        for (int bb = 0; bb < b; ++bb) r += block_counts[(size_t)bb * E + e];
-        off = offs[e];
-      } else {
-        r += block_excl[(size_t)b * E + e];
-        off = offsets[e];
-      }
-      if (capacity < 0 || (int64_t)r < capacity) row = off + r;
-    }
-    rows[tid] = row;
-    dest[(size_t)t * K + tid] = row;
-    if (row >= 0) perm_token[row] = t;
-  }
-  __syncthreads();
-
   const uint4* src = x + (size_t)t * row_chunks;
+  // a buffer resource over the row: pieces past its end read as zero, so the
+  // loads need no branch (a branch around each would make the compiler wait
+  // for every load right after issuing it)
+  const __amdgpu_buffer_rsrc_t row_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)src, 0, row_chunks * (int)sizeof(uint4), kRowBufferFlags);
+  u32x4 held[kHeld];
+#pragma unroll
+  for (int u = 0; u < kHeld; ++u)
+    held[u] = __builtin_amdgcn_raw_buffer_load_b128(
+        row_rsrc, (tid + u * kScatterThreads) * (int)sizeof(uint4), 0, 0);
+
+  if (tid < kWave) {
+    int e = -1, lr = 0;
+    if (lane < K) {
+      e = topk_idx[(size_t)t * K + lane];
+      lr = local_rank[(size_t)t * K + lane];
+    }
+    int row = -1;
+    if constexpr (kFusedScan) {
+      // E <= 256: lane l owns experts 4l .. 4l + 3
+      const int B = (N + kRankBlockTokens - 1) / kRankBlockTokens;
+      // all of the table's loads are issued before any is waited for
+      constexpr int kPer = kFusedScanMaxCounts / kWave;
+      int cv[kPer];
+#pragma unroll
+      for (int m = 0; m < kPer; ++m) {
+        const int i = lane + m * kWave;
+        cv[m] = i < B * E ? block_counts[i] : 0;
+      }
+#pragma unroll
+      for (int m = 0; m < kPer; ++m) {
+        const int i = lane + m * kWave;
+        if (i < B * E) table[i] = cv[m];
+      }
+      int kept[4];
+      int lane_sum = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int ex = lane * 4 + j;
+        int pre = 0, tot = 0;
+        if (ex < E) {
+          for (int bb = 0; bb < B; ++bb) {
+            const int c = table[bb * E + ex];
+            if (bb < b) pre += c;
+            tot += c;
+          }
+          base[ex] = pre;
+          if (t == 0) demand[ex] = tot;
+        }
+        kept[j] = capacity < 0 ? tot : (int)min((int64_t)tot, capacity);
+        lane_sum += kept[j];
+      }
+      int incl = lane_sum;
+#pragma unroll
+      for (int off = 1; off < kWave; off <<= 1) {
+        const int o = __shfl_up(incl, off);
+        if (lane >= off) incl += o;
+      }
+      int run = incl - lane_sum;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int ex = lane * 4 + j;
+        if (ex < E) {
+          offs[ex] = run;
+          if (t == 0) {
+            counts[ex] = kept[j];
+            offsets[ex] = run;
+          }
+        }
+        run += kept[j];
+      }
+      if (lane == kWave - 1) {
+        offs[E] = incl;
+        if (t == 0) offsets[E] = incl;
+      }
+      if (t == 0) {
+        const int per_rank = E / W;
+        for (int r = lane; r <= W; r += kWave) rank_offsets[r] = offs[r * per_rank];
+      }
+      if ((unsigned)e < (unsigned)E) {
+        const int r = lr + base[e];
+        if (capacity < 0 || (int64_t)r < capacity) row = offs[e] + r;
+      }
+    } else {
+      if ((unsigned)e < (unsigned)E) {
+        const int r = lr + block_excl[(size_t)b * E + e];
+        if (capacity < 0 || (int64_t)r < capacity) row = offsets[e] + r;
+      }
+    }
+    if (lane < K) {
+      rows[lane] = row;
+      dest[(size_t)t * K + lane] = row;
+      if (row >= 0) perm_token[row] = t;
+    }
+  }
+  // wave 0's LDS writes are done before the barrier; the row loads stay in
+  // flight across it
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  // One wait for all held pieces before the first store: a store counts in
+  // the same counter as the loads, so a wait placed later would also wait
+  // for the stores issued before it.
+#pragma unroll
+  for (int u = 0; u < kHeld; ++u) asm volatile("" ::"v"(held[u]));
+  const int extra0 = tid + kHeld * kScatterThreads;  // pieces beyond the held ones
+
   if constexpr (kFp8) {
     // row_chunks is a multiple of 16, so the lanes of a group are active
     // together
     constexpr int kPieces = kFp8Group / 8;
     const int groups = row_chunks / kPieces;
     uint2* q = static_cast<uint2*>(x_perm);
-    for (int c = tid; c < row_chunks; c += kScatterThreads) {
-      float scale;
-      const uint2 codes = quantize_piece(src[c], &scale);
+    uint2 codes[kHeld];
+    float scale[kHeld];
+#pragma unroll
+    for (int u = 0; u < kHeld; ++u) {
+      const int c = tid + u * kScatterThreads;
+      if (c < row_chunks) codes[u] = quantize_piece(__builtin_bit_cast(uint4, held[u]), &scale[u]);
+    }
+    for (int k = 0; k < K; ++k) {
+      const int rk = rows[k];
+      if (rk < 0) continue;
+#pragma unroll
+      for (int u = 0; u < kHeld; ++u) {
+        const int c = tid + u * kScatterThreads;
+        if (c < row_chunks) {
+          q[(size_t)rk * row_chunks + c] = codes[u];
+          if (c % kPieces == 0) x_scale[(size_t)rk * groups + c / kPieces] = scale[u];
+        }
+      }
+    }
+    for (int c = extra0; c < row_chunks; c += kScatterThreads) {
+      float sc;
+      const uint2 cd = quantize_piece(src[c], &sc);
       for (int k = 0; k < K; ++k) {
         const int rk = rows[k];
         if (rk < 0) continue;
-        q[(size_t)rk * row_chunks + c] = codes;
-        if (c % kPieces == 0) x_scale[(size_t)rk * groups + c / kPieces] = scale;
+        q[(size_t)rk * row_chunks + c] = cd;
+        if (c % kPieces == 0) x_scale[(size_t)rk * groups + c / kPieces] = sc;
       }
     }
   } else {
-    uint4* dst = static_cast<uint4*>(x_perm);
-    for (int c = tid; c < row_chunks; c += kScatterThreads) {
-      const uint4 v = src[c];
+    u32x4* dst = static_cast<u32x4*>(x_perm);
+    for (int k = 0; k < K; ++k) {
+      const int rk = rows[k];
+      if (rk < 0) continue;
+      u32x4* drow = dst + (size_t)rk * row_chunks;
+#pragma unroll
+      for (int u = 0; u < kHeld; ++u) {
+        const int c = tid + u * kScatterThreads;
+        if (c < row_chunks) drow[c] = held[u];
+      }
+    }
+    for (int c = extra0; c < row_chunks; c += kScatterThreads) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(src + c);
       for (int k = 0; k < K; ++k) {
         const int rk = rows[k];
         if (rk >= 0) dst[(size_t)rk * row_chunks + c] = v;
@@ -281,34 +381,39 @@ hipError_t launch_dispatch(const void* x, size_t row_bytes, int N,
   const bool fp8 = x_scale != nullptr;
   const int row_chunks = (int)(row_bytes / 16);
   const uint4* xs = static_cast<const uint4*>(x);
-  if ((int64_t)B * E <= kFusedScanMaxCounts && E <= kScatterThreads) {
-    if (fp8)
-      dispatch_scatter_kernel<true, true><<<N, kScatterThreads, 0, stream>>>(
-          xs, row_chunks, N, topk_idx, E, K, W, capacity, ws.block_counts, nullptr,
-          ws.local_rank, offsets, demand, counts, rank_offsets, x_perm, x_scale, perm_token,
-          dest);
-    else
-      dispatch_scatter_kernel<true, false><<<N, kScatterThreads, 0, stream>>>(
-          xs, row_chunks, N, topk_idx, E, K, W, capacity, ws.block_counts, nullptr,
-          ws.local_rank, offsets, demand, counts, rank_offsets, x_perm, nullptr, perm_token,
-          dest);
-    return hipGetLastError();
+  const bool fused = (int64_t)B * E <= kFusedScanMaxCounts && E <= kScatterThreads;
+  if (!fused) {
+    dispatch_scan_kernel<<<1, kScanThreads, 0, stream>>>(
+        ws.block_counts, B, E, W, capacity, ws.block_excl, demand, counts,
+        offsets, rank_offsets);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
   }
-  dispatch_scan_kernel<<<1, kScanThreads, 0, stream>>>(
-      ws.block_counts, B, E, W, capacity, ws.block_excl, demand, counts,
-      offsets, rank_offsets);
-  err = hipGetLastError();
-  if (err != hipSuccess) return err;
-  if (fp8)
-    dispatch_scatter_kernel<false, true><<<N, kScatterThreads, 0, stream>>>(
+  const int held = row_chunks <= kScatterThreads ? 1 : row_chunks <= 2 * kScatterThreads ? 2 : 4;
+  auto go = [&](auto fused_c, auto fp8_c, auto held_c) {
+    dispatch_scatter_kernel<decltype(fused_c)::value, decltype(fp8_c)::value,
+                            decltype(held_c)::value><<<N, kScatterThreads, 0, stream>>>(
         xs, row_chunks, N, topk_idx, E, K, W, capacity, ws.block_counts, ws.block_excl,
-        ws.local_rank, offsets, demand, counts, rank_offsets, x_perm, x_scale, perm_token,
-        dest);
-  else
-    dispatch_scatter_kernel<false, false><<<N, kScatterThreads, 0, stream>>>(
-        xs, row_chunks, N, topk_idx, E, K, W, capacity, ws.block_counts, ws.block_excl,
-        ws.local_rank, offsets, demand, counts, rank_offsets, x_perm, nullptr, perm_token,
-        dest);
+        ws.local_rank, offsets, demand, counts, rank_offsets, x_perm,
+        fp8 ? x_scale : nullptr, perm_token, dest);
+  };
+  auto by_held = [&](auto fused_c, auto fp8_c) {
+    using I = std::integral_constant<int, 1>;
+    using II = std::integral_constant<int, 2>;
+    using IV = std::integral_constant<int, kMaxHeld>;
+    if (held == 1) go(fused_c, fp8_c, I{});
+    else if (held == 2) go(fused_c, fp8_c, II{});
+    else go(fused_c, fp8_c, IV{});
+  };
+  using T = std::true_type;
+  using F = std::false_type;
+  if (fused) {
+    if (fp8) by_held(T{}, T{});
+    else by_held(T{}, F{});
+  } else {
+    if (fp8) by_held(F{}, T{});
+    else by_held(F{}, F{});
+  }
   return hipGetLastError();
 }
 
