@@ -162,6 +162,8 @@ constexpr int kRowBufferFlags = 0x00020000;
 //   piece's 16 lanes of one 128-column group agree on its scale, and each
 //   lane stores its 8 codes (8 bytes) and, once per group, the scale to
 //   every kept row.
+//   kHeld: pieces per thread loaded ahead (1, 2 or kMaxHeld); pieces past
+//   kHeld * kScatterThreads are loaded and stored one at a time afterwards.
 template <bool kFusedScan, bool kFp8, int kHeld>
 __global__ __launch_bounds__(kScatterThreads) void dispatch_scatter_kernel(
     const uint4* __restrict__ x, int row_chunks, int N,
