@@ -11,19 +11,63 @@
 // imbalance: with kSigmoid the weight is 1 / (1 + exp(-logit)) and the
 // softmax reductions are skipped; the choice is the same.
 //
-// Mapping: a group of L lanes (L = 8..64, a power of two) owns one token and
-// holds VPL = ceil(E / L) logits per lane, expert e = lane_in_group + i * L,
-// so a group's loads are contiguous.  The max, the sum of exponentials and K
-// argmax rounds are butterfly reductions inside the group (xor shuffles never
-// leave an aligned group).  The comparator is (a > b) or (a == b and lower
-// index), a total order on (logit, index) pairs, so every lane of the group
-// ends each round with the same winner.
+// Mapping: a group of L lanes (L = 8 or 16) owns one token and holds VPL =
+// ceil(E / L) logits per lane, expert e = lane_in_group + i * L, so a
+// group's loads are contiguous and a wave routes 64 / L tokens at once.  The
+// group maximum and the sum of exponentials are reductions whose steps pair
+// lanes inside 16-lane rows by DPP lane moves (quad swaps, half-row and row
+// mirrors); each step combines two values commutatively, so every lane of
+// the group ends with the same bits.  A round of the top-K takes the group
+// maximum of the remaining logits; each lane then names the lowest of its
+// experts holding that maximum, and a group minimum over those names gives
+// the lowest expert index with the maximum logit.  That is the order (a > b)
+// or (a == b and lower index), a total order on (logit, index) pairs.  Lane
+// k of the group keeps round k's result, and lanes 0 .. K - 1 store the
+// token's K results together (K <= 16 <= L whenever E > 8).
 #include "moe_internal.h"
 
 #include <math.h>
 
 namespace moe {
 namespace {
+
+// One DPP lane move of a float (row and bank masks full).
+template <int kCtrl>
+__device__ __forceinline__ float dpp_f32(float a) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, a), kCtrl, 0xf, 0xf, false));
+}
+constexpr int kDppXor1 = 0xb1;        // quad_perm [1, 0, 3, 2]
+constexpr int kDppXor2 = 0x4e;        // quad_perm [2, 3, 0, 1]
+constexpr int kDppHalfMirror = 0x141; // lane i <- 7 - i within each 8 lanes
+constexpr int kDppMirror = 0x140;     // lane i <- 15 - i within each 16 lanes
+
+// Maximum (kMax) or sum of a over each aligned group of L = 8 or 16 lanes,
+// the same bits in every lane of the group.  After the two quad steps every
+// lane holds its quad's value; the half mirror pairs each lane with one of
+// the other quad of its 8, the mirror with one of the other 8 of its 16.
+template <int L, bool kMax>
+__device__ __forceinline__ float group_reduce(float a) {
+  static_assert(L == 8 || L == 16, "groups of 8 or 16 lanes");
+  auto op = [](float x, float y) __attribute__((always_inline)) {
+    return kMax ? fmaxf(x, y) : x + y;
+  };
+  a = op(a, dpp_f32<kDppXor1>(a));
+  a = op(a, dpp_f32<kDppXor2>(a));
+  a = op(a, dpp_f32<kDppHalfMirror>(a));
+  if (L == 16) a = op(a, dpp_f32<kDppMirror>(a));
+  return a;
+}
+
+// Minimum of an int over each aligned group of L = 8 or 16 lanes.
+template <int L>
+__device__ __forceinline__ int group_min(int a) {
+  a = min(a, __builtin_amdgcn_mov_dpp(a, kDppXor1, 0xf, 0xf, false));
+  a = min(a, __builtin_amdgcn_mov_dpp(a, kDppXor2, 0xf, 0xf, false));
+  a = min(a, __builtin_amdgcn_mov_dpp(a, kDppHalfMirror, 0xf, 0xf, false));
+  if (L == 16) a = min(a, __builtin_amdgcn_mov_dpp(a, kDppMirror, 0xf, 0xf, false));
+  return a;
+}
 
 template <int L, int VPL, bool kSigmoid>
 __global__ __launch_bounds__(256) void route_topk_kernel(
@@ -50,49 +94,40 @@ __global__ __launch_bounds__(256) void route_topk_kernel(
     m = v[0];
 #pragma unroll
     for (int i = 1; i < VPL; ++i) m = fmaxf(m, v[i]);
-#pragma unroll
-    for (int off = L / 2; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+    m = group_reduce<L, true>(m);
     s = 0.0f;
 #pragma unroll
     for (int i = 0; i < VPL; ++i) s += expf(v[i] - m);  // padding: exp(-inf) = 0
-#pragma unroll
-    for (int off = L / 2; off >= 1; off >>= 1) s += __shfl_xor(s, off);
+    s = group_reduce<L, false>(s);
   }
 
   float wsum = 0.0f;
-  int32_t* idx_out = topk_idx + (size_t)tok * K;
-  float* w_out = topk_w + (size_t)tok * K;
+  int my_idx = 0;
+  float my_w = 0.0f;
   for (int k = 0; k < K; ++k) {
-    float bv = v[0];
-    int bi = j;
+    float lb = v[0];
 #pragma unroll
-    for (int i = 1; i < VPL; ++i) {
-      if (v[i] > bv) {  // later i has a higher index: strict > keeps ties low
-        bv = v[i];
-        bi = j + i * L;
-      }
-    }
+    for (int i = 1; i < VPL; ++i) lb = fmaxf(lb, v[i]);
+    const float bv = group_reduce<L, true>(lb);
+    // this lane's lowest expert holding bv (E if none), then the group's
+    int le = E;
 #pragma unroll
-    for (int off = L / 2; off >= 1; off >>= 1) {
-      const float ov = __shfl_xor(bv, off);
-      const int oi = __shfl_xor(bi, off);
-      if (ov > bv || (ov == bv && oi < bi)) {
-        bv = ov;
-        bi = oi;
-      }
-    }
+    for (int i = VPL - 1; i >= 0; --i)
+      if (v[i] == bv) le = j + i * L;
+    const int bi = group_min<L>(le);
     const float p = kSigmoid ? 1.0f / (1.0f + expf(-bv)) : expf(bv - m) / s;
     wsum += p;
 #pragma unroll
     for (int i = 0; i < VPL; ++i)
       if (j + i * L == bi) v[i] = -INFINITY;  // taken: never wins again
-    if (valid && j == 0) {
-      idx_out[k] = bi;
-      w_out[k] = p;
+    if (j == k) {
+      my_idx = bi;
+      my_w = p;
     }
   }
-  if (renormalize && valid && j == 0) {
-    for (int k = 0; k < K; ++k) w_out[k] = w_out[k] / wsum;
+  if (valid && j < K) {
+    topk_idx[(size_t)tok * K + j] = my_idx;
+    topk_w[(size_t)tok * K + j] = renormalize ? my_w / wsum : my_w;
   }
 }
 
@@ -120,12 +155,12 @@ hipError_t launch_route_topk(const float* logits, int N, int E, int K, bool sigm
   const bool g = sigmoid;
   if (E <= 8) return launch<8, 1>(logits, N, E, K, g, renormalize, topk_idx, topk_w, stream);
   if (E <= 16) return launch<16, 1>(logits, N, E, K, g, renormalize, topk_idx, topk_w, stream);
-  if (E <= 32) return launch<32, 1>(logits, N, E, K, g, renormalize, topk_idx, topk_w, stream);
-  if (E <= 64) return launch<64, 1>(logits, N, E, K, g, renormalize, topk_idx, topk_w, stream);
-  if (E <= 128) return launch<64, 2>(logits, N, E, K, g, renormalize, topk_idx, topk_w, stream);
-  if (E <= 256) return launch<64, 4>(logits, N, E, K, g, renormalize, topk_idx, topk_w, stream);
-  if (E <= 512) return launch<64, 8>(logits, N, E, K, g, renormalize, topk_idx, topk_w, stream);
-  return launch<64, 16>(logits, N, E, K, g, renormalize, topk_idx, topk_w, stream);
+  if (E <= 32) return launch<16, 2>(logits, N, E, K, g, renormalize, topk_idx, topk_w, stream);
+  if (E <= 64) return launch<16, 4>(logits, N, E, K, g, renormalize, topk_idx, topk_w, stream);
+  if (E <= 128) return launch<16, 8>(logits, N, E, K, g, renormalize, topk_idx, topk_w, stream);
+  if (E <= 256) return launch<16, 16>(logits, N, E, K, g, renormalize, topk_idx, topk_w, stream);
+  if (E <= 512) return launch<16, 32>(logits, N, E, K, g, renormalize, topk_idx, topk_w, stream);
+  return launch<16, 64>(logits, N, E, K, g, renormalize, topk_idx, topk_w, stream);
 }
 
 }  // namespace moe
