@@ -51,6 +51,15 @@ data goes as FP8 instead of BF16, halving the bytes):
             round-to-nearest-even) with the fp32 scale amax / 448, and read
             back as code value * scale.
 
+Residual-MoE ("MoE Inference Communication", section "PR-MoE：从”所有层一样多
+专家”到”哪里需要哪里多”", Phenomenon-II: one fixed dense MLP that every token
+passes through, plus the routed expert, with the two outputs added; it
+matches top-2 routing in quality at top-1's exchange volume):
+
+  shared    y_shared = the SwiGLU MLP with its own weights on every token
+            row, rounded to storage; combine starts each token's sum from
+            y_shared[t] (unweighted) and adds the kept pairs in ascending k.
+
 Where the pages say nothing (the gate function, the tie-break, the order
 inside an expert, the capacity formula, the FFN form) the oracle takes the
 plain reading: fp32-input softmax, lowest index wins ties, ascending token
@@ -471,11 +480,22 @@ def grouped_ffn(x_perm, offsets, expert_weights, act):
     return h_all, y_all
 
 
+def shared_expert(x, wg, wu, wd, act):
+    """The dense MLP of a Residual-MoE layer ("MoE Inference Communication",
+    section "PR-MoE：从”所有层一样多专家”到”哪里需要哪里多”", Phenomenon-II and
+    the Residual bullet: every token passes through one fixed dense MLP
+    beside its routed expert).  Read here as an expert of the same SwiGLU
+    form with its own weights (wg, wu [ffn_s, d]; wd [d, ffn_s]) applied to
+    every token row of x [N, d]; returns y_shared [N, d] rounded to storage.
+    """
+    return expert_ffn(x, wg, wu, wd, act)[1]
+
+
 # --------------------------------------------------------------------------
 # combine
 # --------------------------------------------------------------------------
 
-def combine(y_perm, dest, topk_w, act):
+def combine(y_perm, dest, topk_w, act, shared=None):
     """Weighted merge back to token order.
 
     "MoE 专家并行的 All-to-All 通信瓶颈", flowchart "加权合并回原 token 顺序":
@@ -483,6 +503,13 @@ def combine(y_perm, dest, topk_w, act):
     in float64, rounded to storage.  A dropped pair adds nothing ("MoE 推理
     服务工程真相 2026", section 4.3: the dropped expert's output is zero); a
     token with every pair dropped gets a zero row.
+
+    shared [N, d] (storage values), for a Residual-MoE layer ("MoE Inference
+    Communication", section "PR-MoE：从”所有层一样多专家”到”哪里需要哪里多”",
+    Phenomenon-II: a fixed dense MLP that every token passes through, whose
+    output is added to the routed expert's): the sum starts from shared[t],
+    unweighted, and the kept pairs are added to it in ascending k; a token
+    with every pair dropped gets shared[t].
     """
     y_perm = np.asarray(y_perm, dtype=np.float64)
     dest = np.asarray(dest)
@@ -490,6 +517,8 @@ def combine(y_perm, dest, topk_w, act):
     N, K = dest.shape
     d = y_perm.shape[1]
     out = np.zeros((N, d), dtype=np.float64)
+    if shared is not None:
+        out += np.asarray(shared, dtype=np.float64)
     for k in range(K):
         rows = dest[:, k]
         ok = rows >= 0
@@ -582,12 +611,13 @@ def dequantize_fp8(codes, scales, group=FP8_GROUP):
 
 
 def layer(logits, x, expert_weights, K, W, cap, act, renormalize=False, gate="softmax",
-          reroute=False, fp8=False):
+          reroute=False, fp8=False, shared_weights=None):
     """Route (optionally re-routing overflow), dispatch, FFN and combine;
     returns every intermediate.  fp8=True sends both exchanges as fp8: the
     packed rows are quantized (x8, x_scale) and read back as bf16 for the
     FFN; its output rows are quantized (y8, y_scale) and combined from their
-    fp8 values."""
+    fp8 values.  shared_weights = (wg, wu, wd) makes it a Residual-MoE
+    layer: the shared MLP's output on x (y_shared) is added in combine."""
     N, E = np.asarray(logits).shape
     idx, w = route(logits, K, renormalize, gate)
     rerouted = np.zeros(E, dtype=np.int32)
@@ -606,7 +636,11 @@ def layer(logits, x, expert_weights, K, W, cap, act, renormalize=False, gate="so
         y8, ys = quantize_fp8(y)
         y_in = dequantize_fp8(y8, ys).astype(np.float64)
         res.update(y8=y8, y_scale=ys)
-    out = combine(y_in, disp["dest"], w, act)
+    y_shared = None
+    if shared_weights is not None:
+        y_shared = shared_expert(x, *shared_weights, act)
+        res.update(y_shared=y_shared)
+    out = combine(y_in, disp["dest"], w, act, shared=y_shared)
     res.update(topk_idx=idx, topk_w=w, x_perm=x_perm, h=h, y_perm=y, out=out,
                rerouted=rerouted)
     return res

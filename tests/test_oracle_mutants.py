@@ -8,6 +8,7 @@ from oracle import moe_oracle as O
 import test_oracle as P
 import test_oracle_reroute as PR
 import test_oracle_fp8 as PF
+import test_oracle_residual as PRS
 
 _route = O.route
 _dispatch = O.dispatch
@@ -128,13 +129,32 @@ def _ffn_no_silu(R, wg, wu, wd, act):
     return h, O.round_storage(h @ np.asarray(wd, np.float64).T, act)
 
 
-def _combine_unweighted(y_perm, dest, topk_w, act):
-    return _combine(y_perm, dest, np.ones_like(np.asarray(topk_w)), act)
+def _combine_unweighted(y_perm, dest, topk_w, act, shared=None):
+    return _combine(y_perm, dest, np.ones_like(np.asarray(topk_w)), act, shared)
 
 
-def _combine_includes_dropped(y_perm, dest, topk_w, act):
+def _combine_includes_dropped(y_perm, dest, topk_w, act, shared=None):
     dest = np.where(np.asarray(dest) < 0, 0, dest)
-    return _combine(y_perm, dest, topk_w, act)
+    return _combine(y_perm, dest, topk_w, act, shared)
+
+
+def _combine_shared_weighted(y_perm, dest, topk_w, act, shared=None):
+    if shared is not None:
+        shared = np.asarray(shared, np.float64) * np.asarray(topk_w, np.float64)[:, :1]
+    return _combine(y_perm, dest, topk_w, act, shared)
+
+
+def _combine_shared_rounded_apart(y_perm, dest, topk_w, act, shared=None):
+    out = _combine(y_perm, dest, topk_w, act)
+    if shared is not None:
+        out = O.round_storage(out + np.asarray(shared, np.float64), act)
+    return out
+
+
+def _shared_expert_no_silu(x, wg, wu, wd, act):
+    R = np.asarray(x, np.float64)
+    h = O.round_storage((R @ np.asarray(wg, np.float64).T) * (R @ np.asarray(wu, np.float64).T), act)
+    return O.round_storage(h @ np.asarray(wd, np.float64).T, act)
 
 
 MUTANTS = {
@@ -151,6 +171,9 @@ MUTANTS = {
     "reroute_ignores_room": ("reroute_overflow", _reroute_ignores_room),
     "e4m3_ties_away": ("e4m3_encode", _e4m3_ties_away),
     "quantize_scale_447": ("quantize_fp8", _quantize_scale_447),
+    "combine_shared_weighted": ("combine", _combine_shared_weighted),
+    "combine_shared_rounded_apart": ("combine", _combine_shared_rounded_apart),
+    "shared_expert_no_silu": ("shared_expert", _shared_expert_no_silu),
 }
 
 PINS = [
@@ -172,6 +195,11 @@ PINS = [
     lambda: PF.test_e4m3_encode_matches_torch_cast(),
     lambda: PF.test_quantize_group_properties(),
     lambda: PF.test_quantize_is_exact_on_representable_groups(),
+    lambda: [PRS.test_residual_layer_against_dense_recompute(c) for c in (-1, 2)],
+    lambda: [PRS.test_residual_all_dropped_is_the_shared_mlp(a) for a in ("bf16", "f32")],
+    lambda: PRS.test_shared_mlp_equal_to_the_only_expert_doubles_the_output("bf16"),
+    lambda: PRS.test_zero_shared_output_leaves_the_layer_unchanged(),
+    lambda: PRS.test_residual_combine_rounds_once_and_adds_shared_unweighted(),
 ]
 
 
