@@ -61,6 +61,8 @@ def parse():
                    help="reps of the cold-cache dispatch/combine timing (0 skips it)")
     p.add_argument("--no-exchange", action="store_true",
                    help="skip the virtual multi-source exchange measurements")
+    p.add_argument("--no-residual", action="store_true",
+                   help="skip the Residual-MoE (top-1 + shared MLP) measurements")
     p.add_argument("--plain-weights", action="store_true",
                    help="time the FFN on row-major weights (moe_grouped_ffn) instead of "
                         "packed ones")
@@ -311,6 +313,10 @@ def main():
         if cfg["act"] == "bf16" and d % 128 == 0:
             result["fp8_payload"] = fp8_block(B, layer, inp["x"], cfg, M, stream,
                                               args.cold_reps)
+    if not args.no_residual and cfg["act"] == "bf16":
+        del layer
+        packed = ffn_args[0] if weights == "packed" else None
+        result["residual_moe"] = residual_block(B, synth, inp, cfg, b, stream, packed)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_sample_tokens)
     print(json.dumps(result))
@@ -518,6 +524,47 @@ def fp8_block(B, layer, x, cfg, M, stream, cold_reps):
         "quantize_rows_GBps": q_b / (t_q * 1e-3) / 1e9,
         "dequantize_rows_us": t_dq * 1e3,
         "dequantize_rows_GBps": q_b / (t_dq * 1e-3) / 1e9,
+    }
+
+
+def residual_block(B, synth, inp, cfg, b, stream, packed=None, reps=10):
+    """Residual-MoE ("MoE Inference Communication", section "PR-MoE：从”所有层
+    一样多专家”到”哪里需要哪里多”", Phenomenon-II) at the workload's shape:
+    top-1 routing plus a shared MLP as wide as an expert, on every token, its
+    output added in the combine.  Times the whole layer step (route, dispatch,
+    grouped FFN, shared MLP, residual combine; packed weights), the shared MLP
+    and the residual combine alone, and compares the exchange's wire bytes
+    with the workload's top-K layer (the reason for the design: top-1's
+    all-to-all volume)."""
+    import torch
+
+    N, d, ffn, E, W, K = cfg["N"], cfg["d"], cfg["ffn"], cfg["E"], cfg["W"], cfg["K"]
+    cap = -1
+    if cfg.get("C") is not None:
+        cap = B.moe_capacity(cfg["C"], N, 1, E)
+    layer = B.MoeLayer(N, d, ffn, E, 1, W, cap, torch.bfloat16, "cuda:0", shared_ffn=ffn)
+    experts = packed or B.moe_pack_ffn_weights(inp["w_gate"], inp["w_up"], inp["w_down"])
+    shared = B.moe_pack_ffn_weights(*synth.make_shared_weights(cfg, "cuda:0"))
+    step_ms = _timed(stream, lambda: layer.forward(inp["logits"], inp["x"], experts,
+                                                   shared=shared), reps=reps)
+    shared_ms = _timed(stream, lambda: layer.shared(inp["x"], shared), reps=reps)
+    comb_ms = _timed(stream, lambda: layer.combine(residual=True), reps=reps)
+    M1 = int(layer.disp["offsets"][E].item())
+    comb_bytes = M1 * d * b + 2 * N * d * b + 8 * N
+    shared_flops = 6.0 * N * d * ffn
+    M_k = N * K if cap < 0 else None
+    return {
+        "shape": f"top-1 routing + shared SwiGLU MLP (width {ffn}) on all {N} tokens, "
+                 f"capacity {cap}",
+        "kept_rows_top1": M1,
+        "layer_ms": step_ms,
+        "tokens_per_s": N / (step_ms * 1e-3),
+        "shared_mlp_ms": shared_ms,
+        "shared_mlp_TFLOPs": shared_flops / (shared_ms * 1e-3) / 1e12,
+        "residual_combine_us": comb_ms * 1e3,
+        "residual_combine_GBps": comb_bytes / (comb_ms * 1e-3) / 1e9,
+        "wire_bytes_per_direction_top1": M1 * d * b,
+        "wire_bytes_per_direction_topK_dropless": (M_k * d * b) if M_k is not None else None,
     }
 
 

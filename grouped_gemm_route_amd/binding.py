@@ -45,6 +45,7 @@ SIGNATURES = [
     ("moe_grouped_ffn_packed", ctypes.c_int,
      [_P, _I32, _I32, _I32, _P, _I64, _P, _P, _P, _P, _P, _SZ, _P]),
     ("moe_combine", ctypes.c_int, [_P, _I32, _I32, _I32, _I32, _P, _P, _P, _P]),
+    ("moe_combine_residual", ctypes.c_int, [_P, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _P]),
     ("moe_router_logits", ctypes.c_int, [_P, _I32, _I32, _I32, _P, _I32, _P, _P]),
     ("moe_exchange_workspace_bytes", _SZ, [_I32, _I32]),
     ("moe_exchange_plan", ctypes.c_int,
@@ -518,6 +519,47 @@ def moe_combine(y_perm, dest, topk_w, out=None):
     return out
 
 
+def moe_combine_residual(y_perm, dest, topk_w, shared, out=None):
+    """Residual-MoE combine: out[t] = shared[t] + the weighted sum of the
+    token's kept rows; returns out [N, d]."""
+    _need(y_perm, "y_perm")
+    code = _act_code(y_perm, "y_perm")
+    dev = y_perm.device
+    _need(dest, "dest", torch.int32, dev)
+    _need(topk_w, "topk_w", torch.float32, dev)
+    N, K = dest.shape
+    d = y_perm.shape[1]
+    if tuple(topk_w.shape) != (N, K):
+        raise ValueError("topk_w must match dest [N, K]")
+    _need(shared, "shared", y_perm.dtype, dev)
+    if shared.numel() < N * d or shared.shape[-1] != d:
+        raise ValueError("shared must be [N, d]")
+    if out is None:
+        out = torch.empty(N, d, dtype=y_perm.dtype, device=dev)
+    _need(out, "out", y_perm.dtype, dev)
+    if out.numel() < N * d:
+        raise ValueError("out too small")
+    _check("moe_combine_residual", load_library().moe_combine_residual(
+        _ptr(y_perm), code, N, d, K, _ptr(dest), _ptr(topk_w), _ptr(shared), _ptr(out),
+        _stream(y_perm)))
+    return out
+
+
+def moe_shared_ffn(x, offsets, w_gate, w_up=None, w_down=None, h=None, y=None,
+                   workspace=None):
+    """The dense MLP of a Residual-MoE layer on every token row of x: the
+    grouped FFN with one expert holding rows [0, N).  offsets: device int32
+    tensor holding {0, N}; weights [1, ffn_s, d] / [1, d, ffn_s], or w_gate
+    alone: PackedFfnWeights of one expert.  Returns (h, y)."""
+    if isinstance(w_gate, PackedFfnWeights):
+        if w_gate.E != 1:
+            raise ValueError("the shared MLP is one expert")
+        return moe_grouped_ffn_packed(x, offsets, w_gate, x.shape[0], h, y, workspace)
+    if w_gate.shape[0] != 1:
+        raise ValueError("the shared MLP is one expert")
+    return moe_grouped_ffn(x, offsets, w_gate, w_up, w_down, x.shape[0], h, y, workspace)
+
+
 def moe_exchange_workspace_bytes(E, W):
     return int(load_library().moe_exchange_workspace_bytes(E, W))
 
@@ -591,11 +633,13 @@ class MoeLayer:
     next-best experts between route and dispatch.  fp8=True (bf16 layers)
     sends both exchanges as fp8: dispatch packs e4m3 codes, the rows are
     turned back into bf16 for the FFN, its output rows are quantized and
-    the combine reads them as fp8.
+    the combine reads them as fp8.  shared_ffn > 0 makes it a Residual-MoE
+    layer with a shared MLP of that width: ``forward(..., shared=...)`` runs
+    it on every token and adds its output in the combine.
     """
 
     def __init__(self, N, d, ffn, E, K, W, capacity, dtype, device, renormalize=False,
-                 gate="softmax", reroute=False, fp8=False):
+                 gate="softmax", reroute=False, fp8=False, shared_ffn=0):
         self.N, self.d, self.ffn_dim, self.E, self.K, self.W = N, d, ffn, E, K, W
         self.capacity = int(capacity)
         self.renormalize = renormalize
@@ -618,6 +662,15 @@ class MoeLayer:
         self.rerouted = torch.zeros(E, dtype=torch.int32, device=dev)
         self.reroute_ws = (torch.empty(max(1, moe_reroute_workspace_bytes(N, E, K)),
                                        dtype=torch.uint8, device=dev) if reroute else None)
+        self.shared_ffn = int(shared_ffn)
+        if self.shared_ffn > 0:
+            if fp8:
+                raise ValueError("the Residual-MoE combine reads bf16 or fp32 rows")
+            self.shared_offsets = torch.tensor([0, N], dtype=torch.int32, device=dev)
+            self.h_shared = torch.empty(N, self.shared_ffn, dtype=dtype, device=dev)
+            self.y_shared = torch.empty(N, d, dtype=dtype, device=dev)
+            self.shared_ws = torch.empty(max(1, moe_grouped_ffn_workspace_bytes(N, 1, dtype)),
+                                         dtype=torch.uint8, device=dev)
         if fp8:
             self.disp8 = alloc_dispatch_fp8_outputs(N, d, E, K, W, dev)
             self.disp8["x_perm"] = self.disp["x_perm"]     # receive-side bf16 rows
@@ -651,15 +704,33 @@ class MoeLayer:
         return moe_grouped_ffn(self.disp["x_perm"], self.disp["offsets"], w_gate, w_up, w_down,
                                self.max_rows, self.h, self.y_perm, self.ffn_ws)
 
-    def combine(self):
+    def shared(self, x, w_gate, w_up=None, w_down=None):
+        """The shared MLP on every token (Residual-MoE layers)."""
+        if self.shared_ffn <= 0:
+            raise ValueError("layer built without a shared MLP (shared_ffn=0)")
+        return moe_shared_ffn(x, self.shared_offsets, w_gate, w_up, w_down, self.h_shared,
+                              self.y_shared, self.shared_ws)
+
+    def combine(self, residual=False):
+        if residual:
+            return moe_combine_residual(self.y_perm, self.disp["dest"], self.topk_w,
+                                        self.y_shared, self.out)
         if not self.fp8:
             return moe_combine(self.y_perm, self.disp["dest"], self.topk_w, self.out)
         n_rows = self.disp["offsets"][self.E:]
         moe_fp8_quantize_rows(self.y_perm, n_rows, self.max_rows, self.y8, self.y_scale)
         return moe_combine_fp8(self.y8, self.y_scale, self.disp["dest"], self.topk_w, self.out)
 
-    def forward(self, logits, x, w_gate, w_up=None, w_down=None):
+    def forward(self, logits, x, w_gate, w_up=None, w_down=None, shared=None):
+        """shared (Residual-MoE layers): the shared MLP's weights as a tuple
+        (w_gate, w_up, w_down) of one expert, or PackedFfnWeights of one."""
         self.route(logits)
         self.dispatch(x)
         self.ffn(w_gate, w_up, w_down)
-        return self.combine()
+        if shared is None:
+            return self.combine()
+        if isinstance(shared, PackedFfnWeights):
+            self.shared(x, shared)
+        else:
+            self.shared(x, *shared)
+        return self.combine(residual=True)

@@ -373,22 +373,43 @@ int moe_grouped_ffn_packed(const void* x_perm, int32_t d, int32_t ffn, int32_t E
                     "moe_grouped_ffn_packed");
 }
 
+namespace {
+int combine_checks(const char* name, const void* y_perm, int32_t dtype, int32_t N, int32_t d,
+                   int32_t K, const int32_t* dest, const float* topk_w, const void* out) {
+  if (!y_perm || !dest || !topk_w || !out)
+    return fail(MOE_ERR_INVALID_ARG, "%s: null pointer", name);
+  const int es = elem_size(dtype);
+  if (es == 0) return fail(MOE_ERR_UNSUPPORTED, "%s: dtype %d", name, dtype);
+  if (N < 1 || d < 1 || K < 1)
+    return fail(MOE_ERR_INVALID_ARG, "%s: need N, d, K >= 1", name);
+  if (((int64_t)d * es) % 16 != 0)
+    return fail(MOE_ERR_INVALID_ARG, "%s: row bytes d*%d must be a multiple of 16", name, es);
+  if (K > MOE_MAX_TOPK)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: K <= %d supported", name, MOE_MAX_TOPK);
+  return MOE_OK;
+}
+}  // namespace
+
 int moe_combine(const void* y_perm, int32_t dtype, int32_t N, int32_t d,
                 int32_t K, const int32_t* dest, const float* topk_w, void* out,
                 void* stream) {
-  if (!y_perm || !dest || !topk_w || !out)
-    return fail(MOE_ERR_INVALID_ARG, "moe_combine: null pointer");
-  const int es = elem_size(dtype);
-  if (es == 0) return fail(MOE_ERR_UNSUPPORTED, "moe_combine: dtype %d", dtype);
-  if (N < 1 || d < 1 || K < 1)
-    return fail(MOE_ERR_INVALID_ARG, "moe_combine: need N, d, K >= 1");
-  if (((int64_t)d * es) % 16 != 0)
-    return fail(MOE_ERR_INVALID_ARG, "moe_combine: row bytes d*%d must be a multiple of 16", es);
-  if (K > MOE_MAX_TOPK)
-    return fail(MOE_ERR_UNSUPPORTED, "moe_combine: K <= %d supported", MOE_MAX_TOPK);
+  const int rc = combine_checks("moe_combine", y_perm, dtype, N, d, K, dest, topk_w, out);
+  if (rc != MOE_OK) return rc;
   return hip_status(moe::launch_combine(y_perm, dtype == MOE_DTYPE_BF16, N, d,
-                                        K, dest, topk_w, out, as_stream(stream)),
+                                        K, dest, topk_w, nullptr, out, as_stream(stream)),
                     "moe_combine");
+}
+
+int moe_combine_residual(const void* y_perm, int32_t dtype, int32_t N, int32_t d, int32_t K,
+                         const int32_t* dest, const float* topk_w, const void* shared,
+                         void* out, void* stream) {
+  const int rc =
+      combine_checks("moe_combine_residual", y_perm, dtype, N, d, K, dest, topk_w, out);
+  if (rc != MOE_OK) return rc;
+  if (!shared) return fail(MOE_ERR_INVALID_ARG, "moe_combine_residual: null pointer");
+  return hip_status(moe::launch_combine(y_perm, dtype == MOE_DTYPE_BF16, N, d, K, dest,
+                                        topk_w, shared, out, as_stream(stream)),
+                    "moe_combine_residual");
 }
 
 int moe_router_logits(const void* x, int32_t dtype, int32_t N, int32_t d,

@@ -82,9 +82,11 @@ hipError_t launch_grouped_ffn_packed(const void* x_perm, int d, int ffn, int E,
                                      const void* packed_up, const void* packed_down, void* h,
                                      void* y_perm, void* workspace, hipStream_t stream);
 
+// shared: the Residual-MoE shared MLP's output [N, d] added to each token's
+// sum, or null for the plain combine.
 hipError_t launch_combine(const void* y_perm, bool bf16_data, int N, int d,
                           int K, const int32_t* dest, const float* topk_w,
-                          void* out, hipStream_t stream);
+                          const void* shared, void* out, hipStream_t stream);
 
 // fp8 payload (fp8_codec.h).  Row kernels act on rows [0, min(*n_rows,
 // max_rows)) of d columns; d is a multiple of 128.

@@ -138,6 +138,22 @@ def make_weights(cfg, device="cpu"):
     return wg, wu, wd
 
 
+def make_shared_weights(cfg, device="cpu", ffn_s=None):
+    """The dense MLP of a Residual-MoE layer as one expert: w_gate, w_up
+    [1, ffn_s, d] and w_down [1, d, ffn_s] (ffn_s defaults to the experts'
+    width), N(0, std = 1/sqrt(fan_in)), activation type."""
+    d = cfg["d"]
+    ffn_s = ffn_s or cfg["ffn"]
+    dt = TORCH_DTYPE[cfg["act"]]
+    out = []
+    for name, shape, fan_in in (("shared_gate", (1, ffn_s, d), d), ("shared_up", (1, ffn_s, d), d),
+                                ("shared_down", (1, d, ffn_s), ffn_s)):
+        g = _gen(cfg, name, 0, device)
+        z = torch.randn(*shape, generator=g, device=device, dtype=torch.float32)
+        out.append((z * (1.0 / math.sqrt(fan_in))).to(dt))
+    return tuple(out)
+
+
 def make_router(cfg, device="cpu"):
     """Router weights w_router [E, d], N(0, std = 1/sqrt(d)), activation type."""
     g = _gen(cfg, "w_router", 0, device)

@@ -317,6 +317,26 @@ int moe_combine(const void* y_perm, int32_t dtype, int32_t N, int32_t d,
                 void* stream);
 
 /*
+ * Combine of a Residual-MoE layer.  "MoE Inference Communication", section
+ * "PR-MoE：从”所有层一样多专家”到”哪里需要哪里多”", Phenomenon-II: every token
+ * also passes through one fixed dense MLP, whose output is added to the
+ * routed expert's (with top-1 routing this matches top-2 in quality at
+ * top-1's exchange volume).  The shared MLP is an ordinary SwiGLU FFN: run
+ * moe_grouped_ffn or moe_grouped_ffn_packed on x with E = 1 and offsets =
+ * {0, N} to get `shared`.
+ *   out[t] = shared[t] + sum over k = 0..K-1 with dest[t,k] >= 0 of
+ *            topk_w[t,k] * y_perm[dest[t,k]]
+ * accumulated in fp32 starting from shared[t] (unweighted), then ascending
+ * k, rounded once to dtype; a token with every pair dropped gets shared[t].
+ *   shared [N, d] of dtype (row-major, caller-owned device memory); the
+ *   other arguments as in moe_combine.
+ * Checks: as moe_combine, plus shared non-null (INVALID_ARG).
+ */
+int moe_combine_residual(const void* y_perm, int32_t dtype, int32_t N, int32_t d, int32_t K,
+                         const int32_t* dest, const float* topk_w, const void* shared,
+                         void* out, void* stream);
+
+/*
  * FP8 exchange payload.  "MoE 推理服务工程真相 2026", section 6.3: the
  * all-to-all token data goes as FP8 instead of BF16, halving its bytes.
  * Format: rows of d columns (d a multiple of 128) are cut into groups of

@@ -646,13 +646,16 @@ def layer(logits, x, expert_weights, K, W, cap, act, renormalize=False, gate="so
     return res
 
 
-def token_outputs(tokens, x_tokens, topk_idx, topk_w, dest, expert_weights, act):
+def token_outputs(tokens, x_tokens, topk_idx, topk_w, dest, expert_weights, act,
+                  shared_weights=None):
     """Outputs of selected tokens only, expert by expert.
 
     For layers too large to run whole on the CPU: every kept pair (t,k) of a
     selected token runs its expert's FFN on the single row x[t]; the rows are
     independent, so this equals the corresponding rows of the full layer.
-    x_tokens[i] is the hidden state of token tokens[i].
+    x_tokens[i] is the hidden state of token tokens[i].  shared_weights
+    (Residual-MoE): each token's sum starts from the shared MLP's output on
+    its row, as in combine.
     Returns (y_rows dict (t,k) -> y [d], out [len(tokens), d]).
     """
     tokens = [int(t) for t in tokens]
@@ -673,6 +676,8 @@ def token_outputs(tokens, x_tokens, topk_idx, topk_w, dest, expert_weights, act)
     d = len(next(iter(xs.values())))
     w = np.asarray(topk_w, dtype=np.float32).astype(np.float64)
     out = np.zeros((len(tokens), d), dtype=np.float64)
+    if shared_weights is not None:
+        out += shared_expert(np.stack([xs[t] for t in tokens]), *shared_weights, act)
     for i, t in enumerate(tokens):
         for k in range(topk_idx.shape[1]):
             if dest[t, k] >= 0:

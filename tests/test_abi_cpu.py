@@ -275,3 +275,23 @@ def test_rows_permute_rejects_bad_arguments(lib):
     assert f(FAKE, ctypes.c_void_p(8192), FAKE, FAKE, 4, 24, 0, NUL) == 1   # row bytes
     assert f(FAKE, FAKE, FAKE, FAKE, 4, 64, 0, NUL) == 1                   # src == dst
     assert f(FAKE, ctypes.c_void_p(8192), FAKE, FAKE, -1, 64, 0, NUL) == 1
+
+
+def test_combine_entry_points_reject_bad_arguments(lib):
+    def comb(fn, **kw):
+        a = dict(y=FAKE, dtype=1, N=16, d=64, K=2, dest=FAKE, w=FAKE, shared=FAKE, out=FAKE)
+        a.update(kw)
+        if fn == "plain":
+            return lib.moe_combine(a["y"], a["dtype"], a["N"], a["d"], a["K"], a["dest"],
+                                   a["w"], a["out"], NUL)
+        return lib.moe_combine_residual(a["y"], a["dtype"], a["N"], a["d"], a["K"], a["dest"],
+                                        a["w"], a["shared"], a["out"], NUL)
+    for fn in ("plain", "residual"):
+        assert comb(fn, out=NUL) == 1
+        assert comb(fn, dtype=3) == 2
+        assert comb(fn, N=0) == 1
+        assert comb(fn, d=4) == 1                   # 8 bytes: not a multiple of 16
+        assert comb(fn, K=0) == 1
+        assert comb(fn, K=17) == 2
+    assert comb("residual", shared=NUL) == 1
+    assert "moe_combine_residual" in lib.moe_last_error().decode()

@@ -118,3 +118,19 @@ def test_residual_combine_rounds_once_and_adds_shared_unweighted():
     # token 1: its kept row is zero and its other pair dropped: the shared
     # output, not scaled by any gate weight
     assert out[1, 0] == 3.0
+
+
+def test_sampled_token_outputs_equal_full_residual_layer_rows():
+    rng = np.random.default_rng(12)
+    N, E, K, W, d, ffn, ffn_s = 20, 4, 1, 2, 8, 8, 16
+    logits = rng.standard_normal((N, E)).astype(np.float32)
+    x = O.round_bf16(rng.standard_normal((N, d)))
+    wg, wu, wd = (O.round_bf16(a) for a in _rand_weights(rng, E, d, ffn))
+    sh = tuple(O.round_bf16(a[0]) for a in _rand_weights(rng, 1, d, ffn_s))
+    for cap in (-1, 3):
+        res = O.layer(logits, x, lambda e: (wg[e], wu[e], wd[e]), K, W, cap, "bf16",
+                      shared_weights=sh)
+        toks = [0, 5, 6, 19]
+        _, out = O.token_outputs(toks, x[toks], res["topk_idx"], res["topk_w"], res["dest"],
+                                 lambda e: (wg[e], wu[e], wd[e]), "bf16", shared_weights=sh)
+        assert np.array_equal(out, res["out"][toks])
