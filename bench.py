@@ -201,8 +201,10 @@ def main():
     ms_per_step = elapsed * 1e3 / args.steps
 
     names = ["route", "dispatch", "ffn", "combine"]
-    st = {n: float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(args.steps)]))
-          for j, n in enumerate(names)}
+    per_step = {n: [evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(args.steps)]
+                for j, n in enumerate(names)}
+    per_step["step"] = [evs[i][0].elapsed_time(evs[i][4]) for i in range(args.steps)]
+    st = {n: float(np.mean(per_step[n])) for n in names}
     disp_b, comb_b = algorithmic_bytes(cfg, M, b)
     flops = ffn_flops(cfg, M)
     achieved_tflops = flops / (st["ffn"] * 1e-3) / 1e12
@@ -260,6 +262,10 @@ def main():
         ("ffn_plain_weights_ms" if weights == "packed" else "ffn_packed_weights_ms"):
             other_ffn_ms,
         "tokens_per_s": {n: N / (st[n] * 1e-3) for n in names},
+        # event-timed spread over the timed steps (the means above; `value`
+        # is the host clock around all of them)
+        "median_ms": {n: float(np.median(v)) for n, v in per_step.items()},
+        "min_ms": {n: float(np.min(v)) for n, v in per_step.items()},
     }
     if cold:
         stages.update({
