@@ -151,3 +151,39 @@ def test_full_size_residual_top1_layer_matches_oracle():
     _close("y_shared", _np(layer.y_shared[torch.tensor(toks, device=DEV)]),
            O.shared_expert(xs, *sh_np, "bf16"), "bf16")
     _close("out", _np(layer.out[torch.tensor(toks, device=DEV)]), out_ref, "bf16")
+
+
+@pytest.mark.parametrize("case", [
+    dict(N=1, d=64, ffn=64, E=4, K=2, W=2, cap=-1),      # one token
+    dict(N=40, d=128, ffn=64, E=1, K=1, W=1, cap=-1),    # one expert: weight 1
+    dict(N=64, d=64, ffn=128, E=8, K=3, W=4, cap=0),     # every pair dropped
+])
+def test_residual_layer_edge_cases(case):
+    cfg = synth.config("res_edge", act="bf16", C=None,
+                       **{k: v for k, v in case.items() if k != "cap"})
+    cap = case["cap"]
+    print(f"[residual] edge {case}", flush=True)
+    inp = synth.make_inputs(cfg, DEV)
+    sh = synth.make_shared_weights(cfg, DEV, 192)
+    wts = _weights_np(inp)
+    sh_np = tuple(_np(a[0]) for a in sh)
+    ref = O.layer(_np(inp["logits"]), _np(inp["x"]), lambda e: wts[e], cfg["K"], cfg["W"], cap,
+                  "bf16", shared_weights=sh_np)
+    layer = B.MoeLayer(cfg["N"], cfg["d"], cfg["ffn"], cfg["E"], cfg["K"], cfg["W"], cap,
+                       torch.bfloat16, DEV, shared_ffn=192)
+    out = layer.forward(inp["logits"], inp["x"], inp["w_gate"], inp["w_up"], inp["w_down"],
+                        shared=B.moe_pack_ffn_weights(*sh))
+    torch.cuda.synchronize()
+    assert np.array_equal(_np(layer.disp["dest"]), ref["dest"])
+    _close("y_shared", _np(layer.y_shared), ref["y_shared"], "bf16")
+    _close("out", _np(out), ref["out"], "bf16")
+    if cap == 0:
+        assert torch.equal(out, layer.y_shared)     # nothing kept: the shared rows, bitwise
+
+
+def test_shared_ffn_rejects_more_than_one_expert():
+    cfg = synth.config("res_reject", N=8, d=64, ffn=64, E=2, K=1, W=1, act="bf16", C=None)
+    inp = synth.make_inputs(cfg, DEV)
+    offsets = torch.tensor([0, 8], dtype=torch.int32, device=DEV)
+    with pytest.raises(ValueError):
+        B.moe_shared_ffn(inp["x"], offsets, inp["w_gate"], inp["w_up"], inp["w_down"])
