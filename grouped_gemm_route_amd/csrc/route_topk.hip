@@ -22,8 +22,9 @@
 // experts holding that maximum, and a group minimum over those names gives
 // the lowest expert index with the maximum logit.  That is the order (a > b)
 // or (a == b and lower index), a total order on (logit, index) pairs.  Lane
-// k of the group keeps round k's result, and lanes 0 .. K - 1 store the
-// token's K results together (K <= 16 <= L whenever E > 8).
+// k of the group keeps round k's winner and logit; after the K rounds lanes
+// 0 .. K - 1 compute their gate weights together and store the token's K
+// results (K <= 16 <= L whenever E > 8).
 #include "moe_internal.h"
 
 #include <math.h>
@@ -101,9 +102,8 @@ __global__ __launch_bounds__(256) void route_topk_kernel(
     s = group_reduce<L, false>(s);
   }
 
-  float wsum = 0.0f;
   int my_idx = 0;
-  float my_w = 0.0f;
+  float my_logit = -INFINITY;
   for (int k = 0; k < K; ++k) {
     float lb = v[0];
 #pragma unroll
@@ -115,19 +115,22 @@ __global__ __launch_bounds__(256) void route_topk_kernel(
     for (int i = VPL - 1; i >= 0; --i)
       if (v[i] == bv) le = j + i * L;
     const int bi = group_min<L>(le);
-    const float p = kSigmoid ? 1.0f / (1.0f + expf(-bv)) : expf(bv - m) / s;
-    wsum += p;
 #pragma unroll
     for (int i = 0; i < VPL; ++i)
       if (j + i * L == bi) v[i] = -INFINITY;  // taken: never wins again
     if (j == k) {
       my_idx = bi;
-      my_w = p;
+      my_logit = bv;
     }
   }
+  // the K gate weights at once, lane k holding slot k's (renormalised: over
+  // the sum of the K weights, a group sum)
+  float w = 0.0f;
+  if (j < K) w = kSigmoid ? 1.0f / (1.0f + expf(-my_logit)) : expf(my_logit - m) / s;
+  if (renormalize) w = w / group_reduce<L, false>(w);
   if (valid && j < K) {
     topk_idx[(size_t)tok * K + j] = my_idx;
-    topk_w[(size_t)tok * K + j] = renormalize ? my_w / wsum : my_w;
+    topk_w[(size_t)tok * K + j] = w;
   }
 }
 
