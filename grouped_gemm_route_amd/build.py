@@ -23,7 +23,7 @@ ARCH = "gfx950"
 # Packed fp32 ops are disabled for device code (a hipcc device-side feature;
 # the host pass prints a harmless "not a recognized feature" warning).
 HIPFLAGS = [
-    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Werror",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", INCLUDE, "-I", CSRC,
 ]

@@ -26,6 +26,20 @@ constexpr int kF32TileRows = 64;
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
+// Sigmoid gate score of logit l as a ratio to the score of a logit l0 >= l,
+// s(l) / s(l0) with s(z) = 1 / (1 + exp(-z)), in a form where no exponential
+// overflows and the ratio does not vanish with the scores themselves (all
+// chosen logits far below zero round every plain fp32 score to 0):
+//   l0 < 0:  exp(l - l0) (1 + exp(l0)) / (1 + exp(l))
+//   l0 >= 0: (1 + exp(-l0)) / (1 + exp(-l))
+// The ratio for l = l0 is exactly 1, so a sum of ratios that includes l0's is
+// at least 1.  Used for renormalised sigmoid weights, which are these ratios
+// divided by their sum over the K chosen experts.
+__device__ __forceinline__ float sigmoid_ratio(float l, float l0) {
+  return l0 < 0.0f ? expf(l - l0) * (1.0f + expf(l0)) / (1.0f + expf(l))
+                   : (1.0f + expf(-l0)) / (1.0f + expf(-l));
+}
+
 // ---- launchers (each returns the hipError_t of its launches) -------------
 
 hipError_t launch_route_topk(const float* logits, int N, int E, int K, bool sigmoid,

@@ -110,7 +110,7 @@ __global__ __launch_bounds__(kTokWaves * kWave) void reroute_candidates_kernel(
     v[i] = e < E ? row[e] : -INFINITY;
   }
   float m = 0.0f, s = 1.0f;
-  if (!kSigmoid) {  // softmax denominator, as the route kernel forms it
+  if (!kSigmoid) {  // softmax maximum and denominator over all E logits
     m = v[0];
 #pragma unroll
     for (int i = 1; i < VPL; ++i) m = fmaxf(m, v[i]);
@@ -122,7 +122,16 @@ __global__ __launch_bounds__(kTokWaves * kWave) void reroute_candidates_kernel(
 #pragma unroll
     for (int off = kWave / 2; off >= 1; off >>= 1) s += __shfl_xor(s, off);
   }
-  auto score = [&](float l) { return kSigmoid ? 1.0f / (1.0f + expf(-l)) : expf(l - m) / s; };
+  // Renormalised sigmoid scores are taken as ratios to the score of slot 0's
+  // logit (sigmoid_ratio: finite and not all zero however negative the
+  // logits), which the division by their sum cancels.  Weights follow the
+  // routing kernel's formulas; its sums run in another order, so they agree
+  // with its weights to within fp32 rounding.
+  const float l0 = __shfl(my_l, 0);
+  auto score = [&](float l) {
+    if (kSigmoid && renormalize) return sigmoid_ratio(l, l0);
+    return kSigmoid ? 1.0f / (1.0f + expf(-l)) : expf(l - m) / s;
+  };
   float norm = 1.0f;
   if (renormalize) {  // sum of the original K scores, slot order
     const float mine = lane < K ? score(my_l) : 0.0f;

@@ -126,8 +126,15 @@ __global__ __launch_bounds__(256) void route_topk_kernel(
   // the K gate weights at once, lane k holding slot k's (renormalised: over
   // the sum of the K weights, a group sum)
   float w = 0.0f;
-  if (j < K) w = kSigmoid ? 1.0f / (1.0f + expf(-my_logit)) : expf(my_logit - m) / s;
-  if (renormalize) w = w / group_reduce<L, false>(w);
+  if (kSigmoid && renormalize) {
+    // ratios to slot 0's score (sigmoid_ratio), whose sum is at least 1
+    const float l0 = group_reduce<L, true>(my_logit);  // lanes >= K hold -inf
+    if (j < K) w = sigmoid_ratio(my_logit, l0);
+    w = w / group_reduce<L, false>(w);
+  } else {
+    if (j < K) w = kSigmoid ? 1.0f / (1.0f + expf(-my_logit)) : expf(my_logit - m) / s;
+    if (renormalize) w = w / group_reduce<L, false>(w);
+  }
   if (valid && j < K) {
     topk_idx[(size_t)tok * K + j] = my_idx;
     topk_w[(size_t)tok * K + j] = w;

@@ -130,8 +130,9 @@ size_t moe_reroute_workspace_bytes(int32_t N, int32_t E, int32_t K);
  *   3. candidates are admitted in (token, slot) order while their expert
  *      has room left by step 1 (capacity minus its surviving slots);
  *   4. an admitted slot gets the new expert in topk_idx and its gate score
- *      (as moe_route_topk_gated computes it, including renormalize's
- *      divisor of the token's original K scores) in topk_w.
+ *      in topk_w: moe_route_topk_gated's formula for that expert (with
+ *      renormalize, divided by the sum of the token's original K scores),
+ *      equal to a routing call's weight to within fp32 rounding.
  * Other slots are left unchanged; moe_dispatch with the same capacity then
  * keeps the step-1 survivors plus every admitted slot and drops the rest.
  *   logits       [N, E] fp32, the routing input (finite).

@@ -43,8 +43,15 @@ def test_exchange_matches_oracle(name):
     plan = B.moe_exchange_plan(idx, disp, E, W)
     torch.cuda.synchronize()
 
-    ex = O.exchange(_np(idx), _np(disp["dest"]), E, W)
-    M = int(_np(disp["offsets"])[-1])
+    # the oracle's own route and dispatch feed its exchange plan; the GPU's
+    # routing and dispatch must equal them first
+    ri, _ = O.route(_np(inp["logits"]), K)
+    rd = O.dispatch(ri, E, W, cap)
+    assert np.array_equal(_np(idx), ri)
+    assert np.array_equal(_np(disp["dest"]), rd["dest"])
+    ex = O.exchange(ri, rd["dest"], E, W)
+    M = int(rd["offsets"][-1])
+    assert int(_np(disp["offsets"])[-1]) == M
     assert np.array_equal(_np(plan["src_counts"]), ex["C"])
     assert np.array_equal(_np(plan["traffic"]), ex["D"])
     assert np.array_equal(_np(plan["send_row"]), ex["send_row"])

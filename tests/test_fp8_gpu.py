@@ -208,13 +208,10 @@ def test_fp8_full_size_dense_layer():
     rows = np.unique(dest[dest >= 0])
     yq, ys = O.quantize_fp8(_np(layer.y_perm[torch.from_numpy(rows).to(DEV)]))
     assert np.array_equal(_np(layer.y8[torch.from_numpy(rows).to(DEV)]), yq)
+    # the oracle's combine over the sampled tokens' rows: their fp8 values
+    # renumbered 0 .. len(rows) - 1, dest remapped to match
     lut = {int(r): j for j, r in enumerate(rows)}
-    yv = O.dequantize_fp8(yq, ys).astype(np.float64)
-    w = _np(layer.topk_w)[toks].astype(np.float64)
-    ref = np.zeros((len(toks), cfg["d"]))
-    for i in range(len(toks)):
-        for k in range(cfg["K"]):
-            if dest[i, k] >= 0:
-                ref[i] += w[i, k] * yv[lut[int(dest[i, k])]]
-    ref = O.round_storage(ref, "bf16")
+    dest_s = np.vectorize(lambda r: lut[int(r)] if r >= 0 else -1)(dest).astype(np.int32)
+    ref = O.combine(O.dequantize_fp8(yq, ys).astype(np.float64), dest_s,
+                    _np(layer.topk_w)[toks], "bf16")
     _close("out", _np(layer.out[torch.from_numpy(toks).to(DEV)]), ref)

@@ -125,3 +125,14 @@ def test_reroute_layer_matches_oracle():
     got = layer.out.float().cpu().numpy().astype(np.float64)
     err = np.abs(got - ref["out"])
     assert (err <= 2e-2 + 1e-2 * np.abs(ref["out"])).all(), err.max()
+
+
+def test_reroute_sigmoid_renormalised_far_negative_logits():
+    # renormalised sigmoid weights of re-routed slots stay finite when every
+    # logit is far below zero (plain fp32 scores all round to 0 there)
+    N, E, K, cap = 300, 16, 2, 60
+    g = torch.Generator().manual_seed(11)
+    l = -110.0 - 20.0 * torch.rand(N, E, generator=g)
+    l[:, 0] += 5.0                   # a hot expert that overflows
+    ni, nrr, _ = _check_reroute(l, K, cap, "sigmoid", True)
+    assert nrr.sum() > 0
