@@ -37,6 +37,8 @@ SIGNATURES = [
     ("moe_dispatch_workspace_bytes", _SZ, [_I32, _I32, _I32]),
     ("moe_dispatch", ctypes.c_int,
      [_P, _I32, _I32, _I32, _P, _I32, _I32, _I32, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    ("moe_dispatch_noalloc", ctypes.c_int,
+     [_P, _I32, _I32, _I32, _P, _I32, _I32, _I32, _I64, _P, _P, _P, _P, _P, _P, _P, _P]),
     ("moe_grouped_ffn_workspace_bytes", _SZ, [_I64, _I32, _I32]),
     ("moe_grouped_ffn", ctypes.c_int,
      [_P, _I32, _I32, _I32, _I32, _P, _I64, _P, _P, _P, _P, _P, _P, _SZ, _P]),
@@ -273,6 +275,34 @@ def moe_dispatch(x, topk_idx, E, W, capacity, out=None):
         _ptr(out["demand"]), _ptr(out["counts"]), _ptr(out["offsets"]),
         _ptr(out["rank_offsets"]), _ptr(ws), ws.numel() * ws.element_size(),
         _stream(x)))
+    return out
+
+
+def moe_dispatch_noalloc(x, topk_idx, E, W, capacity, out=None):
+    """moe_dispatch through the allocation-free entry point (the library's
+    own fixed scratch instead of a workspace); returns the dict of outputs
+    (a "workspace" entry, if present, is not used)."""
+    _need(x, "x")
+    code = _act_code(x, "x")
+    N, d = x.shape
+    dev = x.device
+    _need(topk_idx, "topk_idx", torch.int32, dev)
+    K = topk_idx.shape[1]
+    if topk_idx.shape[0] != N:
+        raise ValueError("topk_idx must be [N, K]")
+    if out is None:
+        out = alloc_dispatch_outputs(N, d, E, K, W, x.dtype, dev)
+    sizes = {"x_perm": N * K * d, "perm_token": N * K, "dest": N * K, "demand": E,
+             "counts": E, "offsets": E + 1, "rank_offsets": W + 1}
+    for k in DISPATCH_OUTPUTS:
+        _need(out[k], k, x.dtype if k == "x_perm" else torch.int32, dev)
+        if out[k].numel() < sizes[k]:
+            raise ValueError(f"{k} must hold at least {sizes[k]} elements")
+    _check("moe_dispatch_noalloc", load_library().moe_dispatch_noalloc(
+        _ptr(x), code, N, d, _ptr(topk_idx), E, K, W, int(capacity),
+        _ptr(out["x_perm"]), _ptr(out["perm_token"]), _ptr(out["dest"]),
+        _ptr(out["demand"]), _ptr(out["counts"]), _ptr(out["offsets"]),
+        _ptr(out["rank_offsets"]), _stream(x)))
     return out
 
 

@@ -7,6 +7,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 namespace {
@@ -214,6 +215,79 @@ int moe_dispatch(const void* x, int32_t dtype, int32_t N, int32_t d,
                            x_perm, nullptr, perm_token, dest, demand, counts, offsets,
                            rank_offsets, ws, as_stream(stream)),
       "moe_dispatch");
+}
+
+}  // extern "C"
+
+namespace {
+
+// Scratch of moe_dispatch_noalloc: a fixed array in device memory, one copy
+// per GPU (each device that loads the library holds its own, until the
+// process ends), zero when the library is loaded.  In host code its name is
+// a host-side stand-in, never a device address: the device address comes
+// from hipGetSymbolAddress, looked up once per device with that device
+// current, and only that address is handed to kernels.
+__device__ __align__(256) unsigned char scratch[MOE_DISPATCH_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices] = {};
+
+// Device address of the current device's scratch (looked up on first use).
+int scratch_address(const char* fn, void** out) {
+  int dev = -1;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return hip_status(err, fn);
+  if (dev < 0 || dev >= kMaxScratchDevices)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: device %d beyond the %d this call supports", fn, dev,
+                kMaxScratchDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (err != hipSuccess) return hip_status(err, fn);
+    if (p == nullptr) return fail(MOE_ERR_HIP, "%s: no device address for the scratch", fn);
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_dispatch_noalloc(const void* x, int32_t dtype, int32_t N, int32_t d,
+                         const int32_t* topk_idx, int32_t E, int32_t K, int32_t W,
+                         int64_t capacity, void* x_perm, int32_t* perm_token, int32_t* dest,
+                         int32_t* demand, int32_t* counts, int32_t* offsets,
+                         int32_t* rank_offsets, void* stream) {
+  static const char* fn = "moe_dispatch_noalloc";
+  const int es = elem_size(dtype);
+  if (x && es == 0) return fail(MOE_ERR_UNSUPPORTED, "%s: dtype %d", fn, dtype);
+  // the usual checks, with the scratch standing in for the workspace (a
+  // non-null placeholder: the size is checked just below)
+  const size_t need = (N >= 1 && E >= 1 && K >= 1) ? moe::dispatch_workspace_bytes(N, E, K) : 0;
+  int st = dispatch_checks(fn, x, es ? es : 1, N, d, topk_idx, E, K, W, capacity, x_perm,
+                           perm_token, dest, demand, counts, offsets, rank_offsets,
+                           reinterpret_cast<const void*>(1), need);
+  if (st != MOE_OK) return st;
+  if (need > (size_t)MOE_DISPATCH_NOALLOC_SCRATCH_BYTES)
+    return fail(MOE_ERR_UNSUPPORTED,
+                "%s: these sizes need %zu bytes of scratch, above the %zu this call holds "
+                "(N=%d E=%d K=%d); use moe_dispatch with a workspace",
+                fn, need, (size_t)MOE_DISPATCH_NOALLOC_SCRATCH_BYTES, N, E, K);
+  void* ws_ptr = nullptr;
+  st = scratch_address(fn, &ws_ptr);
+  if (st != MOE_OK) return st;
+  // Nothing in the scratch needs to start at zero: the rank kernel writes
+  // every per-block count and local rank, the scan every exclusive base.
+  const moe::DispatchWorkspace ws = moe::dispatch_workspace(ws_ptr, N, E, K);
+  return hip_status(
+      moe::launch_dispatch(x, (size_t)d * es, N, topk_idx, E, K, W, capacity, x_perm, nullptr,
+                           perm_token, dest, demand, counts, offsets, rank_offsets, ws,
+                           as_stream(stream)),
+      fn);
 }
 
 int moe_dispatch_fp8(const void* x, int32_t N, int32_t d, const int32_t* topk_idx, int32_t E,

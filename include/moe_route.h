@@ -211,6 +211,29 @@ int moe_dispatch(const void* x, int32_t dtype, int32_t N, int32_t d,
                  int32_t* offsets, int32_t* rank_offsets, void* workspace,
                  size_t workspace_bytes, void* stream);
 
+/*
+ * moe_dispatch for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops and harnesses that forbid
+ * hipMalloc.  Same operation, arguments, checks and results as moe_dispatch,
+ * without the workspace arguments: its scratch is a fixed array of
+ * MOE_DISPATCH_NOALLOC_SCRATCH_BYTES bytes in the library's device memory,
+ * one per GPU, held from the first call on that GPU until the process ends.
+ * The call allocates nothing (its first call on a GPU looks the array's
+ * address up once).  Every call on one GPU shares that GPU's array and
+ * leaves its contents behind; nothing in it needs to start at zero.  Calls
+ * that may overlap on one GPU (different streams or host threads without
+ * ordering) race on the array.
+ * Checks: as moe_dispatch; sizes whose moe_dispatch_workspace_bytes(N, E, K)
+ *         exceed MOE_DISPATCH_NOALLOC_SCRATCH_BYTES (UNSUPPORTED); a device
+ *         ordinal of 64 or more (UNSUPPORTED).
+ */
+#define MOE_DISPATCH_NOALLOC_SCRATCH_BYTES (4u << 20)
+int moe_dispatch_noalloc(const void* x, int32_t dtype, int32_t N, int32_t d,
+                         const int32_t* topk_idx, int32_t E, int32_t K, int32_t W,
+                         int64_t capacity, void* x_perm, int32_t* perm_token, int32_t* dest,
+                         int32_t* demand, int32_t* counts, int32_t* offsets,
+                         int32_t* rank_offsets, void* stream);
+
 /* Bytes of device workspace moe_grouped_ffn needs for these sizes. */
 size_t moe_grouped_ffn_workspace_bytes(int64_t max_rows, int32_t E,
                                        int32_t dtype);

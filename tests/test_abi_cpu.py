@@ -295,3 +295,28 @@ def test_combine_entry_points_reject_bad_arguments(lib):
         assert comb(fn, K=17) == 2
     assert comb("residual", shared=NUL) == 1
     assert "moe_combine_residual" in lib.moe_last_error().decode()
+
+
+def test_dispatch_noalloc_rejects_on_the_host(lib):
+    # every rejection happens before the scratch's device address is looked
+    # up, so no GPU is needed
+    f = lib.moe_dispatch_noalloc
+    ok = dict(x=FAKE, dt=1, N=64, d=64, idx=FAKE, E=8, K=2, W=2, cap=-1)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(a["x"], a["dt"], a["N"], a["d"], a["idx"], a["E"], a["K"], a["W"], a["cap"],
+                 FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, NUL)
+    assert call(x=NUL) == 1
+    assert call(N=0) == 1
+    assert call(W=3) == 1
+    assert call(cap=-2) == 1
+    assert call(dt=7) == 2
+    assert call(E=2048, K=2) == 2
+    # scratch: moe_dispatch_workspace_bytes above the fixed 4 MiB array
+    limit = 4 << 20
+    assert lib.moe_dispatch_workspace_bytes(300000, 8, 4) > limit
+    assert call(N=300000, E=8, K=4) == 2
+    assert "scratch" in lib.moe_last_error().decode()
+    # the largest bench workload fits
+    assert lib.moe_dispatch_workspace_bytes(32768, 256, 8) <= limit
