@@ -496,8 +496,8 @@ int moe_router_logits(const void* x, int32_t dtype, int32_t N, int32_t d,
     return fail(MOE_ERR_INVALID_ARG, "moe_router_logits: need N, d, E >= 1");
   if (E > MOE_MAX_EXPERTS)
     return fail(MOE_ERR_UNSUPPORTED, "moe_router_logits: E <= %d supported", MOE_MAX_EXPERTS);
-  if (dtype == MOE_DTYPE_BF16 && d % 64 != 0)
-    return fail(MOE_ERR_UNSUPPORTED, "moe_router_logits: bf16 needs d a multiple of 64 (d=%d)", d);
+  if (d % 8 != 0)
+    return fail(MOE_ERR_INVALID_ARG, "moe_router_logits: d must be a multiple of 8 (d=%d)", d);
   if ((int64_t)N * E >= ((int64_t)1 << 31) || (int64_t)256 * d * es >= ((int64_t)1 << 31))
     return fail(MOE_ERR_UNSUPPORTED, "moe_router_logits: sizes too large");
   return hip_status(moe::launch_router_logits(x, dtype == MOE_DTYPE_BF16, N, d, w_router, E,

@@ -162,8 +162,8 @@ int moe_reroute_overflow(const float* logits, int32_t N, int32_t E, int32_t K, i
  * logits agree with an exact sum to within the fp32 summation bound and
  * near-ties may order differently.
  *   x          [N, d] of dtype; w_router [E, d] of dtype; logits [N, E] fp32 out.
- * Checks: pointers non-null; N, d, E >= 1 (INVALID_ARG); dtype; E <=
- *         MOE_MAX_EXPERTS; bf16 needs d a multiple of 64; N*E < 2^31
+ * Checks: pointers non-null; N, d, E >= 1; d a multiple of 8
+ *         (INVALID_ARG); dtype; E <= MOE_MAX_EXPERTS; N*E < 2^31
  *         (UNSUPPORTED).
  */
 int moe_router_logits(const void* x, int32_t dtype, int32_t N, int32_t d,

@@ -320,3 +320,12 @@ def test_dispatch_noalloc_rejects_on_the_host(lib):
     assert "scratch" in lib.moe_last_error().decode()
     # the largest bench workload fits
     assert lib.moe_dispatch_workspace_bytes(32768, 256, 8) <= limit
+
+
+def test_router_rejects_bad_arguments(lib):
+    f = lib.moe_router_logits
+    assert f(NUL, 1, 4, 64, FAKE, 8, FAKE, NUL) == 1
+    assert f(FAKE, 1, 0, 64, FAKE, 8, FAKE, NUL) == 1
+    assert f(FAKE, 1, 4, 60, FAKE, 8, FAKE, NUL) == 1          # d not a multiple of 8
+    assert f(FAKE, 9, 4, 64, FAKE, 8, FAKE, NUL) == 2          # dtype
+    assert f(FAKE, 1, 4, 64, FAKE, 1025, FAKE, NUL) == 2       # E limit

@@ -7,8 +7,11 @@ those paths, fully and partly filled, for bf16 and fp32 rows and for the fp8
 payload.  Two expert counts cover both ways of finding the expert offsets:
 each scatter block scanning the small per-block count table itself (8
 experts), and the one-block scan kernel (128 experts over 9 blocks of
-tokens: a table of 1152 counts).  Everything compared is an integer or a
-bit copy, so it must match exactly.
+tokens: a table of 1152 counts).  Further cases take both paths at their
+edges (one block of tokens, whole blocks and a ragged last one, one expert,
+the largest expert count, the largest table the scatter scans itself) and
+repeat each call three times on one workspace.  Everything compared is an
+integer or a bit copy, so it must match exactly.
 """
 import numpy as np
 import pytest
@@ -103,3 +106,34 @@ def test_dispatch_fp8_row_widths_match_oracle(d):
     pt = ref["perm_token"].astype(np.int64)
     assert np.array_equal(_np(out["x8"])[:M], tq[pt])
     assert np.array_equal(_np(out["x_scale"])[:M], ts[pt])
+
+
+# (N, E, K, W, C): the two paths at their edges (the scatter scans the
+# per-block count table itself while it holds at most 1024 counts)
+EDGE_ROUTINGS = [
+    (4096, 8, 2, 8, None),     # 16 x 8 counts
+    (4097, 8, 2, 8, None),     # a ragged last block of one token
+    (6000, 4, 2, 2, 1.1),      # with a capacity
+    (256, 16, 4, 4, None),     # one whole block
+    (16384, 64, 8, 8, 0.9),    # 64 x 64 counts: the scan kernel
+    (9000, 1, 1, 1, None),     # one expert
+    (32768, 32, 4, 8, None),   # 128 x 32 = 4096 counts: the scan kernel
+    (700, 1024, 16, 8, None),  # the largest expert count
+]
+
+
+@pytest.mark.parametrize("N,E,K,W,C", EDGE_ROUTINGS)
+def test_dispatch_paths_match_oracle(N, E, K, W, C):
+    cfg = synth.config(f"edge_{N}_{E}_{K}", N=N, d=64, ffn=64, E=E, K=K, W=W, act="bf16", C=C)
+    print(f"[dispatch] edge N={N} E={E} K={K} W={W} C={C}", flush=True)
+    cap = O.capacity(C, N, K, E) if C is not None else -1
+    inp = synth.make_inputs(cfg, DEV, weights=False)
+    idx, _ = B.moe_route_topk(inp["logits"], K)
+    ref = _dispatch_reference(cfg, inp, idx, cap)
+    out = None
+    for _ in range(3):            # one workspace, three calls in a row
+        out = B.moe_dispatch(inp["x"], idx, E, W, cap, out)
+        torch.cuda.synchronize()
+        M = _check_indices(out, ref)
+        perm = torch.from_numpy(ref["perm_token"].astype(np.int64)).to(DEV)
+        assert torch.equal(out["x_perm"][:M], inp["x"][perm])

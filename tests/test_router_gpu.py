@@ -23,6 +23,20 @@ CASES = {
                                 act="bf16"), None),
     "e1024": (synth.config("rt_e1024", N=97, d=128, ffn=64, E=1024, K=16, W=8, act="bf16"),
               None),
+    # the skinny kernel (up to 64 experts per block): every expert-tile count,
+    # token counts off the 16-token block, and d a multiple of 8 but not of
+    # 64 or 32 (the last step of a row is partly past its end), also with
+    # more than 64 experts (two expert groups)
+    "skinny_e3_d200": (synth.config("rt_sk1", N=45, d=200, ffn=64, E=3, K=2, W=1, act="bf16"),
+                       None),
+    "skinny_e20_d72": (synth.config("rt_sk2", N=130, d=72, ffn=64, E=20, K=4, W=4, act="bf16"),
+                       None),
+    "skinny_e64_d1000": (synth.config("rt_sk4", N=77, d=1000, ffn=64, E=64, K=8, W=8,
+                                      act="bf16"), None),
+    "skinny_e70_d200": (synth.config("rt_sk70", N=50, d=200, ffn=64, E=70, K=6, W=2,
+                                     act="bf16"), None),
+    "skinny_e8_d8": (synth.config("rt_sk_d8", N=33, d=8, ffn=64, E=8, K=2, W=2, act="bf16"),
+                     None),
 }
 
 
