@@ -63,6 +63,9 @@ def parse():
                    help="skip the virtual multi-source exchange measurements")
     p.add_argument("--no-residual", action="store_true",
                    help="skip the Residual-MoE (top-1 + shared MLP) measurements")
+    p.add_argument("--no-per-rank", action="store_true",
+                   help="skip the per-virtual-rank FFN timing (it launches the same GEMM "
+                        "kernels on one rank's rows, which would mix into a profile's averages)")
     p.add_argument("--plain-weights", action="store_true",
                    help="time the FFN on row-major weights (moe_grouped_ffn) instead of "
                         "packed ones")
@@ -312,6 +315,9 @@ def main():
     }
 
     result["metrics"] = routing_metrics(layer, cfg, cap, M)
+    if weights == "packed" and not args.no_per_rank:
+        result["metrics"]["per_rank_ffn"] = per_rank_ffn_block(B, layer, ffn_args[0], cfg,
+                                                               stream)
     if not args.no_exchange:
         result["exchange"] = exchange_block(B, layer, inp["x"], cfg, M, b, stream)
         result["router_projection"] = router_block(B, synth, inp["x"], cfg, b, stream)
@@ -341,8 +347,14 @@ def routing_metrics(layer, cfg, cap, M):
     demand = layer.disp["demand"].cpu().numpy().astype(np.int64)
     counts = layer.disp["counts"].cpu().numpy().astype(np.int64)
     per_rank = counts.reshape(W, E // W).sum(axis=1)
+    # capacity_factor_effective (section 5.1's dispatcher metric, "C_eff >
+    # 0.8"): kept rows over the expert buffers' slots, M / (E c), c = the
+    # capacity, or for a dropless layer the largest expert's rows (the
+    # capacity a padded exchange would need): mean over largest load
+    c = cap if cap >= 0 else int(counts.max())
     return {
         "kept_rows": M,
+        "capacity_factor_effective": float(M / (E * c)) if c > 0 else 0.0,
         "dropped_pairs": int(N * K - M),
         "drop_rate": float((N * K - M) / (N * K)),
         "experts_overflowing": int((demand > cap).sum()) if cap >= 0 else 0,
@@ -353,6 +365,40 @@ def routing_metrics(layer, cfg, cap, M):
         "rank_load_std_over_mean": float(per_rank.std() / max(per_rank.mean(), 1e-9)),
         "rank_load_max_over_min": float(per_rank.max() / max(per_rank.min(), 1)),
     }
+
+
+def per_rank_ffn_block(B, layer, packed, cfg, stream, reps=5):
+    """Expert compute time per virtual rank ("MoE 专家并行的 All-to-All 通信瓶颈",
+    section "可观测指标与故障定位": each card's expert time, to find the slowest
+    card).  Rank r's experts [r E/W, (r+1) E/W) run as one grouped-FFN call
+    on its own rows of the packed buffer, as they would on its own GPU; the
+    EP step waits for the slowest rank."""
+    import torch
+
+    E, W = cfg["E"], cfg["W"]
+    Ep = E // W
+    offs = layer.disp["offsets"]
+    ro = layer.disp["rank_offsets"].cpu().tolist()
+    up_e = packed.up.numel() // E
+    dn_e = packed.down.numel() // E
+    ms = []
+    for r in range(W):
+        rows = ro[r + 1] - ro[r]
+        if rows == 0:
+            ms.append(0.0)
+            continue
+        sub = B.PackedFfnWeights(packed.up[r * Ep * up_e:(r + 1) * Ep * up_e],
+                                 packed.down[r * Ep * dn_e:(r + 1) * Ep * dn_e], Ep,
+                                 packed.d, packed.ffn)
+        sub_offs = (offs[r * Ep:(r + 1) * Ep + 1] - ro[r]).contiguous()
+        x_sub = layer.disp["x_perm"][ro[r]:ro[r + 1]]
+        h_sub = layer.h[ro[r]:ro[r + 1]]
+        y_sub = layer.y_perm[ro[r]:ro[r + 1]]
+        ms.append(_timed(stream, lambda: B.moe_grouped_ffn_packed(
+            x_sub, sub_offs, sub, rows, h_sub, y_sub, layer.ffn_ws), reps=reps))
+    mean = sum(ms) / len(ms)
+    return {"ms": ms, "slowest_rank": int(max(range(W), key=lambda i: ms[i])),
+            "max_over_mean": float(max(ms) / mean) if mean > 0 else 0.0}
 
 
 def exchange_block(B, layer, src_x, cfg, M, b, stream):
@@ -598,8 +644,13 @@ def router_block(B, synth, x, cfg, b, stream):
             "TFLOPs": 2.0 * N * d * E / (ms * 1e-3) / 1e12}
 
 
-def cpu_baseline(cfg, inp, n_tok):
-    """The oracle, untouched, on the first n_tok tokens of the same workload."""
+def cpu_baseline(cfg, inp, n_tok, runs=3):
+    """The oracle, untouched, on the first n_tok tokens of the same workload,
+    stage by stage: route, dispatch (histogram, capacity, layout and the row
+    copies), the grouped FFN and combine, each timed with perf_counter, the
+    median of `runs` runs.  Routing, dispatch and combine are single-threaded
+    numpy; the FFN's products use the BLAS thread pool."""
+    import numpy as np
     from oracle import moe_oracle as O
 
     n = min(n_tok, cfg["N"])
@@ -622,18 +673,39 @@ def cpu_baseline(cfg, inp, n_tok):
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover - threadpoolctl missing
         threads = 1
-    t0 = time.perf_counter()
-    O.layer(logits, x, fn, cfg["K"], cfg["W"], cap_s, cfg["act"])
-    dt = time.perf_counter() - t0
+    times = {k: [] for k in ("route", "dispatch", "ffn", "combine")}
+    for _ in range(runs):
+        t = time.perf_counter()
+        idx, w = O.route(logits, cfg["K"])
+        times["route"].append(time.perf_counter() - t)
+        t = time.perf_counter()
+        disp = O.dispatch(idx, cfg["E"], cfg["W"], cap_s)
+        x_perm = O.pack(x, disp["perm_token"])
+        times["dispatch"].append(time.perf_counter() - t)
+        t = time.perf_counter()
+        _, y = O.grouped_ffn(x_perm, disp["offsets"], fn, cfg["act"])
+        times["ffn"].append(time.perf_counter() - t)
+        t = time.perf_counter()
+        O.combine(y, disp["dest"], w, cfg["act"])
+        times["combine"].append(time.perf_counter() - t)
+    med = {k: float(np.median(v)) for k, v in times.items()}
+    total = sum(med.values())
+    affinity = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else None
     return {
-        "value": n / dt,
+        "value": n / total,
         "unit": "tokens/s",
         "cores": threads,
         "kind": "oracle",
         "sample": f"first {n} of {cfg['N']} tokens of the same workload (same logits, hidden "
                   f"states and weights; capacity recomputed for {n} tokens), whole oracle "
-                  f"layer in float64 numpy, {dt:.1f} s; BLAS threads {threads}, host cpus "
-                  f"{os.cpu_count()}",
+                  f"layer in float64 numpy stage by stage, median of {runs} runs per stage, "
+                  f"{total:.1f} s per layer; route, dispatch and combine on 1 core, the FFN's "
+                  f"products on {threads} BLAS threads",
+        "stage_s": med,
+        "stage_tokens_per_s": {k: (n / v if v > 0 else None) for k, v in med.items()},
+        "os_cpu_count": os.cpu_count(),
+        "affinity_cpus": affinity,
+        "blas_threads": threads,
     }
 
 

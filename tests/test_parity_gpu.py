@@ -135,6 +135,19 @@ SMALL = {
                                       W=2, act="bf16", C=None),
     "split8_bf16": synth.config("split8_bf16", N=29, d=4096, ffn=512, E=2, K=1, W=2,
                                 act="bf16", C=None),
+    # the same splits at the tile heights of the full-size layers: 128-row
+    # tiles of the packed-weight kernel and 256-row tiles of the row-major one.
+    # One expert of 512 rows: every pass splits (packed gate/up 4 pieces, down
+    # 8; row-major gate/up 4, down 8); two ragged experts (278 and 234 rows):
+    # the down passes split (6 and 5 pieces) with partly empty last tiles; one
+    # expert of 600 rows and ffn 2048: the gate/up passes split (6 and 5) with
+    # an 88-row last tile.
+    "split_full_e1": synth.config("split_full_e1", N=512, d=4096, ffn=4096, E=1, K=1, W=1,
+                                  act="bf16", C=None),
+    "split_full_ragged_e2": synth.config("split_full_ragged_e2", N=512, d=4096, ffn=4096,
+                                         E=2, K=1, W=2, act="bf16", C=None),
+    "split_full_tail": synth.config("split_full_tail", N=600, d=4096, ffn=2048, E=1, K=1, W=1,
+                                    act="bf16", C=None),
 }
 
 
