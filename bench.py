@@ -314,6 +314,7 @@ def main():
         "stages": stages,
     }
 
+    result["graph"] = graph_block(layer, inp, ffn_args, N, stream, args.steps)
     result["metrics"] = routing_metrics(layer, cfg, cap, M)
     if weights == "packed" and not args.no_per_rank:
         result["metrics"]["per_rank_ffn"] = per_rank_ffn_block(B, layer, ffn_args[0], cfg,
@@ -335,6 +336,26 @@ def main():
 
 
 XGMI_EGRESS_GBPS = 7 * 153.0   # MI355X: 7 xGMI links of about 153 GB/s each
+
+
+def graph_block(layer, inp, ffn_args, N, stream, steps):
+    """The same layer step captured once as a HIP graph (MoeLayer.capture)
+    and replayed `steps` times, timed between two synchronisations like the
+    eager steps: the launch costs of the four calls' kernels leave the
+    step, which matters for decode-sized layers."""
+    import torch
+
+    graph = layer.capture(inp["logits"], inp["x"], *ffn_args)
+    for _ in range(3):
+        graph.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        graph.replay()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    del graph
+    return {"steps": steps, "ms_per_step": ms, "tokens_per_s": N / (ms * 1e-3)}
 
 
 def routing_metrics(layer, cfg, cap, M):

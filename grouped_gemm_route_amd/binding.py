@@ -751,6 +751,31 @@ class MoeLayer:
         moe_fp8_quantize_rows(self.y_perm, n_rows, self.max_rows, self.y8, self.y_scale)
         return moe_combine_fp8(self.y8, self.y_scale, self.disp["dest"], self.topk_w, self.out)
 
+    def capture(self, logits, x, w_gate, w_up=None, w_down=None, shared=None, warmup=2):
+        """Record ``forward`` on these buffers as one HIP graph and return it
+        (a torch.cuda.CUDAGraph).  ``graph.replay()`` then enqueues route ->
+        dispatch -> grouped FFN -> combine as one graph launch, reading
+        whatever the buffers hold at replay time: decode-sized layers, whose
+        step is a handful of short kernels, lose the per-call launch costs.
+        Nothing is allocated inside the captured calls (every buffer and
+        workspace belongs to the layer), and no library call records a
+        memset.  The input buffers, weights and the layer must stay alive,
+        at the same addresses, for as long as the graph is replayed.  A few
+        eager calls run first (``warmup``) so that one-time set-up (kernel
+        attributes, device properties) happens outside the capture."""
+        dev = self.topk_idx.device
+        side = torch.cuda.Stream(device=dev)
+        side.wait_stream(torch.cuda.current_stream(dev))
+        with torch.cuda.stream(side):
+            for _ in range(warmup):
+                self.forward(logits, x, w_gate, w_up, w_down, shared)
+        torch.cuda.current_stream(dev).wait_stream(side)
+        torch.cuda.synchronize(dev)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            self.forward(logits, x, w_gate, w_up, w_down, shared)
+        return graph
+
     def forward(self, logits, x, w_gate, w_up=None, w_down=None, shared=None):
         """shared (Residual-MoE layers): the shared MLP's weights as a tuple
         (w_gate, w_up, w_down) of one expert, or PackedFfnWeights of one."""
