@@ -37,6 +37,16 @@ CASES = {
                                      act="bf16"), None),
     "skinny_e8_d8": (synth.config("rt_sk_d8", N=33, d=8, ffn=64, E=8, K=2, W=2, act="bf16"),
                      None),
+    # the tiled kernel: 128 x 256 tiles with the last token block and the
+    # expert tile ragged (E not a multiple of 4: scalar stores), and with two
+    # expert blocks and a single 64-wide stage; 64 x 64 tiles with ragged
+    # tokens and experts
+    "tiled_big_ragged": (synth.config("rt_tb", N=16001, d=192, ffn=64, E=250, K=8, W=2,
+                                      act="bf16"), None),
+    "tiled_big_e260_d64": (synth.config("rt_tb2", N=20000, d=64, ffn=64, E=260, K=4, W=4,
+                                        act="bf16"), None),
+    "tiled_small_ragged": (synth.config("rt_ts", N=2500, d=320, ffn=64, E=130, K=8, W=2,
+                                        act="bf16"), None),
 }
 
 
