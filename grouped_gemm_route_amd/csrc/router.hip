@@ -248,18 +248,18 @@ constexpr int skinny_steps_in_flight() { return NET <= 2 ? 16 : 8; }
 
 template <int NET>
 __global__ __launch_bounds__(kSkWaves * kWave) void router_logits_skinny_kernel(
-    const bf16* __restrict__ x, int N, int d, const bf16* __restrict__ w, int E,
+    const bf16* __restrict__ x, int N, int d, const bf16* __restrict__ w, int E, int epb,
     float* __restrict__ logits) {
   constexpr int kRU = skinny_steps_in_flight<NET>();
   __shared__ f32x4 red[kSkWaves][NET][kWave];
   const int t0 = blockIdx.x * kSkTokens;
-  const int e0 = blockIdx.y * (NET * 16);
+  const int e0 = blockIdx.y * epb;  // epb <= NET * 16 experts per block
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
   const int r = lane & 15;
   const int g = lane >> 4;
   const int nt = min(kSkTokens, N - t0);
-  const int ne = min(NET * 16, E - e0);
+  const int ne = min(epb, E - e0);
   const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(x + (size_t)t0 * d), 0, (uint32_t)((size_t)nt * d * 2), kRBufferFlags);
   const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
@@ -310,7 +310,7 @@ __global__ __launch_bounds__(kSkWaves * kWave) void router_logits_skinny_kernel(
 #pragma unroll
     for (int wv = 0; wv < kSkWaves; ++wv) v += red[wv][j][src][m % 4];
     const int t = t0 + m, e = e0 + j * 16 + n;
-    if (t < N && e < E) logits[(size_t)t * E + e] = v;
+    if (t < N && j * 16 + n < ne) logits[(size_t)t * E + e] = v;
   }
 }
 
@@ -329,9 +329,10 @@ __global__ __launch_bounds__(256) void router_logits_f32_kernel(
 
 template <int NET>
 hipError_t launch_skinny(const bf16* x, int N, int d, const bf16* w, int E, float* logits,
-                         hipStream_t stream) {
-  const dim3 grid((N + kSkTokens - 1) / kSkTokens, (E + NET * 16 - 1) / (NET * 16));
-  router_logits_skinny_kernel<NET><<<grid, kSkWaves * kWave, 0, stream>>>(x, N, d, w, E, logits);
+                         hipStream_t stream, int epb = NET * 16) {
+  const dim3 grid((N + kSkTokens - 1) / kSkTokens, (E + epb - 1) / epb);
+  router_logits_skinny_kernel<NET>
+      <<<grid, kSkWaves * kWave, 0, stream>>>(x, N, d, w, E, epb, logits);
   return hipGetLastError();
 }
 
@@ -390,12 +391,20 @@ hipError_t launch_router_logits(const void* x, bool bf16_data, int N, int d,
       return launch_skinny<4>(xb, N, d, wb, E, logits, stream);
     }
     // more experts: the cheapest of the large tile, the small tile and the
-    // skinny form on 16-expert blocks (few tokens)
+    // skinny form on blocks of 16, 8, 4 or 2 experts (few tokens: x, read
+    // by every block of its token rows, comes from L2 and w_router is spread
+    // over more CUs)
     const int cus = router_cus();
     const int64_t big = router_cost(N, E, 128, 256, cus);
     const int64_t small = router_cost(N, E, 64, 64, cus);
-    const int64_t skinny = router_cost(N, E, kSkTokens, 16, cus);
-    if (skinny < small && skinny < big) return launch_skinny<1>(xb, N, d, wb, E, logits, stream);
+    int epb = 16;
+    int64_t skinny = router_cost(N, E, kSkTokens, 16, cus);
+    for (int c = 8; c >= 2; c /= 2) {
+      const int64_t cost = router_cost(N, E, kSkTokens, c, cus);
+      if (cost < skinny) skinny = cost, epb = c;
+    }
+    if (skinny < small && skinny < big)
+      return launch_skinny<1>(xb, N, d, wb, E, logits, stream, epb);
     if (big <= small) return launch_tiled<128, 256, 2, 4, 16>(xb, N, d, wb, E, logits, stream);
     return launch_tiled<64, 64, 2, 2, 8>(xb, N, d, wb, E, logits, stream);
   }

@@ -47,6 +47,12 @@ CASES = {
                                         act="bf16"), None),
     "tiled_small_ragged": (synth.config("rt_ts", N=2500, d=320, ffn=64, E=130, K=8, W=2,
                                         act="bf16"), None),
+    # few tokens and many experts: the skinny kernel on blocks of 2 and of 4
+    # experts, the last block ragged
+    "skinny_epb2": (synth.config("rt_e2", N=20, d=256, ffn=64, E=130, K=8, W=2, act="bf16"),
+                    None),
+    "skinny_epb4": (synth.config("rt_e4", N=40, d=256, ffn=64, E=202, K=8, W=2, act="bf16"),
+                    None),
 }
 
 
