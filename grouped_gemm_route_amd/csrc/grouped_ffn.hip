@@ -565,10 +565,21 @@ __global__ __launch_bounds__(NW * kWave, 1) void ffn_gemm_bf16_kernel(
 // ---------------------------------------------------------------------------
 // fp32 FMA GEMM (small layers)
 // ---------------------------------------------------------------------------
+// Block tile 32 tokens x 32 output features (x 2 for gate and up), the
+// reduction in chunks of up to 128 staged in LDS: 256 threads, thread t
+// owning token t / 8 and features 4 (t % 8) .. + 4.  Small layers are bound
+// by load latency, so a tile is small (more blocks) and the next chunk's
+// loads are in flight while the current one is multiplied.  Each operand
+// row is loaded as 16-byte pieces (Kdim is a multiple of 8); thread t loads
+// row t % 32 of a 32-row operand, pieces t / 32 + 8 i, and writes them
+// transposed into LDS ([k][row], conflict-free).  Rows past the tile or the
+// output width are clamped to the last valid one and never stored; pieces
+// past Kdim are zero.
 
-constexpr int kFM = kF32TileRows;  // 64 tokens
-constexpr int kFN = 64;            // output columns
-constexpr int kFK = 16;
+constexpr int kFM = kF32TileRows;  // 32 tokens
+constexpr int kFN = 32;            // output features
+constexpr int kFK = 128;           // reduction elements per chunk
+constexpr int kFP = kFK / 4 / (kThreads / 32);  // 16-byte pieces per thread and operand
 
 template <bool kDual>
 __global__ __launch_bounds__(kThreads) void ffn_gemm_f32_kernel(
@@ -576,9 +587,10 @@ __global__ __launch_bounds__(kThreads) void ffn_gemm_f32_kernel(
     const float* __restrict__ w1, int Nout, float* __restrict__ out,
     const int4* __restrict__ tiles, const int* __restrict__ tile_start,
     const int* __restrict__ num_tiles, int E, int n_tiles) {
-  __shared__ float a_s[kFK][kFM + 1];
-  __shared__ float w0_s[kFK][kFN + 1];
-  __shared__ float w1_s[kDual ? kFK : 1][kFN + 1];
+  static_assert(kFM == 32 && kFN == 32 && kFP * 4 * (kThreads / 32) == kFK, "fp32 tile");
+  __shared__ float a_s[kFK][kFM];
+  __shared__ float w0_s[kFK][kFN];
+  __shared__ float w1_s[kDual ? kFK : 1][kFN];
   int slot, n_tile;
   if (!map_block(tile_start, num_tiles, E, n_tiles, &slot, &n_tile)) return;
   const int4 tile = tiles[slot];
@@ -587,59 +599,66 @@ __global__ __launch_bounds__(kThreads) void ffn_gemm_f32_kernel(
   const int rows = tile.z - tile.y;
   const int n0 = n_tile * kFN;
   const int tid = threadIdx.x;
-  const int tx = tid % 16;  // columns tx*4 ..
-  const int ty = tid / 16;  // rows ty*4 ..
+  const int tx = tid % 8;   // features 4 tx ..
+  const int ty = tid / 8;   // token ty
+  const int lr = tid % 32;  // operand row this thread loads
+  const int lp = tid / 32;  // its first 16-byte piece of a chunk
   const size_t wbase = (size_t)e * Nout * Kdim;
+  const float* arow = act + (size_t)(row0 + min(lr, rows - 1)) * Kdim;
+  const float* w0row = w0 + wbase + (size_t)min(n0 + lr, Nout - 1) * Kdim;
+  const float* w1row = kDual ? w1 + wbase + (size_t)min(n0 + lr, Nout - 1) * Kdim : nullptr;
 
-  float acc0[4][4] = {}, acc1[4][4] = {};
+  float4 ra[kFP], rw0[kFP], rw1[kDual ? kFP : 1];
+  auto load = [&](int k0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < kFP; ++i) {
+      const int k = k0 + (lp + 8 * i) * 4;
+      const bool in = k < Kdim;
+      ra[i] = in ? *reinterpret_cast<const float4*>(arow + k) : float4{0, 0, 0, 0};
+      rw0[i] = in ? *reinterpret_cast<const float4*>(w0row + k) : float4{0, 0, 0, 0};
+      if (kDual) rw1[i] = in ? *reinterpret_cast<const float4*>(w1row + k) : float4{0, 0, 0, 0};
+    }
+  };
+  float acc0[4] = {}, acc1[4] = {};
+  load(0);
   for (int k0 = 0; k0 < Kdim; k0 += kFK) {
+    __syncthreads();  // every thread is done with the previous chunk
 #pragma unroll
-    for (int i = 0; i < (kFM * kFK) / kThreads; ++i) {
-      const int q = tid + i * kThreads;
-      const int r = q / kFK, kk = q % kFK;
-      const int k = k0 + kk;
-      const int row = row0 + min(r, rows - 1);
-      a_s[kk][r] = k < Kdim ? act[(size_t)row * Kdim + k] : 0.0f;
-      const int n = min(n0 + r, Nout - 1);
-      w0_s[kk][r] = k < Kdim ? w0[wbase + (size_t)n * Kdim + k] : 0.0f;
-      if (kDual) w1_s[kk][r] = k < Kdim ? w1[wbase + (size_t)n * Kdim + k] : 0.0f;
-    }
-    __syncthreads();
+    for (int i = 0; i < kFP; ++i) {
+      const int kk = (lp + 8 * i) * 4;
 #pragma unroll
-    for (int kk = 0; kk < kFK; ++kk) {
-      float a[4], b0[4], b1[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) a[i] = a_s[kk][ty * 4 + i];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        b0[j] = w0_s[kk][tx * 4 + j];
-        if (kDual) b1[j] = w1_s[kk][tx * 4 + j];
+      for (int c = 0; c < 4; ++c) {
+        a_s[kk + c][lr] = ra[i][c];
+        w0_s[kk + c][lr] = rw0[i][c];
+        if (kDual) w1_s[kk + c][lr] = rw1[i][c];
       }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          acc0[i][j] = fmaf(a[i], b0[j], acc0[i][j]);
-          if (kDual) acc1[i][j] = fmaf(a[i], b1[j], acc1[i][j]);
-        }
     }
     __syncthreads();
-  }
+    if (k0 + kFK < Kdim) load(k0 + kFK);  // in flight during this chunk
+    const int kc = min(kFK, Kdim - k0);
+    for (int kk = 0; kk < kc; ++kk) {
+      const float a = a_s[kk][ty];
+      const float4 b0 = *reinterpret_cast<const float4*>(&w0_s[kk][tx * 4]);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int m = ty * 4 + i;
-    if (m >= rows) continue;
+      for (int j = 0; j < 4; ++j) acc0[j] = fmaf(a, b0[j], acc0[j]);
+      if (kDual) {
+        const float4 b1 = *reinterpret_cast<const float4*>(&w1_s[kk][tx * 4]);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int n = n0 + tx * 4 + j;
-      if (n >= Nout) continue;
-      float v = acc0[i][j];
-      if (kDual) v = v / (1.0f + __expf(-v)) * acc1[i][j];
-      out[(size_t)(row0 + m) * Nout + n] = v;
+        for (int j = 0; j < 4; ++j) acc1[j] = fmaf(a, b1[j], acc1[j]);
+      }
     }
+  }
+  if (ty >= rows) return;
+  float* orow = out + (size_t)(row0 + ty) * Nout;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int n = n0 + tx * 4 + j;
+    if (n >= Nout) continue;
+    float v = acc0[j];
+    if (kDual) v = v / (1.0f + __expf(-v)) * acc1[j];
+    orow[n] = v;
   }
 }
-
 
 template <int BM, int WM, int NW, bool kDual>
 hipError_t launch_bf16_gemm(const bf16* act, int Kdim, const bf16* w0,

@@ -22,7 +22,7 @@ constexpr int kRankBlockTokens = 256;
 
 // Grouped FFN tile heights (rows of the packed buffer per tile).
 constexpr int kBf16TileRows = 128;
-constexpr int kF32TileRows = 64;
+constexpr int kF32TileRows = 32;
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 

@@ -122,6 +122,11 @@ SMALL = {
                               act="bf16", C=None),
     "f32_nonpow2": synth.config("f32_nonpow2", N=100, d=24, ffn=40, E=6, K=3, W=3,
                                 act="f32", C=1.0),
+    # fp32 layers whose reductions take two 128-element chunks, the second
+    # ragged (gate/up 128 + 72, down 128 + 8), with experts of several
+    # 32-row tiles
+    "f32_two_chunks": synth.config("f32_two_chunks", N=300, d=200, ffn=136, E=5, K=2, W=5,
+                                   act="f32", C=None),
     "renormalized": synth.config("renormalized", N=90, d=64, ffn=64, E=16, K=4, W=4,
                                  act="bf16", C=None, renormalize=True),
     "many_blocks_e8": synth.config("many_blocks_e8", N=1500, d=64, ffn=128, E=8, K=2, W=8,
