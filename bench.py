@@ -313,6 +313,23 @@ def main():
         },
         "stages": stages,
     }
+    if cfg["act"] == "bf16":
+        # the layer's performance targets, stated for the dense8 workload:
+        # the grouped GEMM at >= 50% of bf16 MFMA peak and dispatch + combine
+        # at >= 60% of HBM peak (cold caches; the in-step figure beside it)
+        dc_frac = cold_dc / HBM_PEAK_GBPS if cold else None
+        result["targets"] = {
+            "workload": "dense8",
+            "applies": args.workload == "dense8",
+            "grouped_gemm_mfma_frac": {"value": achieved_tflops / peak, "target": 0.50,
+                                       "met": achieved_tflops / peak >= 0.50},
+            "dispatch_combine_hbm_frac_cold": {
+                "value": dc_frac, "target": 0.60,
+                "met": dc_frac is not None and dc_frac >= 0.60},
+            "dispatch_combine_hbm_frac_in_step": {
+                "value": hot_dc / HBM_PEAK_GBPS, "target": 0.60,
+                "met": hot_dc / HBM_PEAK_GBPS >= 0.60},
+        }
 
     result["graph"] = graph_block(layer, inp, ffn_args, N, stream, args.steps)
     result["metrics"] = routing_metrics(layer, cfg, cap, M)
