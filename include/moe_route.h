@@ -162,9 +162,11 @@ int moe_reroute_overflow(const float* logits, int32_t N, int32_t E, int32_t K, i
  * logits agree with an exact sum to within the fp32 summation bound and
  * near-ties may order differently.
  *   x          [N, d] of dtype; w_router [E, d] of dtype; logits [N, E] fp32 out.
+ * Results are deterministic (every logit's terms are added in a fixed
+ * order for given N, d and E).
  * Checks: pointers non-null; N, d, E >= 1; d a multiple of 8
- *         (INVALID_ARG); dtype; E <= MOE_MAX_EXPERTS; N*E < 2^31
- *         (UNSUPPORTED).
+ *         (INVALID_ARG); dtype; E <= MOE_MAX_EXPERTS; N*E < 2^31 and
+ *         256 * d * element size < 2^31 (UNSUPPORTED).
  */
 int moe_router_logits(const void* x, int32_t dtype, int32_t N, int32_t d,
                       const void* w_router, int32_t E, float* logits, void* stream);
