@@ -95,3 +95,18 @@ def test_router_logits_and_route(name):
         assert np.array_equal(np.sort(_np(idx)[rows][clear], 1), np.sort(ei[clear], 1))
     print(f"[router] {name}: rows checked {len(rows)} max err {np.abs(got - exact).max():.3e}",
           flush=True)
+
+
+@pytest.mark.parametrize("name", ["dense8", "fine128", "decode256", "tiled_big_ragged",
+                                  "skinny_epb4"])
+def test_router_logits_bitwise_repeatable(name):
+    """Two calls on the same inputs give the same bits (the split-reduction
+    waves and the skinny kernel's partial tiles meet in a fixed order)."""
+    cfg, _ = CASES[name]
+    print(f"[router repeat] {name}", flush=True)
+    x = synth.make_x(cfg, DEV)
+    wr = synth.make_router(cfg, DEV)
+    a = B.moe_router_logits(x, wr)
+    b = B.moe_router_logits(x, wr)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
