@@ -70,6 +70,8 @@ __device__ __forceinline__ int group_min(int a) {
   return a;
 }
 
+constexpr int kRouteBufferFlags = 0x00020000;  // raw 32-bit buffer accesses
+
 template <int L, int VPL, bool kSigmoid>
 __global__ __launch_bounds__(256) void route_topk_kernel(
     const float* __restrict__ logits, int N, int E, int K, int renormalize,
@@ -82,12 +84,24 @@ __global__ __launch_bounds__(256) void route_topk_kernel(
                   lane / L;
   const bool valid = tok < N;
 
+  // the wave's rows through one buffer descriptor (wave-uniform, so it sits
+  // in scalar registers): the range ends at the wave's last token below N,
+  // so a token past N reads zeros without a branch; an expert past E reads
+  // whatever follows and becomes -inf
   float v[VPL];
-  const float* row = logits + (size_t)(valid ? tok : 0) * E;
+  const int tok0 = __builtin_amdgcn_readfirstlane(
+      (blockIdx.x * (blockDim.x / kWave) + wave) * kGroupsPerWave);
+  const int wave_bytes =
+      __builtin_amdgcn_readfirstlane(max(0, min(kGroupsPerWave, N - tok0)) * E * 4);
+  const __amdgpu_buffer_rsrc_t rr = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(logits + (size_t)tok0 * E), 0, (uint32_t)wave_bytes, kRouteBufferFlags);
+  const int row_off = (lane / L) * E * 4;
 #pragma unroll
   for (int i = 0; i < VPL; ++i) {
     const int e = j + i * L;
-    v[i] = e < E ? (valid ? row[e] : 0.0f) : -INFINITY;
+    const float raw = __builtin_bit_cast(
+        float, __builtin_amdgcn_raw_buffer_load_b32(rr, row_off + e * 4, 0, 0));
+    v[i] = e < E ? raw : -INFINITY;
   }
 
   float m = 0.0f, s = 1.0f;
@@ -98,7 +112,9 @@ __global__ __launch_bounds__(256) void route_topk_kernel(
     m = group_reduce<L, true>(m);
     s = 0.0f;
 #pragma unroll
-    for (int i = 0; i < VPL; ++i) s += expf(v[i] - m);  // padding: exp(-inf) = 0
+    // v_exp_f32 on (v - m) log2(e): within about 2^-22 of expf relative
+    // to the largest term, far inside the weights' tolerance
+    for (int i = 0; i < VPL; ++i) s += __expf(v[i] - m);  // padding: exp(-inf) = 0
     s = group_reduce<L, false>(s);
   }
 
@@ -132,7 +148,7 @@ __global__ __launch_bounds__(256) void route_topk_kernel(
     if (j < K) w = sigmoid_ratio(my_logit, l0);
     w = w / group_reduce<L, false>(w);
   } else {
-    if (j < K) w = kSigmoid ? 1.0f / (1.0f + expf(-my_logit)) : expf(my_logit - m) / s;
+    if (j < K) w = kSigmoid ? 1.0f / (1.0f + expf(-my_logit)) : __expf(my_logit - m) / s;
     if (renormalize) w = w / group_reduce<L, false>(w);
   }
   if (valid && j < K) {
