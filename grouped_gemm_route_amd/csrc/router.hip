@@ -7,9 +7,10 @@
 // bf16, more than 64 experts (and d a multiple of 64), when N leaves enough
 // token blocks: an MFMA GEMM (v_mfma_f32_32x32x16_bf16, fp32 accumulate)
 // on block tiles of TT tokens x TE experts, 64 reduction elements per stage.
-// A block moves (TT + TE) rows of d elements through its CU, so the tile is
-// the largest that still gives every CU a block: 128 x 256 (16 waves) when
-// N / 128 covers the CUs, else 64 x 64 (8 waves).  Both operands go straight
+// A block moves (TT + TE) rows of d elements through its CU, so a CU moves
+// ceil(blocks / CUs) (TT + TE) rows in all; the launcher takes whichever of
+// 128 x 256 (16 waves), 64 x 64 (8 waves) and the skinny form below makes
+// that count smallest.  Both operands go straight
 // into LDS (buffer loads to LDS) in a ring of S stages, S - 1 of them in
 // flight while one is multiplied, with one fence-free barrier per stage;
 // the chunk swizzle of the grouped GEMM keeps the 128-byte rows
