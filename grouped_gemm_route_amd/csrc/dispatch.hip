@@ -139,14 +139,20 @@ __global__ __launch_bounds__(kScanThreads) void dispatch_scan_kernel(
   for (int r = tid; r <= W; r += blockDim.x) rank_offsets[r] = kept_s[r * per_rank];
 }
 
-constexpr int kScatterThreads = 256;
-// Largest per-block count table (blocks x experts) that every scatter block
-// scans for itself instead of waiting for the one-block scan kernel.
+// Threads of a scatter block (one token): 64, 128 or the most, 256.
+constexpr int kScatterMaxThreads = 256;
+// Largest per-block count table (blocks x experts), and most experts, that
+// every scatter block scans for itself instead of waiting for the one-block
+// scan kernel.
 constexpr int kFusedScanMaxCounts = 1024;
+constexpr int kFusedScanMaxExperts = 256;
 // At most this many 16-byte pieces of the token's row per thread are loaded
-// before the index work (rows of up to 4 * kScatterThreads pieces are held
-// whole in registers); launches pick the fewest that hold the row.
+// before the index work (rows of up to 4 * threads pieces are held whole in
+// registers); launches pick the fewest that hold the row.
 constexpr int kMaxHeld = 4;
+// Below this many tokens the scatter runs 256 threads per token whatever the
+// row width.
+constexpr int kScatterFewTokens = 1024;
 // buffer resource word 3 for raw 32-bit accesses (data format 32)
 constexpr int kRowBufferFlags = 0x00020000;
 
@@ -163,9 +169,12 @@ constexpr int kRowBufferFlags = 0x00020000;
 //   lane stores its 8 codes (8 bytes) and, once per group, the scale to
 //   every kept row.
 //   kHeld: pieces per thread loaded ahead (1, 2 or kMaxHeld); pieces past
-//   kHeld * kScatterThreads are loaded and stored one at a time afterwards.
-template <bool kFusedScan, bool kFp8, int kHeld>
-__global__ __launch_bounds__(kScatterThreads) void dispatch_scatter_kernel(
+//   kHeld * kThreads are loaded and stored one at a time afterwards.
+//   kThreads: the block's threads.  Fewer threads, each holding more
+//   pieces, launch fewer waves for the same bytes: with many tokens the
+//   launch picks about a quarter of the row's pieces (64, 128 or 256).
+template <bool kFusedScan, bool kFp8, int kHeld, int kThreads>
+__global__ __launch_bounds__(kThreads) void dispatch_scatter_kernel(
     const uint4* __restrict__ x, int row_chunks, int N,
     const int32_t* __restrict__ topk_idx, int E, int K, int W, int64_t capacity,
     const int32_t* __restrict__ block_counts, const int32_t* __restrict__ block_excl,
@@ -176,8 +185,8 @@ __global__ __launch_bounds__(kScatterThreads) void dispatch_scatter_kernel(
     int32_t* __restrict__ dest) {
   __shared__ int rows[MOE_MAX_TOPK];
   __shared__ int table[kFusedScan ? kFusedScanMaxCounts : 1];
-  __shared__ int offs[kFusedScan ? kScatterThreads + 1 : 1];
-  __shared__ int base[kFusedScan ? kScatterThreads : 1];
+  __shared__ int offs[kFusedScan ? kFusedScanMaxExperts + 1 : 1];
+  __shared__ int base[kFusedScan ? kFusedScanMaxExperts : 1];
   const int t = blockIdx.x;
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -193,7 +202,7 @@ __global__ __launch_bounds__(kScatterThreads) void dispatch_scatter_kernel(
 #pragma unroll
   for (int u = 0; u < kHeld; ++u)
     held[u] = __builtin_amdgcn_raw_buffer_load_b128(
-        row_rsrc, (tid + u * kScatterThreads) * (int)sizeof(uint4), 0, 0);
+        row_rsrc, (tid + u * kThreads) * (int)sizeof(uint4), 0, 0);
 
   if (tid < kWave) {
     int e = -1, lr = 0;
@@ -287,7 +296,7 @@ __global__ __launch_bounds__(kScatterThreads) void dispatch_scatter_kernel(
   // for the stores issued before it.
 #pragma unroll
   for (int u = 0; u < kHeld; ++u) asm volatile("" ::"v"(held[u]));
-  const int extra0 = tid + kHeld * kScatterThreads;  // pieces beyond the held ones
+  const int extra0 = tid + kHeld * kThreads;  // pieces beyond the held ones
 
   if constexpr (kFp8) {
     // row_chunks is a multiple of 16, so the lanes of a group are active
@@ -299,7 +308,7 @@ __global__ __launch_bounds__(kScatterThreads) void dispatch_scatter_kernel(
     float scale[kHeld];
 #pragma unroll
     for (int u = 0; u < kHeld; ++u) {
-      const int c = tid + u * kScatterThreads;
+      const int c = tid + u * kThreads;
       if (c < row_chunks) codes[u] = quantize_piece(__builtin_bit_cast(uint4, held[u]), &scale[u]);
     }
     for (int k = 0; k < K; ++k) {
@@ -307,14 +316,14 @@ __global__ __launch_bounds__(kScatterThreads) void dispatch_scatter_kernel(
       if (rk < 0) continue;
 #pragma unroll
       for (int u = 0; u < kHeld; ++u) {
-        const int c = tid + u * kScatterThreads;
+        const int c = tid + u * kThreads;
         if (c < row_chunks) {
           q[(size_t)rk * row_chunks + c] = codes[u];
           if (c % kPieces == 0) x_scale[(size_t)rk * groups + c / kPieces] = scale[u];
         }
       }
     }
-    for (int c = extra0; c < row_chunks; c += kScatterThreads) {
+    for (int c = extra0; c < row_chunks; c += kThreads) {
       float sc;
       const uint2 cd = quantize_piece(src[c], &sc);
       for (int k = 0; k < K; ++k) {
@@ -332,11 +341,11 @@ __global__ __launch_bounds__(kScatterThreads) void dispatch_scatter_kernel(
       u32x4* drow = dst + (size_t)rk * row_chunks;
 #pragma unroll
       for (int u = 0; u < kHeld; ++u) {
-        const int c = tid + u * kScatterThreads;
+        const int c = tid + u * kThreads;
         if (c < row_chunks) drow[c] = held[u];
       }
     }
-    for (int c = extra0; c < row_chunks; c += kScatterThreads) {
+    for (int c = extra0; c < row_chunks; c += kThreads) {
       const u32x4 v = *reinterpret_cast<const u32x4*>(src + c);
       for (int k = 0; k < K; ++k) {
         const int rk = rows[k];
@@ -383,7 +392,7 @@ hipError_t launch_dispatch(const void* x, size_t row_bytes, int N,
   const bool fp8 = x_scale != nullptr;
   const int row_chunks = (int)(row_bytes / 16);
   const uint4* xs = static_cast<const uint4*>(x);
-  const bool fused = (int64_t)B * E <= kFusedScanMaxCounts && E <= kScatterThreads;
+  const bool fused = (int64_t)B * E <= kFusedScanMaxCounts && E <= kFusedScanMaxExperts;
   if (!fused) {
     dispatch_scan_kernel<<<1, kScanThreads, 0, stream>>>(
         ws.block_counts, B, E, W, capacity, ws.block_excl, demand, counts,
@@ -391,21 +400,34 @@ hipError_t launch_dispatch(const void* x, size_t row_bytes, int N,
     err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
-  const int held = row_chunks <= kScatterThreads ? 1 : row_chunks <= 2 * kScatterThreads ? 2 : 4;
-  auto go = [&](auto fused_c, auto fp8_c, auto held_c) {
+  // threads per token: about a quarter of the row's pieces when there are
+  // enough tokens to fill the GPU with the fewer waves (dense8's 512-piece
+  // rows on 128 threads: cold dispatch 22.7 against 28.5 us on 256), else
+  // all 256 (a few tokens of wide rows want every thread)
+  const int threads = N < kScatterFewTokens || row_chunks > 2 * kScatterMaxThreads
+                          ? kScatterMaxThreads
+                          : row_chunks > kScatterMaxThreads ? 128 : 64;
+  const int held = row_chunks <= threads ? 1 : row_chunks <= 2 * threads ? 2 : kMaxHeld;
+  auto go = [&](auto fused_c, auto fp8_c, auto held_c, auto threads_c) {
+    constexpr int kT = decltype(threads_c)::value;
     dispatch_scatter_kernel<decltype(fused_c)::value, decltype(fp8_c)::value,
-                            decltype(held_c)::value><<<N, kScatterThreads, 0, stream>>>(
+                            decltype(held_c)::value, kT><<<N, kT, 0, stream>>>(
         xs, row_chunks, N, topk_idx, E, K, W, capacity, ws.block_counts, ws.block_excl,
         ws.local_rank, offsets, demand, counts, rank_offsets, x_perm,
         fp8 ? x_scale : nullptr, perm_token, dest);
+  };
+  auto by_threads = [&](auto fused_c, auto fp8_c, auto held_c) {
+    if (threads == 64) go(fused_c, fp8_c, held_c, std::integral_constant<int, 64>{});
+    else if (threads == 128) go(fused_c, fp8_c, held_c, std::integral_constant<int, 128>{});
+    else go(fused_c, fp8_c, held_c, std::integral_constant<int, kScatterMaxThreads>{});
   };
   auto by_held = [&](auto fused_c, auto fp8_c) {
     using I = std::integral_constant<int, 1>;
     using II = std::integral_constant<int, 2>;
     using IV = std::integral_constant<int, kMaxHeld>;
-    if (held == 1) go(fused_c, fp8_c, I{});
-    else if (held == 2) go(fused_c, fp8_c, II{});
-    else go(fused_c, fp8_c, IV{});
+    if (held == 1) by_threads(fused_c, fp8_c, I{});
+    else if (held == 2) by_threads(fused_c, fp8_c, II{});
+    else by_threads(fused_c, fp8_c, IV{});
   };
   using T = std::true_type;
   using F = std::false_type;

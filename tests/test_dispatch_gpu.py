@@ -1,10 +1,12 @@
 """Dispatch alone, HIP path vs the oracle, across row widths and count-table sizes.
 
 The scatter kernel holds 1, 2 or 4 of a token's 16-byte row pieces per thread
-(256 threads per token) before it knows the token's rows, and copies any
-further pieces one by one afterwards.  The widths below reach every one of
-those paths, fully and partly filled, for bf16 and fp32 rows and for the fp8
-payload.  Two expert counts cover both ways of finding the expert offsets:
+before it knows the token's rows, and copies any further pieces one by one
+afterwards; it runs 256 threads per token below 1024 tokens, and from 1024
+tokens 64, 128 or 256 by row width (about a quarter of the row's pieces).
+The widths below reach every one of those paths, fully and partly filled,
+for bf16 and fp32 rows and for the fp8 payload, at 300 tokens (256 threads)
+and at 2100 (the narrower blocks).  Two expert counts cover both ways of finding the expert offsets:
 each scatter block scanning the small per-block count table itself (8
 experts), and the one-block scan kernel (128 experts over 9 blocks of
 tokens: a table of 1152 counts).  Further cases take both paths at their
@@ -90,11 +92,13 @@ def test_dispatch_row_widths_match_oracle(act, d, C, routing):
 FP8_WIDTHS = [128, 2048, 4224, 8320]   # 16, 256, 528 and 1040 pieces
 
 
+@pytest.mark.parametrize("routing", ROUTINGS, ids=("e8", "e128"))
 @pytest.mark.parametrize("d", FP8_WIDTHS)
-def test_dispatch_fp8_row_widths_match_oracle(d):
-    N, E, K, W = ROUTINGS[0]
-    cfg = synth.config(f"width_fp8_{d}", N=N, d=d, ffn=64, E=E, K=K, W=W, act="bf16", C=0.8)
-    print(f"[dispatch] fp8 d={d}", flush=True)
+def test_dispatch_fp8_row_widths_match_oracle(d, routing):
+    N, E, K, W = routing
+    cfg = synth.config(f"width_fp8_{d}_{E}", N=N, d=d, ffn=64, E=E, K=K, W=W, act="bf16",
+                       C=0.8)
+    print(f"[dispatch] fp8 d={d} N={N} E={E}", flush=True)
     cap = O.capacity(0.8, N, K, E)
     inp = synth.make_inputs(cfg, DEV, weights=False)
     idx, _ = B.moe_route_topk(inp["logits"], K)
