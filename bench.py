@@ -131,7 +131,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the layer's "
-              "multi-GPU exchange is not part of this build.", file=sys.stderr)
+              "multi-GPU exchange is not implemented here.", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
