@@ -94,6 +94,20 @@ def ffn_flops(cfg, M):
     return 6.0 * M * cfg["d"] * cfg["ffn"]
 
 
+def ffn_bytes(cfg, M, nonempty, b):
+    """HBM bytes the grouped FFN must move: the three weight matrices of
+    every expert that has rows (3 d ffn b each), the kept rows read
+    (M d b), h written and read back (2 M ffn b) and y_perm written
+    (M d b)."""
+    d, ffn = cfg["d"], cfg["ffn"]
+    return nonempty * 3 * d * ffn * b + 2 * M * d * b + 2 * M * ffn * b
+
+
+def route_bytes(cfg, b_logit=4):
+    """Routing reads every logit and writes K ids and K weights per token."""
+    return cfg["N"] * cfg["E"] * b_logit + cfg["N"] * cfg["K"] * 8
+
+
 def source_digest(paths):
     """sha256[:16] of C++ sources with their comments and blank space
     removed, so the digest names the code a counter run measured, not its
@@ -212,6 +226,16 @@ def main():
     flops = ffn_flops(cfg, M)
     achieved_tflops = flops / (st["ffn"] * 1e-3) / 1e12
     peak = MFMA_BF16_PEAK_TFLOPS if cfg["act"] == "bf16" else FP32_PEAK_TFLOPS
+    # which roof binds the grouped FFN: the longer of its flops at peak and
+    # its bytes at peak HBM bandwidth (weight streaming when experts get few
+    # rows)
+    nonempty = int((layer.disp["counts"] > 0).sum().item())
+    fbytes = ffn_bytes(cfg, M, nonempty, b)
+    ffn_gbps = fbytes / (st["ffn"] * 1e-3) / 1e9
+    t_mfma = flops / (peak * 1e12)
+    t_hbm = fbytes / (HBM_PEAK_GBPS * 1e9)
+    ffn_bound = "hbm" if t_hbm > t_mfma else ("mfma" if cfg["act"] == "bf16" else "alu")
+    rbytes = route_bytes(cfg)
 
     # Cold-cache timing of the two HBM-bound stages, outside the timed steps:
     # before each rep a 512 MiB buffer is written and then read, so neither
@@ -260,6 +284,14 @@ def main():
         "dispatch_combine_GBps_in_step": hot_dc,
         "ffn_TFLOPs": achieved_tflops,
         "ffn_mfma_frac": achieved_tflops / peak,
+        "ffn_bytes": fbytes,
+        "ffn_GBps": ffn_gbps,
+        "ffn_hbm_frac": ffn_gbps / HBM_PEAK_GBPS,
+        "ffn_bound": ffn_bound,
+        "ffn_roof_frac": max(t_mfma, t_hbm) / (st["ffn"] * 1e-3),
+        "route_bytes": rbytes,
+        "route_GBps": rbytes / (st["route"] * 1e-3) / 1e9,
+        "route_hbm_frac": rbytes / (st["route"] * 1e-3) / 1e9 / HBM_PEAK_GBPS,
         "ffn_weights": weights,
         "weight_pack_ms": pack_ms,
         ("ffn_plain_weights_ms" if weights == "packed" else "ffn_packed_weights_ms"):
@@ -304,11 +336,11 @@ def main():
         "roofline": {
             "kernel": ("moe_grouped_ffn_packed" if weights == "packed" else "moe_grouped_ffn")
                       + " call (tile schedule + gate/up GEMM + down GEMM)",
-            "bound": "mfma",
-            "achieved": achieved_tflops,
-            "peak": peak,
-            "unit": "TFLOP/s",
-            "frac": achieved_tflops / peak,
+            "bound": ffn_bound,
+            "achieved": ffn_gbps if ffn_bound == "hbm" else achieved_tflops,
+            "peak": HBM_PEAK_GBPS if ffn_bound == "hbm" else peak,
+            "unit": "GB/s" if ffn_bound == "hbm" else "TFLOP/s",
+            "frac": ffn_gbps / HBM_PEAK_GBPS if ffn_bound == "hbm" else achieved_tflops / peak,
             "traffic": load_traffic(args.traffic_json, args.workload, weights),
         },
         "stages": stages,

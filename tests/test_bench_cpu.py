@@ -70,3 +70,16 @@ def test_more_than_one_gpu_is_refused(n):
     assert r.returncode == 2
     assert "one GPU only" in r.stderr
     assert r.stdout == ""
+
+
+def test_ffn_and_route_bytes_by_hand():
+    # dense8: 8 experts with rows, each 3 x 4096 x 14336 bf16 weights
+    # (2,818,572,288 B in all), x_perm read and y_perm written
+    # (2 x 8192 x 4096 x 2 B) and h written and read (2 x 8192 x 14336 x 2 B)
+    cfg = dict(N=4096, d=4096, ffn=14336, E=8, K=2)
+    assert bench.ffn_bytes(cfg, 8192, 8, 2) == 2818572288 + 134217728 + 469762048
+    # experts without rows stream no weights
+    assert bench.ffn_bytes(cfg, 8192, 8, 2) - bench.ffn_bytes(cfg, 8192, 7, 2) == \
+        3 * 4096 * 14336 * 2
+    # routing reads N x E fp32 logits and writes K ids and K weights per token
+    assert bench.route_bytes(cfg) == 4096 * 8 * 4 + 4096 * 2 * 8
