@@ -368,6 +368,8 @@ def main():
     if weights == "packed" and not args.no_per_rank:
         result["metrics"]["per_rank_ffn"] = per_rank_ffn_block(B, layer, ffn_args[0], cfg,
                                                                stream)
+    result["dispatch_paths"] = dispatch_paths_block(B, layer, inp, cfg, cap, stream,
+                                                    args.cold_reps)
     if not args.no_exchange:
         result["exchange"] = exchange_block(B, layer, inp["x"], cfg, M, b, stream)
         result["router_projection"] = router_block(B, synth, inp["x"], cfg, b, stream)
@@ -385,6 +387,71 @@ def main():
 
 
 XGMI_EGRESS_GBPS = 7 * 153.0   # MI355X: 7 xGMI links of about 153 GB/s each
+
+
+def dispatch_paths_block(B, layer, inp, cfg, cap, stream, cold_reps):
+    """Routing + dispatch both ways, timed alike: planned (moe_route_plan,
+    which also ranks and counts the tokens per expert, then
+    moe_dispatch_planned) and plain (moe_route_topk, then moe_dispatch with
+    its own counting pass).  Warm: 20 calls (or pairs) queued behind a spin
+    kernel, so that host call costs stay out, best of 3; cold: the dispatch
+    alone after the same cache scrub as the stages' cold figures (median).
+    step_path names the one the layer step runs (MoeLayer's default)."""
+    import numpy as np
+    import torch
+
+    N, d, E, K, W = cfg["N"], cfg["d"], cfg["E"], cfg["K"], cfg["W"]
+    dev = inp["x"].device
+    lg, x = inp["logits"], inp["x"]
+
+    def queued(fn, reps=20):
+        fn()
+        torch.cuda.synchronize()
+        best = float("inf")
+        for _ in range(3):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            torch.cuda._sleep(20_000_000)
+            e0.record(stream)
+            for _ in range(reps):
+                fn()
+            e1.record(stream)
+            e1.synchronize()
+            best = min(best, e0.elapsed_time(e1) / reps * 1e3)
+        return best
+
+    def cold(lay):
+        scrub = torch.empty(SCRUB_MIB << 18, dtype=torch.float32, device=dev)
+        times = []
+        for i in range(max(cold_reps, 1)):
+            scrub.fill_(float(i))
+            scrub.sum()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            lay.dispatch(x)
+            e1.record(stream)
+            e1.synchronize()
+            times.append(e0.elapsed_time(e1))
+        del scrub
+        return float(np.median(times)) * 1e3
+
+    out = {"step_path": "planned" if layer.planned else "plain"}
+    dests = {}
+    for name, planned in (("planned", True), ("plain", False)):
+        lay = B.MoeLayer(N, d, 16, E, K, W, cap, x.dtype, dev, planned=planned)
+        lay.route(lg)
+        lay.dispatch(x)
+        out[name] = {
+            "route_us": queued(lambda: lay.route(lg)),
+            "dispatch_us": queued(lambda: lay.dispatch(x)),
+            "route_dispatch_us": queued(lambda: (lay.route(lg), lay.dispatch(x))),
+            "cold_dispatch_us": cold(lay),
+        }
+        dests[name] = lay.disp["dest"].clone()
+        del lay
+    out["same_dest"] = bool(torch.equal(dests["planned"], dests["plain"]))
+    return out
 
 
 def graph_block(layer, inp, ffn_args, N, stream, steps):
@@ -599,14 +666,20 @@ def fp8_block(B, layer, x, cfg, M, stream, cold_reps):
     ys = torch.empty(N * K, d // 128, dtype=torch.float32, device=dev)
     out = torch.empty(N, d, dtype=torch.bfloat16, device=dev)
     xp = torch.empty(N * K, d, dtype=torch.bfloat16, device=dev)
-    B.moe_dispatch_fp8(x, layer.topk_idx, E, W, cap, out8)
+    if layer.planned:   # the layer's plan (its routing ran last)
+        def dispatch8():
+            B.moe_dispatch_planned(x, layer.topk_idx, E, W, cap, layer.plan, out8, fp8=True)
+    else:
+        def dispatch8():
+            B.moe_dispatch_fp8(x, layer.topk_idx, E, W, cap, out8)
+    dispatch8()
     B.moe_fp8_quantize_rows(layer.y_perm, n_rows, N * K, y8, ys)
     torch.cuda.synchronize()
 
     scrub = torch.empty(SCRUB_MIB << 18, dtype=torch.float32, device=dev)
     cold = {}
     fns = {
-        "dispatch": lambda: B.moe_dispatch_fp8(x, layer.topk_idx, E, W, cap, out8),
+        "dispatch": dispatch8,
         "combine": lambda: B.moe_combine_fp8(y8, ys, out8["dest"], layer.topk_w, out),
     }
     for name, fn in fns.items():

@@ -7,6 +7,7 @@ from .binding import (  # noqa: F401
     MoeError,
     MoeLayer,
     PackedFfnWeights,
+    alloc_route_plan,
     load_library,
     moe_abi_version,
     moe_capacity,
@@ -14,6 +15,7 @@ from .binding import (  # noqa: F401
     moe_combine_fp8,
     moe_dispatch,
     moe_dispatch_fp8,
+    moe_dispatch_planned,
     moe_dispatch_workspace_bytes,
     moe_exchange_plan,
     moe_exchange_workspace_bytes,
@@ -26,6 +28,8 @@ from .binding import (  # noqa: F401
     moe_packed_ffn_weight_bytes,
     moe_reroute_overflow,
     moe_reroute_workspace_bytes,
+    moe_route_plan,
+    moe_route_plan_bytes,
     moe_route_topk,
     moe_router_logits,
     moe_rows_permute,

@@ -39,6 +39,12 @@ SIGNATURES = [
      [_P, _I32, _I32, _I32, _P, _I32, _I32, _I32, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     ("moe_dispatch_noalloc", ctypes.c_int,
      [_P, _I32, _I32, _I32, _P, _I32, _I32, _I32, _I64, _P, _P, _P, _P, _P, _P, _P, _P]),
+    ("moe_route_plan_bytes", _SZ, [_I32, _I32, _I32]),
+    ("moe_route_plan", ctypes.c_int,
+     [_P, _I32, _I32, _I32, _I32, _I32, _I32, _I64, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    ("moe_dispatch_planned", ctypes.c_int,
+     [_P, _I32, _I32, _I32, _P, _I32, _I32, _I32, _I64, _P, _SZ, _P, _P, _P, _P, _P, _P, _P, _P,
+      _P]),
     ("moe_grouped_ffn_workspace_bytes", _SZ, [_I64, _I32, _I32]),
     ("moe_grouped_ffn", ctypes.c_int,
      [_P, _I32, _I32, _I32, _I32, _P, _I64, _P, _P, _P, _P, _P, _P, _SZ, _P]),
@@ -303,6 +309,98 @@ def moe_dispatch_noalloc(x, topk_idx, E, W, capacity, out=None):
         _ptr(out["x_perm"]), _ptr(out["perm_token"]), _ptr(out["dest"]),
         _ptr(out["demand"]), _ptr(out["counts"]), _ptr(out["offsets"]),
         _ptr(out["rank_offsets"]), _stream(x)))
+    return out
+
+
+def moe_route_plan_bytes(N, E, K):
+    return int(load_library().moe_route_plan_bytes(N, E, K))
+
+
+def alloc_route_plan(N, E, K, device):
+    """A plan buffer for moe_route_plan / moe_dispatch_planned, zeroed (its
+    arrival counter must start at zero; every call leaves it zero)."""
+    return torch.zeros(max(256, moe_route_plan_bytes(N, E, K)), dtype=torch.uint8,
+                       device=device)
+
+
+# MoeLayer's default: planned layers up to this many per-block counts
+PLAN_MAX_COUNTS = 65536
+
+
+def moe_route_plan(logits, K, W, capacity, plan, out=None, renormalize=False, topk_idx=None,
+                   topk_w=None, gate="softmax"):
+    """Routing that also ranks and counts the tokens per expert, into plan.
+    out: a dict holding demand, counts, offsets and rank_offsets (e.g. the
+    dispatch outputs the following moe_dispatch_planned gets; allocated when
+    None).  Returns (topk_idx, topk_w, out)."""
+    _need(logits, "logits", torch.float32)
+    N, E = logits.shape
+    dev = logits.device
+    if topk_idx is None:
+        topk_idx = torch.empty(N, K, dtype=torch.int32, device=dev)
+    if topk_w is None:
+        topk_w = torch.empty(N, K, dtype=torch.float32, device=dev)
+    _need(topk_idx, "topk_idx", torch.int32, dev)
+    _need(topk_w, "topk_w", torch.float32, dev)
+    if topk_idx.numel() != N * K or topk_w.numel() != N * K:
+        raise ValueError("topk_idx/topk_w must hold N*K elements")
+    if out is None:
+        out = {"demand": torch.empty(E, dtype=torch.int32, device=dev),
+               "counts": torch.empty(E, dtype=torch.int32, device=dev),
+               "offsets": torch.empty(E + 1, dtype=torch.int32, device=dev),
+               "rank_offsets": torch.empty(W + 1, dtype=torch.int32, device=dev)}
+    sizes = {"demand": E, "counts": E, "offsets": E + 1, "rank_offsets": W + 1}
+    for k, n in sizes.items():
+        _need(out[k], k, torch.int32, dev)
+        if out[k].numel() < n:
+            raise ValueError(f"{k} must hold at least {n} elements")
+    _need(plan, "plan", None, dev)
+    _check("moe_route_plan", load_library().moe_route_plan(
+        _ptr(logits), N, E, K, _gate(gate), int(bool(renormalize)), W, int(capacity),
+        _ptr(topk_idx), _ptr(topk_w), _ptr(out["demand"]), _ptr(out["counts"]),
+        _ptr(out["offsets"]), _ptr(out["rank_offsets"]), _ptr(plan),
+        plan.numel() * plan.element_size(), _stream(logits)))
+    return topk_idx, topk_w, out
+
+
+def moe_dispatch_planned(x, topk_idx, E, W, capacity, plan, out=None, fp8=False):
+    """moe_dispatch from a plan of moe_route_plan; returns the dict of outputs
+    (as moe_dispatch's; fp8=True: as moe_dispatch_fp8's, x8 and x_scale in
+    place of x_perm)."""
+    _need(x, "x")
+    code = _act_code(x, "x")
+    N, d = x.shape
+    dev = x.device
+    _need(topk_idx, "topk_idx", torch.int32, dev)
+    K = topk_idx.shape[1]
+    if topk_idx.shape[0] != N:
+        raise ValueError("topk_idx must be [N, K]")
+    if out is None:
+        out = (alloc_dispatch_fp8_outputs(N, d, E, K, W, dev) if fp8 else
+               alloc_dispatch_outputs(N, d, E, K, W, x.dtype, dev))
+    sizes = {"perm_token": N * K, "dest": N * K, "demand": E, "counts": E, "offsets": E + 1,
+             "rank_offsets": W + 1}
+    for k, n in sizes.items():
+        _need(out[k], k, torch.int32, dev)
+        if out[k].numel() < n:
+            raise ValueError(f"{k} must hold at least {n} elements")
+    if fp8:
+        rows, scale = out["x8"], out["x_scale"]
+        _need(rows, "x8", torch.uint8, dev)
+        _need(scale, "x_scale", torch.float32, dev)
+        if rows.numel() < N * K * d or scale.numel() < N * K * (d // FP8_GROUP):
+            raise ValueError("x8 / x_scale too small")
+    else:
+        rows, scale = out["x_perm"], None
+        _need(rows, "x_perm", x.dtype, dev)
+        if rows.numel() < N * K * d:
+            raise ValueError(f"x_perm must hold at least {N * K * d} elements")
+    _need(plan, "plan", None, dev)
+    _check("moe_dispatch_planned", load_library().moe_dispatch_planned(
+        _ptr(x), code, N, d, _ptr(topk_idx), E, K, W, int(capacity), _ptr(plan),
+        plan.numel() * plan.element_size(), _ptr(rows), None if scale is None else _ptr(scale),
+        _ptr(out["perm_token"]), _ptr(out["dest"]), _ptr(out["demand"]), _ptr(out["counts"]),
+        _ptr(out["offsets"]), _ptr(out["rank_offsets"]), _stream(x)))
     return out
 
 
@@ -665,17 +763,28 @@ class MoeLayer:
     turned back into bf16 for the FFN, its output rows are quantized and
     the combine reads them as fp8.  shared_ffn > 0 makes it a Residual-MoE
     layer with a shared MLP of that width: ``forward(..., shared=...)`` runs
-    it on every token and adds its output in the combine.
+    it on every token and adds its output in the combine.  planned (the
+    default without reroute) routes with moe_route_plan, which also ranks
+    and counts the tokens per expert, and dispatches with
+    moe_dispatch_planned, which needs no counting pass; planned=False
+    routes with moe_route_topk and dispatches with moe_dispatch.
     """
 
     def __init__(self, N, d, ffn, E, K, W, capacity, dtype, device, renormalize=False,
-                 gate="softmax", reroute=False, fp8=False, shared_ffn=0):
+                 gate="softmax", reroute=False, fp8=False, shared_ffn=0, planned=None):
         self.N, self.d, self.ffn_dim, self.E, self.K, self.W = N, d, ffn, E, K, W
         self.capacity = int(capacity)
         self.renormalize = renormalize
         self.gate = gate
         _gate(gate)
         self.reroute = reroute
+        if planned is None:
+            tokens = 128 if E <= 8 else 64          # moe_route_plan's blocks
+            planned = not reroute and -(-N // tokens) * E <= PLAN_MAX_COUNTS
+        if planned and reroute:
+            raise ValueError("a re-route changes the experts after the plan is made: "
+                             "planned=False with reroute=True")
+        self.planned = bool(planned)
         self.fp8 = fp8
         if fp8 and (dtype != torch.bfloat16 or d % FP8_GROUP):
             raise ValueError("the fp8 payload needs bf16 rows with d a multiple of 128")
@@ -684,6 +793,7 @@ class MoeLayer:
         self.topk_idx = torch.empty(N, K, dtype=torch.int32, device=dev)
         self.topk_w = torch.empty(N, K, dtype=torch.float32, device=dev)
         self.disp = alloc_dispatch_outputs(N, d, E, K, W, dtype, dev)
+        self.plan = alloc_route_plan(N, E, K, dev) if self.planned else None
         self.h = torch.empty(self.max_rows, ffn, dtype=dtype, device=dev)
         self.y_perm = torch.empty(self.max_rows, d, dtype=dtype, device=dev)
         self.ffn_ws = torch.empty(max(1, moe_grouped_ffn_workspace_bytes(self.max_rows, E, dtype)),
@@ -710,6 +820,10 @@ class MoeLayer:
                                        device=dev)
 
     def route(self, logits):
+        if self.planned:
+            moe_route_plan(logits, self.K, self.W, self.capacity, self.plan, self.disp,
+                           self.renormalize, self.topk_idx, self.topk_w, self.gate)
+            return self.topk_idx, self.topk_w
         moe_route_topk(logits, self.K, self.renormalize, self.topk_idx, self.topk_w, self.gate)
         if self.reroute:
             moe_reroute_overflow(logits, self.topk_idx, self.topk_w, self.capacity, self.gate,
@@ -717,9 +831,16 @@ class MoeLayer:
         return self.topk_idx, self.topk_w
 
     def dispatch(self, x):
-        if not self.fp8:
+        """(planned layers: after route, which made the plan)"""
+        if self.planned:
+            moe_dispatch_planned(x, self.topk_idx, self.E, self.W, self.capacity, self.plan,
+                                 self.disp, fp8=self.fp8)
+            if not self.fp8:
+                return self.disp
+        elif not self.fp8:
             return moe_dispatch(x, self.topk_idx, self.E, self.W, self.capacity, self.disp)
-        moe_dispatch_fp8(x, self.topk_idx, self.E, self.W, self.capacity, self.disp)
+        else:
+            moe_dispatch_fp8(x, self.topk_idx, self.E, self.W, self.capacity, self.disp)
         n_rows = self.disp["offsets"][self.E:]
         moe_fp8_dequantize_rows(self.disp["x8"], self.disp["x_scale"], n_rows, self.max_rows,
                                 self.disp["x_perm"])

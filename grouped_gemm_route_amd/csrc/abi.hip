@@ -162,6 +162,13 @@ size_t moe_dispatch_workspace_bytes(int32_t N, int32_t E, int32_t K) {
 
 namespace {
 
+// The per-block count table [ceil(N / tokens) + 64, E] of int32 addressed
+// with 32-bit byte offsets (its scan reads up to 32 rows past a range).
+bool table_fits(int32_t N, int32_t E, int tokens) {
+  const int64_t B = ((int64_t)N + tokens - 1) / tokens;
+  return (B + 64) * E * (int64_t)sizeof(int32_t) < ((int64_t)1 << 31);
+}
+
 // Checks shared by moe_dispatch and moe_dispatch_fp8 (es: bytes per element).
 int dispatch_checks(const char* fn, const void* x, int es, int32_t N, int32_t d,
                     const int32_t* topk_idx, int32_t E, int32_t K, int32_t W, int64_t capacity,
@@ -183,6 +190,8 @@ int dispatch_checks(const char* fn, const void* x, int es, int32_t N, int32_t d,
   if (E > MOE_MAX_EXPERTS || K > MOE_MAX_TOPK)
     return fail(MOE_ERR_UNSUPPORTED, "%s: E <= %d and K <= %d supported", fn, MOE_MAX_EXPERTS,
                 MOE_MAX_TOPK);
+  if (!table_fits(N, E, moe::kRankBlockTokens))
+    return fail(MOE_ERR_UNSUPPORTED, "%s: N*E too large", fn);
   const size_t need = moe::dispatch_workspace_bytes(N, E, K);
   if (!workspace || workspace_bytes < need)
     return fail(MOE_ERR_WORKSPACE, "%s: workspace needs %zu bytes", fn, need);
@@ -215,6 +224,81 @@ int moe_dispatch(const void* x, int32_t dtype, int32_t N, int32_t d,
                            x_perm, nullptr, perm_token, dest, demand, counts, offsets,
                            rank_offsets, ws, as_stream(stream)),
       "moe_dispatch");
+}
+
+size_t moe_route_plan_bytes(int32_t N, int32_t E, int32_t K) {
+  if (N < 1 || E < 1 || K < 1) return 0;
+  return moe::route_plan_bytes(N, E, K);
+}
+
+int moe_route_plan(const float* logits, int32_t N, int32_t E, int32_t K, int32_t gate,
+                   int32_t renormalize, int32_t W, int64_t capacity, int32_t* topk_idx,
+                   float* topk_w, int32_t* demand, int32_t* counts, int32_t* offsets,
+                   int32_t* rank_offsets, void* plan, size_t plan_bytes, void* stream) {
+  const char* fn = "moe_route_plan";
+  const int st = route_checks(fn, logits, N, E, K, topk_idx, topk_w);
+  if (st != MOE_OK) return st;
+  if (!demand || !counts || !offsets || !rank_offsets)
+    return fail(MOE_ERR_INVALID_ARG, "%s: null pointer", fn);
+  if (N < 1 || W < 1 || E % W != 0 || capacity < -1)
+    return fail(MOE_ERR_INVALID_ARG,
+                "%s: need N >= 1, W >= 1, E %% W == 0, capacity >= -1 (N=%d E=%d W=%d "
+                "capacity=%lld)", fn, N, E, W, (long long)capacity);
+  if (gate != MOE_GATE_SOFTMAX && gate != MOE_GATE_SIGMOID)
+    return fail(MOE_ERR_INVALID_ARG, "%s: gate %d is not a moe_gate_t", fn, gate);
+  if (!table_fits(N, E, moe::route_plan_tokens(E)))
+    return fail(MOE_ERR_UNSUPPORTED, "%s: N*E too large", fn);
+  const size_t need = moe::route_plan_bytes(N, E, K);
+  if (!plan || plan_bytes < need)
+    return fail(MOE_ERR_WORKSPACE, "%s: plan needs %zu bytes", fn, need);
+  return hip_status(
+      moe::launch_route_plan(logits, N, E, K, gate == MOE_GATE_SIGMOID, renormalize, W,
+                             capacity, topk_idx, topk_w, demand, counts, offsets, rank_offsets,
+                             moe::route_plan(plan, N, E, K), as_stream(stream)),
+      fn);
+}
+
+int moe_dispatch_planned(const void* x, int32_t dtype, int32_t N, int32_t d,
+                         const int32_t* topk_idx, int32_t E, int32_t K, int32_t W,
+                         int64_t capacity, void* plan, size_t plan_bytes, void* x_perm,
+                         float* x_scale, int32_t* perm_token, int32_t* dest, int32_t* demand,
+                         int32_t* counts, int32_t* offsets, int32_t* rank_offsets,
+                         void* stream) {
+  const char* fn = "moe_dispatch_planned";
+  const int es = elem_size(dtype);
+  if (x && es == 0) return fail(MOE_ERR_UNSUPPORTED, "%s: dtype %d", fn, dtype);
+  if (!x || !topk_idx || !x_perm || !perm_token || !dest || !demand || !counts || !offsets ||
+      !rank_offsets)
+    return fail(MOE_ERR_INVALID_ARG, "%s: null pointer", fn);
+  if (N < 1 || d < 1 || K < 1 || K > E || W < 1 || E % W != 0 || capacity < -1)
+    return fail(MOE_ERR_INVALID_ARG,
+                "%s: need N >= 1, d >= 1, 1 <= K <= E, W >= 1, E %% W == 0, "
+                "capacity >= -1 (N=%d d=%d E=%d K=%d W=%d capacity=%lld)",
+                fn, N, d, E, K, W, (long long)capacity);
+  if (((int64_t)d * es) % 16 != 0)
+    return fail(MOE_ERR_INVALID_ARG, "%s: row bytes d*%d must be a multiple of 16", fn, es);
+  if ((int64_t)N * K >= ((int64_t)1 << 31))
+    return fail(MOE_ERR_INVALID_ARG, "%s: N*K must be below 2^31", fn);
+  if (E > MOE_MAX_EXPERTS || K > MOE_MAX_TOPK)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: E <= %d and K <= %d supported", fn, MOE_MAX_EXPERTS,
+                MOE_MAX_TOPK);
+  if (!table_fits(N, E, moe::route_plan_tokens(E)))
+    return fail(MOE_ERR_UNSUPPORTED, "%s: N*E too large", fn);
+  if (x_scale) {
+    if (dtype != MOE_DTYPE_BF16)
+      return fail(MOE_ERR_INVALID_ARG, "%s: the fp8 payload needs bf16 rows", fn);
+    const int st = fp8_row_checks(fn, d);
+    if (st != MOE_OK) return st;
+  }
+  const size_t need = moe::route_plan_bytes(N, E, K);
+  if (!plan || plan_bytes < need)
+    return fail(MOE_ERR_WORKSPACE, "%s: plan needs %zu bytes", fn, need);
+  return hip_status(
+      moe::launch_dispatch_planned(x, (size_t)d * es, N, topk_idx, E, K, W, capacity,
+                                   moe::route_plan(plan, N, E, K), x_perm, x_scale, perm_token,
+                                   dest, demand, counts, offsets, rank_offsets,
+                                   as_stream(stream)),
+      fn);
 }
 
 }  // extern "C"

@@ -17,10 +17,11 @@
 //                  is popcount(mask[wave][e] & lanes-below-l) plus the
 //                  popcounts of the earlier waves' masks.  The block's
 //                  per-expert totals go to block_counts[b][e].
-//   scan kernel    (one block): per expert, an exclusive scan of the block
-//                  totals over blocks (block_excl) and their sum (demand);
-//                  counts = min(demand, capacity); offsets = exclusive scan
-//                  of counts over experts; rank_offsets[r] = offsets[r*E/W].
+//   scan kernel    (one block, rank_scan.h): per expert, an exclusive scan
+//                  of the block totals over blocks (block_excl) and their
+//                  sum (demand); counts = min(demand, capacity); offsets =
+//                  exclusive scan of counts over experts; rank_offsets[r] =
+//                  offsets[r*E/W].
 //   scatter kernel (one block per token): loads the token's row once from
 //                  HBM in 16-byte pieces; meanwhile r = block_excl + local
 //                  rank, kept iff capacity < 0 or r < capacity, and dest and
@@ -30,10 +31,14 @@
 //                  the scan kernel is not launched.
 // Because experts are numbered rank by rank, the (expert, token) order is
 // rank-major: rank r's send slice is rows [rank_offsets[r], rank_offsets[r+1]).
+// The planned dispatch (launch_dispatch_planned) has no rank kernel: the
+// routing kernel's fused variant (route_topk.hip) has already ranked the
+// tokens and counted them per expert, in blocks of its own size.
 #include "moe_route.h"
 #include "moe_internal.h"
 #include "block_scan.h"
 #include "fp8_codec.h"
+#include "rank_scan.h"
 
 #include <type_traits>
 
@@ -82,61 +87,16 @@ __global__ __launch_bounds__(kRankBlockTokens) void dispatch_rank_kernel(
   }
 }
 
-constexpr int kScanThreads = 1024;
-
-__global__ __launch_bounds__(kScanThreads) void dispatch_scan_kernel(
+// One block: the per-expert scan of the rank kernel's count table
+// (rank_scan.h).
+__global__ __launch_bounds__(kRankScanThreads) void dispatch_scan_kernel(
     const int32_t* __restrict__ block_counts, int B, int E, int W,
     int64_t capacity, int32_t* __restrict__ block_excl,
     int32_t* __restrict__ demand, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ rank_offsets) {
-  __shared__ int part_sum[kScanThreads];
-  __shared__ int kept_s[kScanThreads + 1];
-  __shared__ int wave_sums[kScanThreads / kWave];
-  const int tid = threadIdx.x;
-  // Thread (e, part): part p of P sums a contiguous range of blocks.
-  const int P = kScanThreads / E;  // E <= 1024
-  const int e = tid % E;
-  const int part = tid / E;
-  const bool active = part < P;
-  const int chunk = (B + P - 1) / P;
-  const int b0 = min(B, part * chunk);
-  const int b1 = min(B, b0 + chunk);
-  int s = 0;
-  if (active)
-    for (int b = b0; b < b1; ++b) s += block_counts[(size_t)b * E + e];
-  part_sum[tid] = s;
-  __syncthreads();
-  int kept = 0;
-  if (active) {
-    int run = 0;
-    for (int p = 0; p < part; ++p) run += part_sum[p * E + e];
-    for (int b = b0; b < b1; ++b) {
-      const int c = block_counts[(size_t)b * E + e];
-      block_excl[(size_t)b * E + e] = run;
-      run += c;
-    }
-    if (part == 0) {
-      int tot = 0;
-      for (int p = 0; p < P; ++p) tot += part_sum[p * E + e];
-      demand[e] = tot;
-      kept = capacity < 0 ? tot : (int)min((int64_t)tot, capacity);
-      counts[e] = kept;
-    }
-  }
-  // Exclusive scan of the kept counts over experts (threads 0..E-1 hold them).
-  int total = 0;
-  const int excl = block_exclusive_scan(tid < E ? kept : 0, wave_sums, &total);
-  if (tid < E) {
-    offsets[tid] = excl;
-    kept_s[tid] = excl;
-  }
-  if (tid == 0) {
-    offsets[E] = total;
-    kept_s[E] = total;
-  }
-  __syncthreads();
-  const int per_rank = E / W;
-  for (int r = tid; r <= W; r += blockDim.x) rank_offsets[r] = kept_s[r * per_rank];
+  __shared__ RankScanShared sh;
+  scan_rank_table<false>(block_counts, B, E, W, capacity, block_excl, demand, counts, offsets,
+                         rank_offsets, sh);
 }
 
 // Threads of a scatter block (one token): 64, 128 or the most, 256.
@@ -170,13 +130,15 @@ constexpr int kRowBufferFlags = 0x00020000;
 //   every kept row.
 //   kHeld: pieces per thread loaded ahead (1, 2 or kMaxHeld); pieces past
 //   kHeld * kThreads are loaded and stored one at a time afterwards.
+//   tpb: tokens per rank block (the rank kernel's or the fused routing
+//   kernel's block), the rows of block_counts / block_excl.
 //   kThreads: the block's threads.  Fewer threads, each holding more
 //   pieces, launch fewer waves for the same bytes: with many tokens the
 //   launch picks about a quarter of the row's pieces (64, 128 or 256).
 template <bool kFusedScan, bool kFp8, int kHeld, int kThreads>
 __global__ __launch_bounds__(kThreads) void dispatch_scatter_kernel(
     const uint4* __restrict__ x, int row_chunks, int N,
-    const int32_t* __restrict__ topk_idx, int E, int K, int W, int64_t capacity,
+    const int32_t* __restrict__ topk_idx, int E, int K, int W, int64_t capacity, int tpb,
     const int32_t* __restrict__ block_counts, const int32_t* __restrict__ block_excl,
     const int32_t* __restrict__ local_rank, int32_t* __restrict__ offsets,
     int32_t* __restrict__ demand, int32_t* __restrict__ counts,
@@ -190,7 +152,7 @@ __global__ __launch_bounds__(kThreads) void dispatch_scatter_kernel(
   const int t = blockIdx.x;
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
-  const int b = t / kRankBlockTokens;
+  const int b = t / tpb;  // rank block
 
   const uint4* src = x + (size_t)t * row_chunks;
   // a buffer resource over the row: pieces past its end read as zero, so the
@@ -213,7 +175,7 @@ __global__ __launch_bounds__(kThreads) void dispatch_scatter_kernel(
     int row = -1;
     if constexpr (kFusedScan) {
       // E <= 256: lane l owns experts 4l .. 4l + 3
-      const int B = (N + kRankBlockTokens - 1) / kRankBlockTokens;
+      const int B = (N + tpb - 1) / tpb;
       // all of the table's loads are issued before any is waited for
       constexpr int kPer = kFusedScanMaxCounts / kWave;
       int cv[kPer];
@@ -375,31 +337,20 @@ DispatchWorkspace dispatch_workspace(void* base, int N, int E, int K) {
   return ws;
 }
 
-hipError_t launch_dispatch(const void* x, size_t row_bytes, int N,
-                           const int32_t* topk_idx, int E, int K, int W,
-                           int64_t capacity, void* x_perm, float* x_scale,
-                           int32_t* perm_token, int32_t* dest,
-                           int32_t* demand, int32_t* counts,
-                           int32_t* offsets, int32_t* rank_offsets,
-                           const DispatchWorkspace& ws, hipStream_t stream) {
-  const int B = (N + kRankBlockTokens - 1) / kRankBlockTokens;
-  const size_t lds = (size_t)kRankWaves * E * sizeof(unsigned long long);
-  dispatch_rank_kernel<<<B, kRankBlockTokens, lds, stream>>>(
-      topk_idx, N, E, K, ws.block_counts, ws.local_rank);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
+namespace {
+
+// The scatter launch (threads, held pieces, fused scan and payload chosen
+// from the sizes).
+hipError_t launch_scatter(const void* x, size_t row_bytes, int N, const int32_t* topk_idx,
+                          int E, int K, int W, int64_t capacity, int tpb, bool fused,
+                          const int32_t* block_counts, const int32_t* block_excl,
+                          const int32_t* local_rank, int32_t* offsets, int32_t* demand,
+                          int32_t* counts, int32_t* rank_offsets, void* x_perm, float* x_scale,
+                          int32_t* perm_token, int32_t* dest, hipStream_t stream) {
   // x_scale != nullptr: fp8 payload of a bf16 row (row_bytes = 2 d)
   const bool fp8 = x_scale != nullptr;
   const int row_chunks = (int)(row_bytes / 16);
   const uint4* xs = static_cast<const uint4*>(x);
-  const bool fused = (int64_t)B * E <= kFusedScanMaxCounts && E <= kFusedScanMaxExperts;
-  if (!fused) {
-    dispatch_scan_kernel<<<1, kScanThreads, 0, stream>>>(
-        ws.block_counts, B, E, W, capacity, ws.block_excl, demand, counts,
-        offsets, rank_offsets);
-    err = hipGetLastError();
-    if (err != hipSuccess) return err;
-  }
   // threads per token: about a quarter of the row's pieces when there are
   // enough tokens to fill the GPU with the fewer waves (dense8's 512-piece
   // rows on 128 threads: cold dispatch 22.7 against 28.5 us on 256), else
@@ -412,9 +363,9 @@ hipError_t launch_dispatch(const void* x, size_t row_bytes, int N,
     constexpr int kT = decltype(threads_c)::value;
     dispatch_scatter_kernel<decltype(fused_c)::value, decltype(fp8_c)::value,
                             decltype(held_c)::value, kT><<<N, kT, 0, stream>>>(
-        xs, row_chunks, N, topk_idx, E, K, W, capacity, ws.block_counts, ws.block_excl,
-        ws.local_rank, offsets, demand, counts, rank_offsets, x_perm,
-        fp8 ? x_scale : nullptr, perm_token, dest);
+        xs, row_chunks, N, topk_idx, E, K, W, capacity, tpb, block_counts, block_excl,
+        local_rank, offsets, demand, counts, rank_offsets, x_perm, fp8 ? x_scale : nullptr,
+        perm_token, dest);
   };
   auto by_threads = [&](auto fused_c, auto fp8_c, auto held_c) {
     if (threads == 64) go(fused_c, fp8_c, held_c, std::integral_constant<int, 64>{});
@@ -441,6 +392,68 @@ hipError_t launch_dispatch(const void* x, size_t row_bytes, int N,
   return hipGetLastError();
 }
 
+}  // namespace
+
+namespace {
+
+// Scan of a per-block count table (rows of tpb tokens) and the scatter: the
+// scan kernel when the table is large, else every scatter block scans it;
+// scanned: the table's scan is already in block_excl and the outputs.
+hipError_t scan_and_scatter(const void* x, size_t row_bytes, int N, const int32_t* topk_idx,
+                            int E, int K, int W, int64_t capacity, int tpb, bool scanned,
+                            const int32_t* block_counts, int32_t* block_excl,
+                            const int32_t* local_rank, void* x_perm, float* x_scale,
+                            int32_t* perm_token, int32_t* dest, int32_t* demand, int32_t* counts,
+                            int32_t* offsets, int32_t* rank_offsets, hipStream_t stream) {
+  const int B = (N + tpb - 1) / tpb;
+  const bool fused =
+      !scanned && (int64_t)B * E <= kFusedScanMaxCounts && E <= kFusedScanMaxExperts;
+  if (!fused && !scanned) {
+    dispatch_scan_kernel<<<1, kRankScanThreads, 0, stream>>>(
+        block_counts, B, E, W, capacity, block_excl, demand, counts, offsets, rank_offsets);
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  return launch_scatter(x, row_bytes, N, topk_idx, E, K, W, capacity, tpb, fused, block_counts,
+                        block_excl, local_rank, offsets, demand, counts, rank_offsets, x_perm,
+                        x_scale, perm_token, dest, stream);
+}
+
+}  // namespace
+
+hipError_t launch_dispatch(const void* x, size_t row_bytes, int N,
+                           const int32_t* topk_idx, int E, int K, int W,
+                           int64_t capacity, void* x_perm, float* x_scale,
+                           int32_t* perm_token, int32_t* dest,
+                           int32_t* demand, int32_t* counts,
+                           int32_t* offsets, int32_t* rank_offsets,
+                           const DispatchWorkspace& ws, hipStream_t stream) {
+  const int B = (N + kRankBlockTokens - 1) / kRankBlockTokens;
+  const size_t lds = (size_t)kRankWaves * E * sizeof(unsigned long long);
+  dispatch_rank_kernel<<<B, kRankBlockTokens, lds, stream>>>(
+      topk_idx, N, E, K, ws.block_counts, ws.local_rank);
+  const hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  return scan_and_scatter(x, row_bytes, N, topk_idx, E, K, W, capacity, kRankBlockTokens,
+                          false, ws.block_counts, ws.block_excl, ws.local_rank, x_perm, x_scale,
+                          perm_token, dest, demand, counts, offsets, rank_offsets, stream);
+}
+
+hipError_t launch_dispatch_planned(const void* x, size_t row_bytes, int N,
+                                   const int32_t* topk_idx, int E, int K, int W,
+                                   int64_t capacity, const RoutePlan& plan, void* x_perm,
+                                   float* x_scale, int32_t* perm_token, int32_t* dest,
+                                   int32_t* demand, int32_t* counts, int32_t* offsets,
+                                   int32_t* rank_offsets, hipStream_t stream) {
+  static_assert(kPlanFusedMaxCounts == kFusedScanMaxCounts &&
+                    kPlanFusedMaxExperts == kFusedScanMaxExperts,
+                "the plan's scan modes follow the scatter's fused-scan limits");
+  const bool scanned = plan_scan_mode(N, E) == PlanScan::kInRoute;
+  return scan_and_scatter(x, row_bytes, N, topk_idx, E, K, W, capacity, route_plan_tokens(E),
+                          scanned, plan.block_counts, plan.block_excl, plan.local_rank, x_perm, x_scale,
+                          perm_token, dest, demand, counts, offsets, rank_offsets, stream);
+}
+
 hipError_t launch_rank_scan(const int32_t* idx, int N, int E, int K, int64_t capacity,
                             int32_t* block_counts, int32_t* block_excl,
                             int32_t* local_rank, int32_t* demand, int32_t* counts,
@@ -451,7 +464,7 @@ hipError_t launch_rank_scan(const int32_t* idx, int N, int E, int K, int64_t cap
                                                              local_rank);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  dispatch_scan_kernel<<<1, kScanThreads, 0, stream>>>(block_counts, B, E, 1, capacity,
+  dispatch_scan_kernel<<<1, kRankScanThreads, 0, stream>>>(block_counts, B, E, 1, capacity,
                                                        block_excl, demand, counts, offsets,
                                                        rank_offsets);
   return hipGetLastError();

@@ -46,6 +46,35 @@ hipError_t launch_route_topk(const float* logits, int N, int E, int K, bool sigm
                              int renormalize, int32_t* topk_idx, float* topk_w,
                              hipStream_t stream);
 
+// Routing fused with the dispatch's ranking (route_topk.hip): blocks of
+// kRoutePlanThreads threads route route_plan_tokens(E) tokens each and write
+// their ranks and per-block counts into the plan buffer: [arrival counter |
+// pad to 256 B][block_counts [B, E] | pad][block_excl [B, E] | pad]
+// [local_rank [N, K]], B = ceil(N / tokens).
+constexpr int kRoutePlanThreads = 1024;
+struct RoutePlan {
+  unsigned* arrive;       // 0 between calls (each call that uses it leaves it 0)
+  int32_t* block_counts;  // [B, E]
+  int32_t* block_excl;    // [B, E]
+  int32_t* local_rank;    // [N, K]
+};
+// Where the block counts of a plan are scanned: by every scatter block
+// (tables of up to kPlanFusedMaxCounts counts and kPlanFusedMaxExperts
+// experts), by the routing launch's last block (up to
+// kPlanRouteScanMaxCounts), else by the dispatch's scan kernel.
+enum class PlanScan { kInScatter, kInRoute, kKernel };
+constexpr int64_t kPlanFusedMaxCounts = 1024;
+constexpr int kPlanFusedMaxExperts = 256;
+constexpr int64_t kPlanRouteScanMaxCounts = 32768;
+PlanScan plan_scan_mode(int N, int E);
+int route_plan_tokens(int E);
+size_t route_plan_bytes(int N, int E, int K);
+RoutePlan route_plan(void* base, int N, int E, int K);
+hipError_t launch_route_plan(const float* logits, int N, int E, int K, bool sigmoid,
+                             int renormalize, int W, int64_t capacity, int32_t* topk_idx,
+                             float* topk_w, int32_t* demand, int32_t* counts, int32_t* offsets,
+                             int32_t* rank_offsets, const RoutePlan& plan, hipStream_t stream);
+
 // Workspace carve-up of moe_dispatch.
 struct DispatchWorkspace {
   int32_t* block_counts;  // [B, E]
@@ -64,6 +93,16 @@ hipError_t launch_dispatch(const void* x, size_t row_bytes, int N,
                            int32_t* demand, int32_t* counts,
                            int32_t* offsets, int32_t* rank_offsets,
                            const DispatchWorkspace& ws, hipStream_t stream);
+
+// The dispatch from a plan that launch_route_plan filled for the same
+// topk_idx, W and capacity: the scan of the plan's block counts unless the
+// routing launch did it (plan_scan_mode), and the scatter; no counting pass.
+hipError_t launch_dispatch_planned(const void* x, size_t row_bytes, int N,
+                                   const int32_t* topk_idx, int E, int K, int W,
+                                   int64_t capacity, const RoutePlan& plan, void* x_perm,
+                                   float* x_scale, int32_t* perm_token, int32_t* dest,
+                                   int32_t* demand, int32_t* counts, int32_t* offsets,
+                                   int32_t* rank_offsets, hipStream_t stream);
 
 // Stable per-(token, slot) ranks of a [N, K] expert-id table (entries
 // outside [0, E) are skipped) and their per-expert scan with one rank:

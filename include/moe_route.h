@@ -213,6 +213,68 @@ int moe_dispatch(const void* x, int32_t dtype, int32_t N, int32_t d,
                  int32_t* offsets, int32_t* rank_offsets, void* workspace,
                  size_t workspace_bytes, void* stream);
 
+/* Bytes of the plan buffer moe_route_plan and moe_dispatch_planned use. */
+size_t moe_route_plan_bytes(int32_t N, int32_t E, int32_t K);
+
+/*
+ * Routing that also counts for the dispatch.  "MoE Inference
+ * Communication", section "MoE 计算核优化", fuses the gate's top-k with the
+ * counting and cumsum that build the token-to-expert table, to save
+ * launches.  This call routes as moe_route_topk_gated and, in the same
+ * launch, ranks each block's tokens per expert and counts them, into
+ * `plan`; where the table of counts is of middling size, the launch's last
+ * block also scans it.  moe_dispatch_planned then needs no counting pass of
+ * its own (and, after such a scan, no scan either).
+ *
+ *   logits, N, E, K, gate, renormalize, topk_idx, topk_w: as
+ *              moe_route_topk_gated (the same results, bit for bit).
+ *   W, capacity, demand, counts, offsets, rank_offsets: as moe_dispatch.
+ *              The four outputs are complete once moe_dispatch_planned has
+ *              run on this plan; this call may fill them first.  Pass the
+ *              same buffers and values to both calls.
+ *   plan       device memory of moe_route_plan_bytes(N, E, K) bytes that
+ *              receives each (token, slot)'s rank among the tokens of its
+ *              block with the same expert, each block's per-expert counts
+ *              and their scan.  Its first 256 bytes hold an arrival counter
+ *              that must be zero before the plan's first use (allocate it
+ *              zeroed); every call leaves it zero.  Calls that may overlap
+ *              (different streams) need plans of their own.
+ * Checks: as moe_route_topk_gated; N >= 1, W >= 1, E % W == 0, capacity >=
+ *         -1 (INVALID_ARG); N*E beyond the plan's 32-bit addressing
+ *         (UNSUPPORTED); plan (WORKSPACE).
+ */
+int moe_route_plan(const float* logits, int32_t N, int32_t E, int32_t K, int32_t gate,
+                   int32_t renormalize, int32_t W, int64_t capacity, int32_t* topk_idx,
+                   float* topk_w, int32_t* demand, int32_t* counts, int32_t* offsets,
+                   int32_t* rank_offsets, void* plan, size_t plan_bytes, void* stream);
+
+/*
+ * moe_dispatch from a plan: the same operation ("MoE 推理服务工程真相
+ * 2026", section 2.3: counts per expert, the capacity drop, grouping for the
+ * all-to-all; the dense token-to-expert table built from a cumsum of "MoE
+ * Inference Communication", section "MoE 计算核优化") and the same results,
+ * without moe_dispatch's counting pass over topk_idx.
+ *
+ *   plan       filled by moe_route_plan for this N, E, K, W, capacity and
+ *              topk_idx (all unchanged since); this call may also write its
+ *              scan of the block counts into it.
+ *   x, dtype, N, d, topk_idx, E, K, W, capacity, perm_token, dest, demand,
+ *   counts, offsets, rank_offsets: as moe_dispatch.
+ *   x_scale    NULL: x_perm [N*K, d] receives bit copies of x's rows, as
+ *              moe_dispatch.  Otherwise x is bf16, d a multiple of 128, and
+ *              x_perm (uint8 codes) and x_scale receive the e4m3 payload of
+ *              moe_dispatch_fp8.
+ * Checks: as moe_dispatch, with the plan in place of the workspace
+ *         (WORKSPACE); x_scale with a non-bf16 dtype or d % 128 != 0
+ *         (INVALID_ARG).
+ */
+int moe_dispatch_planned(const void* x, int32_t dtype, int32_t N, int32_t d,
+                         const int32_t* topk_idx, int32_t E, int32_t K, int32_t W,
+                         int64_t capacity, void* plan, size_t plan_bytes, void* x_perm,
+                         float* x_scale, int32_t* perm_token, int32_t* dest, int32_t* demand,
+                         int32_t* counts, int32_t* offsets, int32_t* rank_offsets,
+                         void* stream);
+
 /*
  * moe_dispatch for callers that cannot allocate device memory: code under
  * HIP graph capture, tight serving loops and harnesses that forbid

@@ -329,3 +329,83 @@ def test_router_rejects_bad_arguments(lib):
     assert f(FAKE, 1, 4, 60, FAKE, 8, FAKE, NUL) == 1          # d not a multiple of 8
     assert f(FAKE, 9, 4, 64, FAKE, 8, FAKE, NUL) == 2          # dtype
     assert f(FAKE, 1, 4, 64, FAKE, 1025, FAKE, NUL) == 2       # E limit
+
+
+def _plan(lib, **kw):
+    a = dict(lg=FAKE, N=64, E=8, K=2, gate=0, ren=0, W=2, cap=-1, idx=FAKE, w=FAKE,
+             demand=FAKE, counts=FAKE, offsets=FAKE, roff=FAKE, plan=FAKE, plan_bytes=1 << 30)
+    a.update(kw)
+    return lib.moe_route_plan(a["lg"], a["N"], a["E"], a["K"], a["gate"], a["ren"], a["W"],
+                              a["cap"], a["idx"], a["w"], a["demand"], a["counts"],
+                              a["offsets"], a["roff"], a["plan"], a["plan_bytes"], NUL)
+
+
+def test_route_plan_rejects_bad_arguments(lib):
+    assert _plan(lib, lg=NUL) == 1
+    assert _plan(lib, w=NUL) == 1
+    assert _plan(lib, idx=NUL) == 1
+    assert _plan(lib, N=0) == 1
+    assert _plan(lib, N=-1) == 1
+    assert _plan(lib, K=9) == 1
+    assert _plan(lib, K=0) == 1
+    assert _plan(lib, gate=7) == 1
+    assert _plan(lib, offsets=NUL) == 1
+    assert _plan(lib, roff=NUL) == 1
+    assert _plan(lib, W=3) == 1                  # E % W != 0
+    assert _plan(lib, W=0) == 1
+    assert _plan(lib, cap=-2) == 1
+    assert _plan(lib, E=2048, W=8) == 2
+    assert _plan(lib, E=32, K=17, W=8) == 2
+    need = lib.moe_route_plan_bytes(64, 8, 2)
+    assert need > 0
+    assert _plan(lib, plan_bytes=need - 1) == 3
+    assert _plan(lib, plan=NUL) == 3
+    assert "plan" in lib.moe_last_error().decode()
+
+
+def test_route_plan_bytes_closed_form(lib):
+    # [256-byte counter | block_counts | block_excl | local_rank], each part
+    # padded to 256 bytes; blocks of 128 tokens up to 8 experts, else 64
+    def up(v):
+        return (v + 255) // 256 * 256
+    for N, E, K in [(1, 8, 2), (128, 8, 2), (129, 8, 2), (4096, 8, 2), (64, 9, 2), (65, 128, 8),
+                    (8192, 128, 8), (32768, 256, 8), (16, 256, 8), (1000, 1024, 16)]:
+        T = 128 if E <= 8 else 64
+        B = -(-N // T)
+        assert lib.moe_route_plan_bytes(N, E, K) == 256 + 2 * up(B * E * 4) + up(N * K * 4)
+    assert lib.moe_route_plan_bytes(0, 8, 2) == 0
+    assert lib.moe_route_plan_bytes(16, 0, 2) == 0
+
+
+def _dplan(lib, **kw):
+    a = dict(x=FAKE, dtype=1, N=64, d=128, idx=FAKE, E=8, K=2, W=4, cap=-1, plan=FAKE,
+             plan_bytes=1 << 30, x_perm=FAKE, x_scale=NUL, perm=FAKE, dest=FAKE, demand=FAKE,
+             counts=FAKE, offsets=FAKE, roff=FAKE)
+    a.update(kw)
+    return lib.moe_dispatch_planned(a["x"], a["dtype"], a["N"], a["d"], a["idx"], a["E"],
+                                    a["K"], a["W"], a["cap"], a["plan"], a["plan_bytes"],
+                                    a["x_perm"], a["x_scale"], a["perm"], a["dest"],
+                                    a["demand"], a["counts"], a["offsets"], a["roff"], NUL)
+
+
+def test_dispatch_planned_rejects_bad_arguments(lib):
+    assert _dplan(lib, x=NUL) == 1
+    assert _dplan(lib, offsets=NUL) == 1
+    assert _dplan(lib, dest=NUL) == 1
+    assert _dplan(lib, roff=NUL) == 1
+    assert _dplan(lib, dtype=5) == 2
+    assert _dplan(lib, N=0) == 1
+    assert _dplan(lib, K=9) == 1
+    assert _dplan(lib, W=3) == 1                     # E % W != 0
+    assert _dplan(lib, W=0) == 1
+    assert _dplan(lib, cap=-2) == 1
+    assert _dplan(lib, d=4) == 1                     # 8 bytes per bf16 row
+    assert _dplan(lib, dtype=0, d=2) == 1            # 8 bytes per fp32 row
+    assert _dplan(lib, x_scale=FAKE, dtype=0) == 1   # fp8 payload from fp32 rows
+    assert _dplan(lib, x_scale=FAKE, d=64) == 1      # d not a multiple of 128
+    assert _dplan(lib, E=2048, W=8) == 2
+    assert _dplan(lib, N=1 << 28, K=8) == 1          # N*K >= 2^31
+    assert _dplan(lib, N=1 << 25, E=1024, K=1, W=8) == 2   # count table past 32-bit offsets
+    need = lib.moe_route_plan_bytes(64, 8, 2)
+    assert _dplan(lib, plan_bytes=need - 1) == 3
+    assert _dplan(lib, plan=NUL) == 3
