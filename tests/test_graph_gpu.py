@@ -2,7 +2,10 @@
 replayed: every replay, with new inputs written into the captured buffers
 and eager work and synchronisations between replays, must give bit for bit
 what an eager layer gives on the same inputs (the kernels are deterministic,
-split reductions included), and the eager layer matches the oracle."""
+split reductions included), and the eager layer matches the oracle.  The
+bf16 layers route and dispatch on the planned path (MoeLayer's default):
+the small tables are scanned in the scatter, plan_in_route's by the routing
+launch's last block and plan_scan_kernel's by the scan kernel."""
 import numpy as np
 import pytest
 import torch
@@ -24,6 +27,13 @@ CASES = {
     # partial slots are reused by every replay)
     "split": (synth.config("gr_split", N=48, d=4096, ffn=4096, E=2, K=2, W=2, act="bf16",
                            C=None), True),
+    # the planned routing's count table (32 x 128) scanned by the routing
+    # launch's last block: its arrival counter is reused by every replay
+    "plan_in_route": (synth.config("gr_plan_route", N=2048, d=256, ffn=256, E=128, K=4, W=8,
+                                   act="bf16", C=1.0), True),
+    # a count table (71 x 600) scanned by the dispatch's scan kernel
+    "plan_scan_kernel": (synth.config("gr_plan_kernel", N=4500, d=128, ffn=128, E=600, K=2,
+                                      W=8, act="bf16", C=None), True),
 }
 
 
