@@ -244,6 +244,10 @@ __global__ __launch_bounds__(kThreads) void dispatch_scatter_kernel(
         if (capacity < 0 || (int64_t)r < capacity) row = offsets[e] + r;
       }
     }
+    // a row outside the N*K buffer rows can only come from a count table
+    // that does not belong to this topk_idx (a misused plan); it is dropped,
+    // so the stores below stay inside x_perm and perm_token
+    if ((unsigned)row >= (unsigned)(N * K)) row = -1;
     if (lane < K) {
       rows[lane] = row;
       dest[(size_t)t * K + lane] = row;

@@ -237,8 +237,10 @@ size_t moe_route_plan_bytes(int32_t N, int32_t E, int32_t K);
  *              block with the same expert, each block's per-expert counts
  *              and their scan.  Its first 256 bytes hold an arrival counter
  *              that must be zero before the plan's first use (allocate it
- *              zeroed); every call leaves it zero.  Calls that may overlap
- *              (different streams) need plans of their own.
+ *              zeroed); every call leaves it zero.  A counter that was not
+ *              zero gives wrong dispatch results (moe_dispatch_planned still
+ *              writes only inside its output buffers).  Calls that may
+ *              overlap (different streams) need plans of their own.
  * Checks: as moe_route_topk_gated; N >= 1, W >= 1, E % W == 0, capacity >=
  *         -1 (INVALID_ARG); N*E beyond the plan's 32-bit addressing
  *         (UNSUPPORTED); plan (WORKSPACE).
