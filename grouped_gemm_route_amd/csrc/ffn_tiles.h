@@ -327,6 +327,16 @@ __device__ __forceinline__ f32x4 load_partial(__amdgpu_buffer_rsrc_t r, int voff
 // Buffer descriptor word 3 for raw (untyped) buffer loads on CDNA.
 constexpr int kBufferFlags = 0x00020000;
 
+// SwiGLU of one gate/up pair of fp32 accumulators: silu(g) * u, silu(g) =
+// g / (1 + e^-g).  The quotient is taken with the hardware reciprocal
+// (v_rcp_f32, within 1 ulp) instead of the correctly rounded division's
+// dozen instructions: the bf16 rounding that follows is 2^15 times coarser.
+// For g below about -88, e^-g = inf, the reciprocal is 0 and silu(g) = -0,
+// as the exact quotient gives.
+__device__ __forceinline__ float swiglu(float g, float u) {
+  return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
+}
+
 constexpr int kBK = 64;             // reduction elements per stage
 constexpr int kRowBytes = kBK * (int)sizeof(bf16);  // 128: one LDS row
 

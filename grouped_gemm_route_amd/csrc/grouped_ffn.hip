@@ -539,7 +539,7 @@ __global__ __launch_bounds__(NW * kWave, 1) void ffn_gemm_bf16_kernel(
             for (int q = 0; q < 4; ++q) {
               const float g = acc[i][j][r4 * 4 + q];
               const float u = acc[i + kHalf][j][r4 * 4 + q];
-              o[q] = (bf16)(g / (1.0f + __expf(-g)) * u);
+              o[q] = (bf16)swiglu(g, u);
             }
             *reinterpret_cast<bf16x4*>(orow + f) = o;
           }

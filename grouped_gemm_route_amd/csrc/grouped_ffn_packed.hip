@@ -55,6 +55,28 @@ constexpr int kFragBytes = 1024;                  // 32 rows x 16 reduction elem
 constexpr int kStepBytes = 4 * kFragBytes;        // one panel, one 16-wide step
 constexpr int kPkCols = kPkWaves * kPanelRows;    // weight rows per block tile
 
+// Output staging (epilogue): each wave's tile of BM rows x its output
+// features (64 after SwiGLU, 128 in the down pass) in its own LDS region,
+// rows 16 bytes longer than their data so that the 32 rows one register
+// group writes fall on different LDS banks.
+template <bool kDual>
+constexpr int staged_row_bytes() {
+  return (kDual ? 64 : kPanelRows) * (int)sizeof(bf16) + 16;
+}
+// LDS of a block: the activation stages during the main loop, the wave
+// staging areas in the epilogue (the same bytes), then the arrival flag of
+// split tiles.
+template <int BM, bool kDual>
+constexpr int packed_flag_offset() {
+  return 4 * BM * kRowBytes > kPkWaves * BM * staged_row_bytes<kDual>()
+             ? 4 * BM * kRowBytes
+             : kPkWaves * BM * staged_row_bytes<kDual>();
+}
+template <int BM, bool kDual>
+constexpr size_t packed_lds_bytes() {
+  return (size_t)packed_flag_offset<BM, kDual>() + 256;
+}
+
 // One thread per 16-byte piece of the packed matrix, written in order.
 __global__ __launch_bounds__(256) void pack_weights_kernel(
     const bf16* __restrict__ w0, const bf16* __restrict__ w1, int Nrows, int Kdim, int P,
@@ -320,7 +342,7 @@ __global__ __launch_bounds__(kPkWaves * kWave, 1) void ffn_gemm_packed_kernel(
     // store_partial), and once they are in memory the piece counts itself in;
     // the piece that arrives last adds the pieces in piece order, re-arms the
     // counter and stores the tile.  The arrival flag sits past the activation
-    // stages.
+    // stages and the epilogue's staging areas.
     if (unit.parts > 1) {
       constexpr int kUnitFloats = NW * kTW * kTM * kWave * 16;
       constexpr int kUnitBytes = kUnitFloats * (int)sizeof(float);
@@ -344,7 +366,7 @@ __global__ __launch_bounds__(kPkWaves * kWave, 1) void ffn_gemm_packed_kernel(
           }
       wait_vmcnt<0>();
       __syncthreads();
-      int* const flag = reinterpret_cast<int*>(lds_bytes + kStages * kAStage);
+      int* const flag = reinterpret_cast<int*>(lds_bytes + packed_flag_offset<BM, kDual>());
       if (threadIdx.x == 0) *flag = atomicAdd(&split_cnt[unit.split], 1);
       __syncthreads();
       if (*flag != unit.parts - 1) continue;
@@ -384,27 +406,37 @@ __global__ __launch_bounds__(kPkWaves * kWave, 1) void ffn_gemm_packed_kernel(
 
     // Epilogue.  Accumulator register r of lane l holds weight row
     // (r / 4) * 8 + (l / 32) * 4 + r % 4 of its 32-row fragment and token
-    // l % 32 of its 32-token operand: runs of 4 consecutive output features.
+    // l % 32 of its 32-token operand: runs of 4 consecutive output features,
+    // one per row for 32 rows.  Stored from the registers, each 8-byte run
+    // would be a write of its own (a store instruction then touches 32 rows
+    // and takes about 0.2 us); instead each wave stages its tile, rounded to
+    // bf16 (after SwiGLU in the gate/up pass), row by row in its own LDS
+    // region, and then stores whole row segments: 16 bytes per lane, a row's
+    // features side by side.  The staging areas cover activation stages:
+    // the barrier lets every wave's last direct-to-LDS loads land first
+    // (each wave waits for its own at the end of the main loop), and the next
+    // unit's loads start after the block barrier at its top.
+    constexpr int kWF = kDual ? 64 : kPanelRows;  // output features of a wave
+    constexpr int kSRow = staged_row_bytes<kDual>();
+    char* const st = lds_bytes + wave * (BM * kSRow);
+    __syncthreads();
 #pragma unroll
     for (int j = 0; j < kTM; ++j) {
-      const int m_local = j * 32 + lrow;
-      if (m_local >= rows) continue;
-      bf16* orow = out + (size_t)(row0 + m_local) * Nout;
+      char* const srow = st + (j * 32 + lrow) * kSRow;
       if (kDual) {
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
 #pragma unroll
           for (int r4 = 0; r4 < 4; ++r4) {
-            const int f = pn * 64 + i * 32 + r4 * 8 + lhalf * 4;
-            if (f >= Nout) continue;
             bf16x4 o;
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
               const float g = acc[i][j][r4 * 4 + c];
               const float u = acc[i + 2][j][r4 * 4 + c];
-              o[c] = (bf16)(g / (1.0f + __expf(-g)) * u);
+              o[c] = (bf16)swiglu(g, u);
             }
-            *reinterpret_cast<bf16x4*>(orow + f) = o;
+            const int fl = i * 32 + r4 * 8 + lhalf * 4;
+            *reinterpret_cast<bf16x4*>(srow + fl * (int)sizeof(bf16)) = o;
           }
         }
       } else {
@@ -412,22 +444,31 @@ __global__ __launch_bounds__(kPkWaves * kWave, 1) void ffn_gemm_packed_kernel(
         for (int i = 0; i < kTW; ++i) {
 #pragma unroll
           for (int r4 = 0; r4 < 4; ++r4) {
-            const int f = pn * kPanelRows + i * 32 + r4 * 8 + lhalf * 4;
-            if (f >= Nout) continue;
             bf16x4 o;
 #pragma unroll
             for (int c = 0; c < 4; ++c) o[c] = (bf16)acc[i][j][r4 * 4 + c];
-            *reinterpret_cast<bf16x4*>(orow + f) = o;
+            const int fl = i * 32 + r4 * 8 + lhalf * 4;
+            *reinterpret_cast<bf16x4*>(srow + fl * (int)sizeof(bf16)) = o;
           }
         }
       }
     }
+    // this wave's LDS writes are done before its lanes read other lanes' rows
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    constexpr int kLPR = kWF / 8;         // lanes per row (16 bytes each)
+    constexpr int kRPI = kWave / kLPR;    // rows per store instruction
+    const int fo = pn * kWF + (lane % kLPR) * 8;  // this lane's first output feature
+#pragma unroll 4
+    for (int r0 = 0; r0 < BM; r0 += kRPI) {
+      if (r0 >= rows) break;
+      const int m_local = r0 + lane / kLPR;
+      if (m_local < rows && fo < Nout) {
+        const uint4 v =
+            *reinterpret_cast<const uint4*>(st + m_local * kSRow + (lane % kLPR) * 16);
+        *reinterpret_cast<uint4*>(out + (size_t)(row0 + m_local) * Nout + fo) = v;
+      }
+    }
   }
-}
-
-template <int BM>
-constexpr size_t packed_lds_bytes() {
-  return (size_t)4 * BM * kRowBytes + 256;  // four activation stages + the arrival flag
 }
 
 template <int BM, bool kDual>
@@ -439,7 +480,7 @@ hipError_t launch_packed_gemm(const bf16* act, int Kdim, const bf16* wpk, int No
   std::call_once(once, [] {
     attr = hipFuncSetAttribute(
         reinterpret_cast<const void*>(&ffn_gemm_packed_kernel<BM, kDual>),
-        hipFuncAttributeMaxDynamicSharedMemorySize, (int)packed_lds_bytes<BM>());
+        hipFuncAttributeMaxDynamicSharedMemorySize, (int)packed_lds_bytes<BM, kDual>());
   });
   if (attr != hipSuccess) return attr;
   const int n_tiles = (P + kPkWaves - 1) / kPkWaves;
@@ -448,7 +489,7 @@ hipError_t launch_packed_gemm(const bf16* act, int Kdim, const bf16* wpk, int No
   const int grid = cps * kXcds;
   (void)max_tiles;
   const int* xcd_start = ws.xcd_start + (kDual ? 0 : kXcds * (E + 1));
-  ffn_gemm_packed_kernel<BM, kDual><<<grid, kPkWaves * kWave, packed_lds_bytes<BM>(), stream>>>(
+  ffn_gemm_packed_kernel<BM, kDual><<<grid, kPkWaves * kWave, packed_lds_bytes<BM, kDual>(), stream>>>(
       act, Kdim, wpk, Nout, P, out, ws.tiles, ws.tile_start, ws.deal_rank, xcd_start, E,
       n_tiles, cps, ws.partial, ws.split_cnt + (kDual ? 0 : kMaxSplitUnits));
   return hipGetLastError();
