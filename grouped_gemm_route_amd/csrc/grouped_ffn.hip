@@ -520,42 +520,56 @@ __global__ __launch_bounds__(NW * kWave, 1) void ffn_gemm_bf16_kernel(
 
     // Epilogue.  Accumulator register r of lane l holds weight row
     // (r / 4) * 8 + (l / 32) * 4 + r % 4 of its 32-row weight tile and token
-    // l % 32 of its 32-row token tile: runs of 4 consecutive output features.
+    // l % 32 of its 32-row token tile: runs of 4 consecutive output features,
+    // one per row for 32 rows.  As in the packed-weight kernel, each wave
+    // stages its tile (its kTM x 32 rows by its output features, contiguous:
+    // wrow[0] onwards), rounded to bf16 after SwiGLU in the gate/up pass, in
+    // its own LDS region with rows 16 bytes longer than their data, and then
+    // stores whole row segments of 16 bytes per lane.  The staging regions
+    // cover the operand stages: every wave's loads land and its operand
+    // reads end before the barrier.
+    {
+      constexpr int kHalf = G::kTW / 2;
+      constexpr int kWF = (kDual ? kHalf : G::kTW) * 32;  // output features of a wave
+      constexpr int kSRow = kWF * (int)sizeof(bf16) + 16;
+      constexpr int kRows = G::kTM * 32;
+      static_assert((size_t)G::kWaves * kRows * kSRow <= G::kLds, "staging fits the LDS");
+      char* const st = lds_bytes + wave * (kRows * kSRow);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
 #pragma unroll
-    for (int j = 0; j < G::kTM; ++j) {
-      const int m_local = arow0 + j * 32 + lrow;
-      if (m_local >= rows) continue;
-      bf16* orow = out + (size_t)(row0 + m_local) * Nout;
-      if (kDual) {
-        constexpr int kHalf = G::kTW / 2;
+      for (int j = 0; j < G::kTM; ++j) {
+        char* const srow = st + (j * 32 + lrow) * kSRow;
 #pragma unroll
-        for (int i = 0; i < kHalf; ++i) {
+        for (int i = 0; i < (kDual ? kHalf : G::kTW); ++i) {
 #pragma unroll
           for (int r4 = 0; r4 < 4; ++r4) {
-            const int f = n0 + wrow[i] + r4 * 8 + lhalf * 4;
-            if (f >= Nout) continue;
             bf16x4 o;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-              const float g = acc[i][j][r4 * 4 + q];
-              const float u = acc[i + kHalf][j][r4 * 4 + q];
-              o[q] = (bf16)swiglu(g, u);
+              if (kDual)
+                o[q] = (bf16)swiglu(acc[i][j][r4 * 4 + q], acc[i + kHalf][j][r4 * 4 + q]);
+              else
+                o[q] = (bf16)acc[i][j][r4 * 4 + q];
             }
-            *reinterpret_cast<bf16x4*>(orow + f) = o;
+            const int fl = i * 32 + r4 * 8 + lhalf * 4;
+            *reinterpret_cast<bf16x4*>(srow + fl * (int)sizeof(bf16)) = o;
           }
         }
-      } else {
-#pragma unroll
-        for (int i = 0; i < G::kTW; ++i) {
-#pragma unroll
-          for (int r4 = 0; r4 < 4; ++r4) {
-            const int f = n0 + wrow[i] + r4 * 8 + lhalf * 4;
-            if (f >= Nout) continue;
-            bf16x4 o;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) o[q] = (bf16)acc[i][j][r4 * 4 + q];
-            *reinterpret_cast<bf16x4*>(orow + f) = o;
-          }
+      }
+      // this wave's LDS writes are done before its lanes read other lanes' rows
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      constexpr int kLPR = kWF / 8;       // lanes per row (16 bytes each)
+      constexpr int kRPI = kWave / kLPR;  // rows per store instruction
+      const int fo = n0 + wrow[0] + (lane % kLPR) * 8;  // this lane's first output feature
+#pragma unroll 4
+      for (int r0 = 0; r0 < kRows; r0 += kRPI) {
+        if (arow0 + r0 >= rows) break;
+        const int m_local = arow0 + r0 + lane / kLPR;
+        if (m_local < rows && fo < Nout) {
+          const uint4 v =
+              *reinterpret_cast<const uint4*>(st + (r0 + lane / kLPR) * kSRow + (lane % kLPR) * 16);
+          *reinterpret_cast<uint4*>(out + (size_t)(row0 + m_local) * Nout + fo) = v;
         }
       }
     }
