@@ -114,6 +114,10 @@ def _close(name, got, ref):
     # 64-row tiles (mean 48 rows per expert) and 32-row tiles (decode-sized)
     dict(N=384, d=256, ffn=320, E=16, K=2),
     dict(N=12, d=512, ffn=256, E=64, K=4),
+    # d and ffn not multiples of 128: the last down panel (and, in the
+    # row-major kernel, the last column tile) ends past d, the last gate/up
+    # column tile holds one panel of features; ragged row tiles
+    dict(N=300, d=320, ffn=192, E=4, K=2),
 ])
 def test_packed_ffn_split_layers_match_oracle_and_repeat(case):
     cfg = synth.config("packed_split", W=1, act="bf16", C=None, **case)
@@ -122,12 +126,14 @@ def test_packed_ffn_split_layers_match_oracle_and_repeat(case):
     pw = B.moe_pack_ffn_weights(inp["w_gate"], inp["w_up"], inp["w_down"])
     M = int(layer.disp["offsets"][-1])
     ws = layer.ffn_ws
-    results = []
+    results, plain = [], []
     for rep in range(3):
         # alternate with the plain-weight call on the same workspace: the
         # split counters each call leaves behind must be re-armed
-        B.moe_grouped_ffn(layer.disp["x_perm"], layer.disp["offsets"], inp["w_gate"],
-                          inp["w_up"], inp["w_down"], layer.max_rows, workspace=ws)
+        hp, yp = B.moe_grouped_ffn(layer.disp["x_perm"], layer.disp["offsets"], inp["w_gate"],
+                                   inp["w_up"], inp["w_down"], layer.max_rows, workspace=ws)
+        torch.cuda.synchronize()
+        plain.append((hp[:M].clone(), yp[:M].clone()))
         h, y = B.moe_grouped_ffn_packed(layer.disp["x_perm"], layer.disp["offsets"], pw,
                                         layer.max_rows, workspace=ws)
         torch.cuda.synchronize()
@@ -137,3 +143,5 @@ def test_packed_ffn_split_layers_match_oracle_and_repeat(case):
     h_ref, y_ref = _oracle_rows(inp, layer, M)
     _close("h", results[0][0].float().cpu().numpy(), h_ref)
     _close("y_perm", results[0][1].float().cpu().numpy(), y_ref)
+    _close("h (row-major weights)", plain[0][0].float().cpu().numpy(), h_ref)
+    _close("y_perm (row-major weights)", plain[0][1].float().cpu().numpy(), y_ref)
