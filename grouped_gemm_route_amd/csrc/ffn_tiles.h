@@ -208,8 +208,10 @@ __device__ __forceinline__ bool map_block(const int* __restrict__ tile_start,
 // [kb, ke) of reduction tiles.  For a piece of a split tile, split >= 0
 // numbers the tile's arrival counter, the tile is piece `piece` of `parts`
 // and its pieces' partials go to workspace slots pslot0 + 0 .. parts - 1.
+// half >= 0: a half-width unit, the column tile's half `half` (packed-weight
+// kernel only); -1: the whole column tile.
 struct Unit {
-  int slot, n_tile, kb, ke, split, piece, parts, pslot0;
+  int slot, n_tile, kb, ke, split, piece, parts, pslot0, half;
 };
 
 // Expert holding global block position L (0 <= L < n_tiles * tile_start[E]):
@@ -247,8 +249,12 @@ __device__ __forceinline__ int xcd_range(const int* __restrict__ tile_start, int
 // last R tiles becomes s = min(cps / R, kMaxSplit, nk / kMinSplitTiles)
 // pieces of consecutive reduction tiles, which take the XCD's block numbers
 // after the whole tiles and so fill its last round, if that saves at least
-// kSplitMinSaved reduction tiles of the round (nk - nk / s); otherwise
-// every tile stays whole.
+// kSplitMinSaved reduction tiles of the round (nk - nk / s).  Otherwise, with
+// kNarrow and a last round at most half full (2 R <= cps), each of the last R
+// tiles becomes two half-width units (each half of its column tile's weight
+// rows, the whole reduction: no partial sums), which take the block numbers
+// after the whole tiles; else every tile stays whole.
+template <bool kNarrow = false>
 __device__ __forceinline__ bool map_unit(int b, const int* __restrict__ tile_start,
                                          const int* __restrict__ deal_rank,
                                          const int* __restrict__ xcd_start, int E,
@@ -262,15 +268,20 @@ __device__ __forceinline__ bool map_unit(int b, const int* __restrict__ tile_sta
   const int R = B % cps;
   int s = R > 0 ? min(min(cps / R, kMaxSplit), nk / kMinSplitTiles) : 1;
   if (s < 2 || nk - nk / s < kSplitMinSaved) s = 1;
-  const int whole = s > 1 ? B - R : B;
+  const bool narrow = kNarrow && s == 1 && R > 0 && 2 * R <= cps;
+  const int ways = s > 1 ? s : (narrow ? 2 : 1);  // units per tile of the last round
+  const int whole = ways > 1 ? B - R : B;
   // (fields are set once, at the end: per-branch stores to a struct through
   // a pointer can end up in scratch memory)
   const bool is_piece = i >= whole;
   const int p = i - whole;
-  if (is_piece && (s == 1 || p >= R * s)) return false;
-  const int t = is_piece ? p / s : 0;
-  const int piece = is_piece ? p % s : 0;
-  const int parts = is_piece ? s : 1;
+  if (is_piece && (ways == 1 || p >= R * ways)) return false;
+  const int t = is_piece ? p / ways : 0;
+  const int sub = is_piece ? p % ways : 0;
+  const bool kpiece = is_piece && s > 1;  // a piece of a split tile
+  const int piece = kpiece ? sub : 0;
+  const int parts = kpiece ? s : 1;
+  const int half = is_piece && narrow ? sub : -1;
   const int entry = is_piece ? whole + t : i;
   int e = 0, r = 0;
   if (rr) {
@@ -293,10 +304,11 @@ __device__ __forceinline__ bool map_unit(int b, const int* __restrict__ tile_sta
             n_tile,
             piece * nk / parts,
             (piece + 1) * nk / parts,
-            is_piece ? x * cps + t : -1,
+            kpiece ? x * cps + t : -1,
             piece,
             parts,
-            x * cps + t * s};
+            x * cps + t * s,
+            half};
   return true;
 }
 

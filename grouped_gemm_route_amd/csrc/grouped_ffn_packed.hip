@@ -35,6 +35,9 @@
 //     direct-to-LDS buffer loads, two reduction tiles ahead, and every wave
 //     reads all BM rows from it (one 16-byte read per 32-token operand).
 //     16-byte chunks are XOR-swizzled as in the row-major kernel.
+// A half-width unit (a tile of an XCD's partial last round, ffn_tiles.h
+// map_unit) covers half the column tile: two waves per panel, two fragments
+// each.
 // Compared with staging both operands through LDS (grouped_ffn.hip: 256 x
 // 256 block tiles, each operand read from LDS by two waves), the LDS traffic
 // per 64-wide reduction tile drops from 192 KB to 80 KB at the same MFMA
@@ -137,7 +140,8 @@ __global__ __launch_bounds__(kPkWaves * kWave, 1) void ffn_gemm_packed_kernel(
   // launched only to find no work.
   for (int vb = blockIdx.x;; vb += gridDim.x) {
     Unit unit;
-    if (!map_unit(vb, tile_start, deal_rank, xcd_start, E, n_tiles, Kdim / kBK, cps, &unit))
+    if (!map_unit<true>(vb, tile_start, deal_rank, xcd_start, E, n_tiles, Kdim / kBK, cps,
+                        &unit))
       break;
     // the previous unit's waves are done with the LDS stages
     __syncthreads();
@@ -148,7 +152,15 @@ __global__ __launch_bounds__(kPkWaves * kWave, 1) void ffn_gemm_packed_kernel(
     const int rows = tile.z - tile.y;
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    const int pn = unit.n_tile * NW + wave;  // this wave's panel
+    // A half-width unit (unit.half >= 0) covers panels 2 half, 2 half + 1 of
+    // the column tile, two waves per panel, each wave two of the panel's four
+    // fragments: the gate/up pass's matching gate and up fragments (SwiGLU
+    // stays in registers), the down pass's 64 consecutive rows.
+    const bool nar = unit.half >= 0;
+    const int pn = nar ? unit.n_tile * NW + unit.half * 2 + (wave >> 1)
+                       : unit.n_tile * NW + wave;  // this wave's panel
+    const int nfrag0 = kDual ? (wave & 1) : 2 * (wave & 1);  // half-width: first fragment
+    constexpr int kNStride = kDual ? 2 : 1;                  // and the step to the second
     const int S = Kdim / 16;
     const int nk = unit.ke - unit.kb;        // reduction tiles of this unit
     const int nsteps = nk * 4;
@@ -198,8 +210,10 @@ __global__ __launch_bounds__(kPkWaves * kWave, 1) void ffn_gemm_packed_kernel(
 
     // (offsets go through locals: an array element or a conditional
     // expression as a buffer builtin's argument drops the kernel's host stub)
-    auto load_w = [&](int slot, int i, int q) __attribute__((always_inline)) {
-      const int voff = w_lane + i * kFragBytes;
+    auto load_w = [&](auto ktw_c, int slot, int i, int q) __attribute__((always_inline)) {
+      constexpr int KTW = decltype(ktw_c)::value;
+      const int frag = KTW == kTW ? i : nfrag0 + i * kNStride;
+      const int voff = w_lane + frag * kFragBytes;
       const int soff = w_step0 + q * kStepBytes;
       wf[slot][i] =
           __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(wr, voff, soff, 0));
@@ -240,16 +254,28 @@ __global__ __launch_bounds__(kPkWaves * kWave, 1) void ffn_gemm_packed_kernel(
     // own load.  Past the last tile the loads repeat the last step or tile
     // into ring slots and stages nobody reads again, so the body has no
     // branches.
-    auto step = [&](auto jn_c, auto sl_c, auto ks_c, int kt) __attribute__((always_inline)) {
+    // A half-width unit's step has KTW = 2 weight operands: 2 kTM slots,
+    // activation load l in slot 2 l + 1 of step 0 (after both weight loads of
+    // that step), and 13 + kAL loads between tile kt + 1's activations and
+    // the wait (none later in their step, 6 in steps 1..3, 2 + kAL in step 0
+    // of tile kt, 4 in its steps 1..2 and 1 before the wait; the prologue
+    // issues 2 kDist after tile 1's).
+    auto step = [&](auto ktw_c, auto jn_c, auto sl_c, auto ks_c, int kt)
+                    __attribute__((always_inline)) {
+      constexpr int KTW = decltype(ktw_c)::value;
       constexpr int JN = decltype(jn_c)::value;
       constexpr int SL = decltype(sl_c)::value;
       constexpr int KS = decltype(ks_c)::value;
-      constexpr int n = kTW * kTM;                   // MFMA slots
+      constexpr int n = KTW * kTM;                   // MFMA slots
+      constexpr int kWaitN = KTW == kTW ? 30 : 13 + kAL;
+      // half-width units hold half the weight bytes per step in flight: they
+      // load 7 steps ahead (the ring's limit) instead of kDist
+      constexpr int kD = KTW == kTW ? kDist : kRing - 1;
       constexpr int per_read = n / kTM;              // slots per operand read, steps 0..2
       constexpr int half = n / 2;
       constexpr int per_read3 = half / kTM > 0 ? half / kTM : 1;
       const int q = kt * 4 + KS;
-      const int qw = min(q + kDist, nsteps - 1);
+      const int qw = min(q + kD, nsteps - 1);
       const int cur = (kt & (kStages - 1));
       const int nxt = ((kt + 1) & (kStages - 1));
       const int kt_a = min(kt + 2, nk - 1);
@@ -257,11 +283,15 @@ __global__ __launch_bounds__(kPkWaves * kWave, 1) void ffn_gemm_packed_kernel(
       for (int m = 0; m < n; ++m) {
         const int i = m / kTM, j = m % kTM;
         if (KS == 3 && m == half) {
-          wait_vmcnt<30>();
+          wait_vmcnt<kWaitN>();
           fence_free_barrier();
         }
-        if (j == 0) load_w((SL + kDist) % kRing, i, qw);
-        if (KS == 0 && j == kTM / 2 && i < kAL) load_a((kt + 2) & (kStages - 1), kt_a, i);
+        if (j == 0) load_w(ktw_c, (SL + kD) % kRing, i, qw);
+        if (KTW == kTW) {
+          if (KS == 0 && j == kTM / 2 && i < kAL) load_a((kt + 2) & (kStages - 1), kt_a, i);
+        } else {
+          if (KS == 0 && m % 2 == 1) load_a((kt + 2) & (kStages - 1), kt_a, m / 2);
+        }
         if (KS < 3) {
           if (m % per_read == 1 % per_read && m / per_read < JN)
             read_a((KS + 1) & 1, cur, KS + 1, m / per_read);
@@ -281,59 +311,67 @@ __global__ __launch_bounds__(kPkWaves * kWave, 1) void ffn_gemm_packed_kernel(
     using C2 = std::integral_constant<int, 2>;
     using C3 = std::integral_constant<int, 3>;
     // tile kt uses ring slots (kt % 2) * 4 + ks
-    auto tile_fn = [&](auto jn_c, auto ph_c, int kt) __attribute__((always_inline)) {
+    auto tile_fn = [&](auto ktw_c, auto jn_c, auto ph_c, int kt) __attribute__((always_inline)) {
       constexpr int PH = decltype(ph_c)::value;
-      step(jn_c, std::integral_constant<int, PH + 0>{}, C0{}, kt);
-      step(jn_c, std::integral_constant<int, PH + 1>{}, C1{}, kt);
-      step(jn_c, std::integral_constant<int, PH + 2>{}, C2{}, kt);
-      step(jn_c, std::integral_constant<int, PH + 3>{}, C3{}, kt);
+      step(ktw_c, jn_c, std::integral_constant<int, PH + 0>{}, C0{}, kt);
+      step(ktw_c, jn_c, std::integral_constant<int, PH + 1>{}, C1{}, kt);
+      step(ktw_c, jn_c, std::integral_constant<int, PH + 2>{}, C2{}, kt);
+      step(ktw_c, jn_c, std::integral_constant<int, PH + 3>{}, C3{}, kt);
     };
     using P0 = std::integral_constant<int, 0>;
     using P4 = std::integral_constant<int, 4>;
     // JN: 32-token operands that hold rows (a ragged last tile of an expert
     // multiplies fewer; a run-time test per MFMA would force the accumulators
     // out of registers, so the loop comes in one variant per JN)
-    auto main_loop = [&](auto jn_c) __attribute__((always_inline)) {
+    auto main_loop = [&](auto ktw_c, auto jn_c) __attribute__((always_inline)) {
+      constexpr int KTW = decltype(ktw_c)::value;
       constexpr int JN = decltype(jn_c)::value;
-      // prologue: activation tiles 0 and 1, weight steps 0 .. kDist - 1; wait
-      // for tile 0 (after it: kAL + 4 kDist loads)
+      constexpr int kD = KTW == kTW ? kDist : kRing - 1;
+      // prologue: activation tiles 0 and 1, weight steps 0 .. kD - 1; wait
+      // for tile 0 (after it: kAL + KTW kD loads)
 #pragma unroll
       for (int l = 0; l < kAL; ++l) load_a(0, 0, l);
 #pragma unroll
       for (int l = 0; l < kAL; ++l) load_a(1, min(1, nk - 1), l);
 #pragma unroll
-      for (int s = 0; s < kDist; ++s)
+      for (int s = 0; s < kD; ++s)
 #pragma unroll
-        for (int i = 0; i < kTW; ++i) load_w(s, i, min(s, nsteps - 1));
-      wait_vmcnt<kAL + 4 * kDist>();
+        for (int i = 0; i < KTW; ++i) load_w(ktw_c, s, i, min(s, nsteps - 1));
+      wait_vmcnt<kAL + KTW * kD>();
       fence_free_barrier();
 #pragma unroll
       for (int j = 0; j < kTM; ++j)
         if (j < JN) read_a(0, 0, 0, j);
       if (nk & 1) {
-        tile_fn(jn_c, P0{}, 0);
+        tile_fn(ktw_c, jn_c, P0{}, 0);
         for (int kt = 1; kt < nk; kt += 2) {
-          tile_fn(jn_c, P4{}, kt);
-          tile_fn(jn_c, P0{}, kt + 1);
+          tile_fn(ktw_c, jn_c, P4{}, kt);
+          tile_fn(ktw_c, jn_c, P0{}, kt + 1);
         }
       } else {
         for (int kt = 0; kt < nk; kt += 2) {
-          tile_fn(jn_c, P0{}, kt);
-          tile_fn(jn_c, P4{}, kt + 1);
+          tile_fn(ktw_c, jn_c, P0{}, kt);
+          tile_fn(ktw_c, jn_c, P4{}, kt + 1);
         }
       }
       // the trailing repeat loads land before the block can end (and its LDS
       // be handed to another block)
       wait_vmcnt<0>();
     };
-    if (jlim >= kTM)
-      main_loop(std::integral_constant<int, kTM>{});
-    else if (kTM > 2 && jlim == 3)
-      main_loop(std::integral_constant<int, (kTM > 2 ? 3 : kTM)>{});
-    else if (kTM > 1 && jlim == 2)
-      main_loop(std::integral_constant<int, (kTM > 1 ? 2 : kTM)>{});
+    auto run_loop = [&](auto ktw_c) __attribute__((always_inline)) {
+      if (jlim >= kTM)
+        main_loop(ktw_c, std::integral_constant<int, kTM>{});
+      else if (kTM > 2 && jlim == 3)
+        main_loop(ktw_c, std::integral_constant<int, (kTM > 2 ? 3 : kTM)>{});
+      else if (kTM > 1 && jlim == 2)
+        main_loop(ktw_c, std::integral_constant<int, (kTM > 1 ? 2 : kTM)>{});
+      else
+        main_loop(ktw_c, C1{});
+    };
+    if (nar)
+      run_loop(std::integral_constant<int, 2>{});
     else
-      main_loop(C1{});
+      run_loop(std::integral_constant<int, kTW>{});
 
     // A piece of a split tile (map_unit): its fp32 accumulators go to its
     // workspace slot in register order (each store instruction writes one
@@ -416,58 +454,70 @@ __global__ __launch_bounds__(kPkWaves * kWave, 1) void ffn_gemm_packed_kernel(
     // the barrier lets every wave's last direct-to-LDS loads land first
     // (each wave waits for its own at the end of the main loop), and the next
     // unit's loads start after the block barrier at its top.
-    constexpr int kWF = kDual ? 64 : kPanelRows;  // output features of a wave
-    constexpr int kSRow = staged_row_bytes<kDual>();
-    char* const st = lds_bytes + wave * (BM * kSRow);
-    __syncthreads();
+    // A half-width unit's wave holds half as many output features (32 after
+    // SwiGLU, 64 in the down pass) and stages them in the first half of each
+    // of its rows.
+    auto epilogue = [&](auto nar_c) __attribute__((always_inline)) {
+      constexpr bool kNar = decltype(nar_c)::value;
+      constexpr int kWF = (kDual ? 64 : kPanelRows) / (kNar ? 2 : 1);  // output features of a wave
+      constexpr int kSRow = staged_row_bytes<kDual>();
+      char* const st = lds_bytes + wave * (BM * kSRow);
+      __syncthreads();
 #pragma unroll
-    for (int j = 0; j < kTM; ++j) {
-      char* const srow = st + (j * 32 + lrow) * kSRow;
-      if (kDual) {
+      for (int j = 0; j < kTM; ++j) {
+        char* const srow = st + (j * 32 + lrow) * kSRow;
+        if (kDual) {
+          constexpr int kPairs = kNar ? 1 : 2;  // gate operands; up operand i + kPairs
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
+          for (int i = 0; i < kPairs; ++i) {
 #pragma unroll
-          for (int r4 = 0; r4 < 4; ++r4) {
-            bf16x4 o;
+            for (int r4 = 0; r4 < 4; ++r4) {
+              bf16x4 o;
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
-              const float g = acc[i][j][r4 * 4 + c];
-              const float u = acc[i + 2][j][r4 * 4 + c];
-              o[c] = (bf16)swiglu(g, u);
+              for (int c = 0; c < 4; ++c) {
+                const float g = acc[i][j][r4 * 4 + c];
+                const float u = acc[i + kPairs][j][r4 * 4 + c];
+                o[c] = (bf16)swiglu(g, u);
+              }
+              const int fl = i * 32 + r4 * 8 + lhalf * 4;
+              *reinterpret_cast<bf16x4*>(srow + fl * (int)sizeof(bf16)) = o;
             }
-            const int fl = i * 32 + r4 * 8 + lhalf * 4;
-            *reinterpret_cast<bf16x4*>(srow + fl * (int)sizeof(bf16)) = o;
           }
-        }
-      } else {
+        } else {
 #pragma unroll
-        for (int i = 0; i < kTW; ++i) {
+          for (int i = 0; i < (kNar ? 2 : kTW); ++i) {
 #pragma unroll
-          for (int r4 = 0; r4 < 4; ++r4) {
-            bf16x4 o;
+            for (int r4 = 0; r4 < 4; ++r4) {
+              bf16x4 o;
 #pragma unroll
-            for (int c = 0; c < 4; ++c) o[c] = (bf16)acc[i][j][r4 * 4 + c];
-            const int fl = i * 32 + r4 * 8 + lhalf * 4;
-            *reinterpret_cast<bf16x4*>(srow + fl * (int)sizeof(bf16)) = o;
+              for (int c = 0; c < 4; ++c) o[c] = (bf16)acc[i][j][r4 * 4 + c];
+              const int fl = i * 32 + r4 * 8 + lhalf * 4;
+              *reinterpret_cast<bf16x4*>(srow + fl * (int)sizeof(bf16)) = o;
+            }
           }
         }
       }
-    }
-    // this wave's LDS writes are done before its lanes read other lanes' rows
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    constexpr int kLPR = kWF / 8;         // lanes per row (16 bytes each)
-    constexpr int kRPI = kWave / kLPR;    // rows per store instruction
-    const int fo = pn * kWF + (lane % kLPR) * 8;  // this lane's first output feature
+      // this wave's LDS writes are done before its lanes read other lanes' rows
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      constexpr int kLPR = kWF / 8;       // lanes per row (16 bytes each)
+      constexpr int kRPI = kWave / kLPR;  // rows per store instruction
+      const int f0 = kNar ? pn * (kDual ? 64 : kPanelRows) + (wave & 1) * kWF : pn * kWF;
+      const int fo = f0 + (lane % kLPR) * 8;  // this lane's first output feature
 #pragma unroll 4
-    for (int r0 = 0; r0 < BM; r0 += kRPI) {
-      if (r0 >= rows) break;
-      const int m_local = r0 + lane / kLPR;
-      if (m_local < rows && fo < Nout) {
-        const uint4 v =
-            *reinterpret_cast<const uint4*>(st + m_local * kSRow + (lane % kLPR) * 16);
-        *reinterpret_cast<uint4*>(out + (size_t)(row0 + m_local) * Nout + fo) = v;
+      for (int r0 = 0; r0 < BM; r0 += kRPI) {
+        if (r0 >= rows) break;
+        const int m_local = r0 + lane / kLPR;
+        if (m_local < rows && fo < Nout) {
+          const uint4 v =
+              *reinterpret_cast<const uint4*>(st + m_local * kSRow + (lane % kLPR) * 16);
+          *reinterpret_cast<uint4*>(out + (size_t)(row0 + m_local) * Nout + fo) = v;
+        }
       }
-    }
+    };
+    if (nar)
+      epilogue(std::true_type{});
+    else
+      epilogue(std::false_type{});
   }
 }
 
