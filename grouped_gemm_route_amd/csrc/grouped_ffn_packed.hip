@@ -259,7 +259,7 @@ __global__ __launch_bounds__(kPkWaves * kWave, 1) void ffn_gemm_packed_kernel(
     // that step), and 13 + kAL loads between tile kt + 1's activations and
     // the wait (none later in their step, 6 in steps 1..3, 2 + kAL in step 0
     // of tile kt, 4 in its steps 1..2 and 1 before the wait; the prologue
-    // issues 2 kDist after tile 1's).
+    // issues 2 x 7 weight loads after tile 1's).
     auto step = [&](auto ktw_c, auto jn_c, auto sl_c, auto ks_c, int kt)
                     __attribute__((always_inline)) {
       constexpr int KTW = decltype(ktw_c)::value;
