@@ -138,11 +138,10 @@ __global__ __launch_bounds__(kPkWaves * kWave, 1) void ffn_gemm_packed_kernel(
   // One block per CU walks its XCD's list: block slot b = blockIdx.x + k
   // gridDim.x (gridDim.x is 8 x the blocks resident per XCD), so no block is
   // launched only to find no work.
-  for (int vb = blockIdx.x;; vb += gridDim.x) {
-    Unit unit;
-    if (!map_unit<true>(vb, tile_start, deal_rank, xcd_start, E, n_tiles, Kdim / kBK, cps,
-                        &unit))
-      break;
+  Unit unit;
+  bool have = map_unit<true>(blockIdx.x, tile_start, deal_rank, xcd_start, E, n_tiles,
+                             Kdim / kBK, cps, &unit);
+  for (int vb = blockIdx.x; have; vb += gridDim.x) {
     // the previous unit's waves are done with the LDS stages
     __syncthreads();
     const int kofs = unit.kb * kBK;
@@ -381,6 +380,11 @@ __global__ __launch_bounds__(kPkWaves * kWave, 1) void ffn_gemm_packed_kernel(
     // the piece that arrives last adds the pieces in piece order, re-arms the
     // counter and stores the tile.  The arrival flag sits past the activation
     // stages and the epilogue's staging areas.
+    // The next unit's mapping (a chain of dependent schedule reads) is taken
+    // here, so that its latency passes during this unit's epilogue.
+    Unit next;
+    const bool more = map_unit<true>(vb + (int)gridDim.x, tile_start, deal_rank, xcd_start, E,
+                                     n_tiles, Kdim / kBK, cps, &next);
     if (unit.parts > 1) {
       constexpr int kUnitFloats = NW * kTW * kTM * kWave * 16;
       constexpr int kUnitBytes = kUnitFloats * (int)sizeof(float);
@@ -407,7 +411,11 @@ __global__ __launch_bounds__(kPkWaves * kWave, 1) void ffn_gemm_packed_kernel(
       int* const flag = reinterpret_cast<int*>(lds_bytes + packed_flag_offset<BM, kDual>());
       if (threadIdx.x == 0) *flag = atomicAdd(&split_cnt[unit.split], 1);
       __syncthreads();
-      if (*flag != unit.parts - 1) continue;
+      if (*flag != unit.parts - 1) {
+        unit = next;
+        have = more;
+        continue;
+      }
       // the partials of one weight operand (all kTM token operands) of one
       // piece are loaded together, so a piece costs one memory round trip per
       // weight operand
@@ -518,6 +526,8 @@ __global__ __launch_bounds__(kPkWaves * kWave, 1) void ffn_gemm_packed_kernel(
       epilogue(std::true_type{});
     else
       epilogue(std::false_type{});
+    unit = next;
+    have = more;
   }
 }
 
